@@ -1,0 +1,82 @@
+"""Plain fp64 building blocks of the decoder (ORACLE — test infrastructure only).
+
+Each function is the textbook definition, evaluated in float64 with numpy.
+The rounding points of the storage contract (bf16 at GEMM inputs, bf16 q/k/v,
+fp32 residual) are applied by the callers in ``oracle/model.py`` through
+``round_act``.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+SQRT_2_OVER_PI = np.sqrt(2.0 / np.pi)
+
+
+def round_bf16(x) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 (ties to even), returned as
+    float64.  bfloat16 keeps 8 significant bits and fp32's exponent range; the
+    quantum is 2^(e-8) for x = m*2^e, m in [0.5, 1), and 2^-133 in the
+    subnormal range."""
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    q = np.ldexp(1.0, np.maximum(e - 8, -133))
+    return np.rint(x / q) * q
+
+
+def round_f32(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def rmsnorm(x: np.ndarray, eps: float) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps), gain 1 (no learned gain in the synthetic models)."""
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def gelu_tanh(x: np.ndarray) -> np.ndarray:
+    """GELU, tanh approximation (Hendrycks & Gimpel, 2016, section 2)."""
+    return 0.5 * x * (1.0 + np.tanh(SQRT_2_OVER_PI * (x + 0.044715 * x ** 3)))
+
+
+def rope(x: np.ndarray, positions: np.ndarray, base: float) -> np.ndarray:
+    """Rotary position embedding (Su et al., RoFormer, 2021, section 3.4.2):
+    each pair (2j, 2j+1) of a head vector at position p is rotated by the angle
+    p * base^(-2j/d).  x: [..., T, H, d]; positions: [T]."""
+    d = x.shape[-1]
+    j = np.arange(d // 2, dtype=np.float64)
+    inv_freq = base ** (-2.0 * j / d)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * inv_freq[None, :]  # [T, d/2]
+    c = np.cos(ang)[:, None, :]
+    s = np.sin(ang)[:, None, :]
+    x0 = x[..., 0::2]
+    x1 = x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x0 * c - x1 * s
+    out[..., 1::2] = x0 * s + x1 * c
+    return out
+
+
+def softmax(a: np.ndarray, axis: int = -1) -> np.ndarray:
+    m = np.max(a, axis=axis, keepdims=True)
+    e = np.exp(a - m)
+    return e / np.sum(e, axis=axis, keepdims=True)
+
+
+def entropy_direct(p: np.ndarray) -> np.ndarray:
+    """H = -sum p ln p with 0 ln 0 = 0, per row."""
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = np.where(p > 0.0, p * np.log(np.where(p > 0.0, p, 1.0)), 0.0)
+    return -np.sum(t, axis=-1)
+
+
+def e4m3_round(x: np.ndarray) -> np.ndarray:
+    """Round to the OCP FP8 E4M3 grid (1 sign, 4 exponent bits with bias 7,
+    3 mantissa bits, max finite 448, no infinities), ties to even; values
+    beyond 448 saturate.  Returned as float64."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    _, e = np.frexp(a)  # a = m 2^e, m in [0.5,1)
+    # normal quantum 2^(e-4) (4 significant bits); subnormal quantum 2^-9
+    q = np.ldexp(1.0, np.maximum(e - 4, -9))
+    r = np.rint(a / q) * q
+    r = np.minimum(r, 448.0)
+    return np.sign(x) * r

@@ -1,0 +1,145 @@
+"""Seeded synthetic inputs shared by the CPU oracle and the GPU path.
+
+This module manufactures inputs only (weights, prompt tokens, KV-cache fills,
+Dirichlet self-conditioning rows) and holds none of the decoding method's
+arithmetic.  The definition of every generator is in ``gen.c``; ``gen_dev.hip``
+is its device twin for model sizes the host cannot fill quickly.  A pure-numpy
+restatement (``*_np``) exists for the small cases the tests use to pin the C
+code.
+
+Tensor ids (``TID``) name each logical weight of the model; logical layouts
+are row-major ``[out][in]`` (``[E][out][in]`` for expert banks).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libdgsynth.so")
+_lib = None
+
+# Tensor ids for the synthetic generator.
+TID = {
+    "embed": 1,
+    "lm_head": 2,
+    "sc_up": 3,
+    "sc_down": 4,
+    "kv_k": 5,
+    "kv_v": 6,
+    "dirichlet": 7,
+    "prompt": 10,
+}
+LAYER_TID_BASE = 100
+LAYER_TID_STRIDE = 16
+LAYER_TENSORS = ("wqkv", "wo", "wr", "sh_g", "sh_u", "sh_d", "ex_g", "ex_u", "ex_d")
+
+
+def layer_tid(layer: int, name: str) -> int:
+    return LAYER_TID_BASE + LAYER_TID_STRIDE * layer + LAYER_TENSORS.index(name)
+
+
+def build(force: bool = False) -> str:
+    """Compile gen.c into libdgsynth.so (gcc, OpenMP)."""
+    src = os.path.join(_HERE, "gen.c")
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(src):
+        subprocess.check_call(
+            ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", src, "-o", _LIB_PATH + ".tmp", "-lm"]
+        )
+        os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    return _LIB_PATH
+
+
+def _get_lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        u64, f32, i64 = ctypes.c_uint64, ctypes.c_float, ctypes.c_int64
+        vp = ctypes.c_void_p
+        lib.synth_scale_for_std.argtypes = [ctypes.c_double]
+        lib.synth_scale_for_std.restype = f32
+        lib.synth_normal_f32.argtypes = [u64, u64, u64, u64, f32, vp]
+        lib.synth_normal_bf16.argtypes = [u64, u64, u64, u64, f32, vp]
+        lib.synth_tokens.argtypes = [u64, u64, u64, u64, ctypes.c_uint32, vp]
+        lib.synth_dirichlet_rows.argtypes = [u64, u64, i64, i64, ctypes.c_double, vp]
+        _lib = lib
+    return _lib
+
+
+def scale_for_std(std: float) -> np.float32:
+    return np.float32(_get_lib().synth_scale_for_std(float(std)))
+
+
+def normal(seed: int, tensor: int, shape, std: float, dtype: str = "bf16", start: int = 0):
+    """N(0, std^2)-shaped values (Irwin-Hall of 4 uniforms).
+
+    dtype "bf16" returns uint16 bit patterns, "f32" returns float32."""
+    n = int(np.prod(shape))
+    lib = _get_lib()
+    sc = ctypes.c_float(scale_for_std(std))
+    if dtype == "bf16":
+        out = np.empty(n, dtype=np.uint16)
+        lib.synth_normal_bf16(seed, tensor, start, n, sc, out.ctypes.data)
+    elif dtype == "f32":
+        out = np.empty(n, dtype=np.float32)
+        lib.synth_normal_f32(seed, tensor, start, n, sc, out.ctypes.data)
+    else:
+        raise ValueError(dtype)
+    return out.reshape(shape)
+
+
+def tokens(seed: int, tensor: int, n: int, vocab: int, start: int = 0) -> np.ndarray:
+    out = np.empty(n, dtype=np.int32)
+    _get_lib().synth_tokens(seed, tensor, start, n, vocab, out.ctypes.data)
+    return out
+
+
+def dirichlet_rows(seed: int, tensor: int, rows: int, vocab: int, alpha: float) -> np.ndarray:
+    out = np.empty((rows, vocab), dtype=np.float32)
+    _get_lib().synth_dirichlet_rows(seed, tensor, rows, vocab, alpha, out.ctypes.data)
+    return out
+
+
+def bf16_bits_to_f32(u16: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to float32."""
+    return (u16.astype(np.uint32) << 16).view(np.float32)
+
+
+# ---- pure-numpy restatement of the same definitions (small sizes only) ----
+_M64 = (1 << 64) - 1
+
+
+def hash_np(seed: int, tensor: int, idx: np.ndarray) -> np.ndarray:
+    idx = idx.astype(np.uint64)
+    with np.errstate(over="ignore"):
+        z = (np.uint64(seed & _M64) + np.uint64(0x9E3779B97F4A7C15) * (idx + np.uint64(1))
+             + np.uint64((0xD1B54A32D192ED03 * (tensor + 1)) & _M64))
+        z = (z ^ (z >> np.uint64(30))) * np.uint64(0xBF58476D1CE4E5B9)
+        z = (z ^ (z >> np.uint64(27))) * np.uint64(0x94D049BB133111EB)
+    return z ^ (z >> np.uint64(31))
+
+
+def normal_np(seed: int, tensor: int, n: int, std: float, dtype: str = "bf16", start: int = 0):
+    z = hash_np(seed, tensor, np.arange(start, start + n, dtype=np.uint64))
+    m = np.uint64(0xFFFF)
+    s = ((z & m).astype(np.int64) + ((z >> np.uint64(16)) & m).astype(np.int64)
+         + ((z >> np.uint64(32)) & m).astype(np.int64) + (z >> np.uint64(48)).astype(np.int64) - 131070)
+    scale = np.float32(std / np.sqrt((65536.0 * 65536.0 - 1.0) / 3.0))
+    f = s.astype(np.float32) * scale
+    if dtype == "f32":
+        return f
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
+    return u.astype(np.uint16)
+
+
+def tokens_np(seed: int, tensor: int, n: int, vocab: int, start: int = 0) -> np.ndarray:
+    z = hash_np(seed, tensor, np.arange(start, start + n, dtype=np.uint64))
+    hi = z >> np.uint64(32)
+    with np.errstate(over="ignore"):
+        return ((hi * np.uint64(vocab)) >> np.uint64(32)).astype(np.int32)

@@ -1,0 +1,114 @@
+"""Workload definitions: model shapes and the seeded synthetic run recipes.
+
+These are inputs (sizes, dtypes, seeds, the LM-head scale of the random-init
+models), shared by the oracle and the GPU path.  The sampler's own constants
+(temperature endpoints, entropy bound, stop threshold) are not here: each side
+states them itself.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field, replace
+
+
+@dataclass(frozen=True)
+class ModelShape:
+    n_layers: int
+    d_model: int
+    n_q_heads: int
+    n_kv_heads: int
+    d_head: int
+    n_experts: int
+    top_k: int
+    d_expert: int
+    d_shared: int
+    vocab: int
+    d_selfcond: int
+    dtype: str = "bf16"          # dense weights and activation storage: "f32" | "bf16"
+    expert_dtype: str = "bf16"   # "f32" | "bf16" | "fp8"
+    lm_dtype: str = "bf16"       # "f32" | "bf16" | "fp8"
+    rope_base: float = 10000.0
+    norm_eps: float = 1e-6
+    weight_std: float = 0.02
+    weight_seed: int = 0
+
+    @property
+    def qkv_rows(self) -> int:
+        return (self.n_q_heads + 2 * self.n_kv_heads) * self.d_head
+
+    @property
+    def q_dim(self) -> int:
+        return self.n_q_heads * self.d_head
+
+    @property
+    def kv_dim(self) -> int:
+        return self.n_kv_heads * self.d_head
+
+    def param_counts(self) -> dict:
+        d = self.d_model
+        per_layer_dense = self.qkv_rows * d + d * self.q_dim + self.n_experts * d + 3 * self.d_shared * d
+        per_layer_experts = self.n_experts * 3 * self.d_expert * d
+        embed = self.vocab * d
+        sc = 2 * d * self.d_selfcond
+        total_tied = self.n_layers * (per_layer_dense + per_layer_experts) + embed + sc
+        active = (self.n_layers * (per_layer_dense + self.top_k * 3 * self.d_expert * d)
+                  + embed + sc)
+        return {
+            "per_layer": per_layer_dense + per_layer_experts,
+            "embed": embed,
+            "selfcond": sc,
+            "total_tied_head": total_tied,
+            "total_untied_head": total_tied + embed,
+            "active_tied_head": active,
+        }
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    model: ModelShape
+    batch: int
+    canvas: int
+    prefix: int                  # prompt tokens causally encoded before the first canvas
+    prefix_mode: str = "encode"  # "encode" (run the causal encoder) | "random_kv" (N(0,1) cache)
+    n_steps: int = 48
+    adaptive: bool = True
+    lm_scale: float = 1.0
+    n_blocks: int = 1
+    sampler_seeds: tuple = (0,)
+    prompt_seed: int = 0
+    selfcond_init: str = "none"  # "none" | "dirichlet" (external P for the first step)
+    dirichlet_alpha: float = 0.05
+    first_step: int = 0
+
+
+TINY = ModelShape(n_layers=2, d_model=256, n_q_heads=4, n_kv_heads=2, d_head=64, n_experts=8,
+                  top_k=2, d_expert=128, d_shared=128, vocab=4096, d_selfcond=128,
+                  dtype="f32", expert_dtype="f32", lm_dtype="f32")
+
+FULL_LAYER = ModelShape(n_layers=1, d_model=2816, n_q_heads=16, n_kv_heads=8, d_head=256,
+                        n_experts=128, top_k=8, d_expert=704, d_shared=2112, vocab=262144,
+                        d_selfcond=1408)
+
+FULL_30 = replace(FULL_LAYER, n_layers=30)
+
+FULL_LAYER_FP8 = replace(FULL_LAYER, expert_dtype="fp8", lm_dtype="fp8")
+
+WORKLOADS = {
+    # 2-layer fp32 denoiser; prefix 64 encoded causally; canvas 32; <=48 adaptive steps.
+    "tiny": Workload("tiny", TINY, batch=1, canvas=32, prefix=64, n_steps=48, adaptive=True,
+                     lm_scale=8.0),
+    # one full-width layer + LM head; random N(0,1) cache of 2048; Dirichlet(0.05) self-cond;
+    # single step at t = 1 of a 48-step budget.
+    "layer1": Workload("layer1", FULL_LAYER, batch=1, canvas=256, prefix=2048,
+                       prefix_mode="random_kv", n_steps=48, adaptive=False, lm_scale=1.0,
+                       selfcond_init="dirichlet", first_step=1),
+    # full 30-layer model; 4096-token causal prefix; one canvas; fixed 12 / 48 and adaptive.
+    "full30": Workload("full30", FULL_30, batch=1, canvas=256, prefix=4096, n_steps=12,
+                       adaptive=False, lm_scale=1.0),
+    # long context on the one-layer model: 32768 prefix, 8 committed canvases.
+    "longctx": Workload("longctx", FULL_LAYER, batch=1, canvas=256, prefix=32768, n_steps=48,
+                        adaptive=True, n_blocks=8, lm_scale=1.0),
+    # fp8 experts + LM head, 4 independent canvases with 8192-token prefixes, 12 steps.
+    "fp8batch4": Workload("fp8batch4", FULL_LAYER_FP8, batch=4, canvas=256, prefix=8192,
+                          n_steps=12, adaptive=False, lm_scale=1.0, sampler_seeds=(0, 1, 2, 3)),
+}

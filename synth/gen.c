@@ -1,0 +1,120 @@
+/*
+ * Seeded synthetic inputs for the block-diffusion decoder: weights, tokens,
+ * KV-cache fills and Dirichlet rows.  This file holds no step of the decoding
+ * method; it only manufactures inputs.  Both the CPU oracle and the GPU path
+ * receive exactly the values produced here (or by the device twin in
+ * gen_dev.hip, which implements the same definition and is checked against
+ * this file bit for bit).
+ *
+ * Definition (all integer, so host and device agree exactly):
+ *   h(seed, tensor, i) = SplitMix64 finaliser applied to
+ *       seed + G*(i+1) + H*(tensor+1)      (mod 2^64)
+ *     with G = 0x9E3779B97F4A7C15, H = 0xD1B54A32D192ED03 and the finaliser
+ *     of Steele, Lea & Flood, "Fast splittable pseudorandom number
+ *     generators" (OOPSLA 2014), with the mixing constants of Vigna's
+ *     splitmix64.
+ *   normal value   = fp32( (sum of the four 16-bit fields of h) - 131070 )
+ *                    * scale,   scale = fp32(std / sqrt((65536^2-1)/3))
+ *                    (Irwin-Hall sum of 4 uniforms: mean 0, variance std^2,
+ *                    support +-3.46 std), then bf16 by round-to-nearest-even
+ *                    when a bf16 tensor is asked for.
+ *   token          = (hi32(h) * V) >> 32   (exactly uniform when V is 2^b).
+ *   uniform in (0,1) = ((h >> 11) + 0.5) * 2^-53.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+static inline uint64_t synth_hash(uint64_t seed, uint64_t tensor, uint64_t i) {
+  uint64_t z = seed + 0x9E3779B97F4A7C15ull * (i + 1) + 0xD1B54A32D192ED03ull * (tensor + 1);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+static inline float synth_normal_value(uint64_t z, float scale) {
+  int32_t s = (int32_t)(z & 0xFFFF) + (int32_t)((z >> 16) & 0xFFFF) +
+              (int32_t)((z >> 32) & 0xFFFF) + (int32_t)(z >> 48) - 131070;
+  return (float)s * scale;
+}
+
+static inline uint16_t synth_bf16_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+float synth_scale_for_std(double std) {
+  return (float)(std / sqrt((65536.0 * 65536.0 - 1.0) / 3.0));
+}
+
+void synth_normal_f32(uint64_t seed, uint64_t tensor, uint64_t start, uint64_t count, float scale,
+                      float* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < (int64_t)count; ++j)
+    out[j] = synth_normal_value(synth_hash(seed, tensor, start + (uint64_t)j), scale);
+}
+
+void synth_normal_bf16(uint64_t seed, uint64_t tensor, uint64_t start, uint64_t count, float scale,
+                       uint16_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < (int64_t)count; ++j)
+    out[j] = synth_bf16_rne(synth_normal_value(synth_hash(seed, tensor, start + (uint64_t)j), scale));
+}
+
+void synth_tokens(uint64_t seed, uint64_t tensor, uint64_t start, uint64_t count, uint32_t vocab,
+                  int32_t* out) {
+  for (uint64_t j = 0; j < count; ++j) {
+    uint64_t hi = synth_hash(seed, tensor, start + j) >> 32;
+    out[j] = (int32_t)((hi * (uint64_t)vocab) >> 32);
+  }
+}
+
+static inline double synth_uniform(uint64_t seed, uint64_t tensor, uint64_t i) {
+  return ((double)(synth_hash(seed, tensor, i) >> 11) + 0.5) * (1.0 / 9007199254740992.0);
+}
+
+/* Standard normal by Box-Muller from two uniforms (host only; used for the
+ * Gamma draws of the Dirichlet rows, never for weights). */
+static inline double synth_std_normal(uint64_t seed, uint64_t tensor, uint64_t i) {
+  double u1 = synth_uniform(seed, tensor, 2 * i), u2 = synth_uniform(seed, tensor, 2 * i + 1);
+  return sqrt(-2.0 * log(u1)) * cos(6.283185307179586 * u2);
+}
+
+/* Gamma(alpha, 1) for alpha < 1 by Marsaglia & Tsang (ACM TOMS 2000) on
+ * alpha+1 with the U^(1/alpha) boost.  Each draw j uses its own sub-stream
+ * (tensor, j) so rows can be generated in parallel. */
+static double synth_gamma(uint64_t seed, uint64_t tensor, uint64_t j, double alpha) {
+  double a = alpha < 1.0 ? alpha + 1.0 : alpha;
+  double d = a - 1.0 / 3.0, c = 1.0 / sqrt(9.0 * d);
+  uint64_t sub = 0x5D588B656C078965ull * (j + 1) ^ tensor;
+  for (uint64_t it = 0;; ++it) {
+    double x = synth_std_normal(seed, sub, 3 * it), v = 1.0 + c * x;
+    if (v <= 0.0) continue;
+    v = v * v * v;
+    double u = synth_uniform(seed, sub, 3 * it + 2);
+    if (log(u) < 0.5 * x * x + d - d * v + d * log(v)) {
+      double g = d * v;
+      if (alpha < 1.0) g *= pow(synth_uniform(seed, sub ^ 0xA5A5A5A5ull, it + 7), 1.0 / alpha);
+      return g;
+    }
+  }
+}
+
+/* rows x V Dirichlet(alpha) rows, normalised in fp64, rounded once to fp32. */
+void synth_dirichlet_rows(uint64_t seed, uint64_t tensor, int64_t rows, int64_t V, double alpha,
+                          float* out) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < rows; ++r) {
+    double* g = (double*)malloc((size_t)V * sizeof(double));
+    double s = 0.0;
+    for (int64_t v = 0; v < V; ++v) {
+      g[v] = synth_gamma(seed, tensor, (uint64_t)(r * V + v), alpha);
+      s += g[v];
+    }
+    for (int64_t v = 0; v < V; ++v) out[r * V + v] = (float)(g[v] / s);
+    free(g);
+  }
+}
