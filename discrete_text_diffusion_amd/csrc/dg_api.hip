@@ -1,0 +1,667 @@
+// Host side of the C ABI (include/dg.h): argument checks, the workspace plan,
+// and the launch sequence of encode / denoise / commit.  Allocates nothing.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/dg.h"
+#include "dg_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMoeBM = 32;        // row tile of the grouped expert GEMMs (bf16)
+constexpr int kSimpleBM = 16;     // row tile of the fp32 GEMMs
+constexpr int kMaxRoutePairs = 8192;
+constexpr int kMaxSplit = 16;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+struct Shape {
+  int L, d, nq, nkv, dh, E, k, de, ds, V, dsc, dt;
+  float rope_base, eps;
+  int qdim, kvdim, qkv, n_sh, nvt;
+  size_t act;  // bytes per activation element
+};
+
+Shape shape_of(const dg_model_config* c) {
+  Shape s;
+  s.L = c->n_layers; s.d = c->d_model; s.nq = c->n_q_heads; s.nkv = c->n_kv_heads; s.dh = c->d_head;
+  s.E = c->n_experts; s.k = c->top_k; s.de = c->d_expert; s.ds = c->d_shared; s.V = c->vocab;
+  s.dsc = c->d_selfcond; s.dt = c->dtype;
+  s.rope_base = c->rope_base; s.eps = c->norm_eps;
+  s.qdim = s.nq * s.dh; s.kvdim = s.nkv * s.dh; s.qkv = s.qdim + 2 * s.kvdim;
+  s.n_sh = s.de > 0 ? s.ds / s.de : 0;
+  s.nvt = s.V / 256;
+  s.act = s.dt == DG_DTYPE_BF16 ? 2 : 4;
+  return s;
+}
+
+int check_config(const dg_model_config* c) {
+  if (!c) return DG_ERR_INVALID_ARG;
+  if (c->n_layers < 1 || c->d_model < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->d_head < 2 ||
+      c->n_experts < 1 || c->top_k < 1 || c->top_k > c->n_experts || c->d_expert < 1 || c->d_shared < 1 ||
+      c->vocab < 256 || c->d_selfcond < 1)
+    return DG_ERR_INVALID_ARG;
+  if (c->dtype != DG_DTYPE_F32 && c->dtype != DG_DTYPE_BF16) return DG_ERR_UNSUPPORTED;
+  if (c->n_q_heads % c->n_kv_heads || c->d_shared % c->d_expert || c->vocab % 256 || c->d_head % 2 ||
+      c->top_k > 16 || c->n_experts > 255 || c->d_head > 256)
+    return DG_ERR_UNSUPPORTED;
+  if (c->dtype == DG_DTYPE_BF16) {
+    const int G = c->n_q_heads / c->n_kv_heads;
+    if (c->d_head != 256 || (G != 1 && G != 2 && G != 4) || c->d_model % 64 || c->d_expert % 64 ||
+        c->d_shared % 64 || c->d_selfcond % 64 || (c->n_q_heads * c->d_head) % 64 || c->n_experts % 16)
+      return DG_ERR_UNSUPPORTED;
+  } else {
+    if (c->d_model % 2 || c->d_expert % 2 || c->d_selfcond % 2 || c->n_experts % 2) return DG_ERR_UNSUPPORTED;
+  }
+  return DG_OK;
+}
+
+// Token capacity of one pass through the layer stack.
+int max_tokens(const Shape& s, int batch, int max_canvas) {
+  const int route_cap = kMaxRoutePairs / s.k;
+  return std::max(std::min(2048, route_cap), batch * max_canvas);
+}
+
+struct Plan {
+  int T;        // tokens per pass
+  int Tdn;      // denoise tokens
+  int att_rows; // attention partial rows (split x tokens)
+  size_t x, n, q, ckv_k, ckv_v, o, att_o, att_ml, o_part, r_part, ids, wts, row_token, inv, offsets, tiles,
+      n_tiles, h, Y, lm_f, lm_i, logits, e_part, ebar, hsc, sc_out, total;
+};
+
+Plan make_plan(const Shape& s, int batch, int max_canvas) {
+  Plan p;
+  p.T = max_tokens(s, batch, max_canvas);
+  p.Tdn = batch * max_canvas;
+  p.att_rows = std::max(4096, kMaxSplit * p.Tdn);
+  const size_t T = p.T, Tdn = p.Tdn;
+  const size_t rows_moe = T * s.k + (size_t)s.n_sh * T;
+  const size_t max_tiles = T * s.k / kSimpleBM + s.E + (size_t)s.n_sh * ((T + kSimpleBM - 1) / kSimpleBM) + 8;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off += align_up(bytes); return o; };
+  p.x = take(T * s.d * 4);
+  p.n = take(T * s.d * s.act);
+  p.q = take(T * s.qdim * s.act);
+  p.ckv_k = take(Tdn * s.kvdim * s.act);
+  p.ckv_v = take(Tdn * s.kvdim * s.act);
+  p.o = take(T * s.qdim * s.act);
+  p.att_o = take((size_t)p.att_rows * s.nq * s.dh * 4);
+  p.att_ml = take((size_t)p.att_rows * s.nq * 8);
+  p.o_part = take(8 * T * s.d * 4);
+  p.r_part = take(8 * T * s.E * 4);
+  p.ids = take(T * s.k * 4);
+  p.wts = take(T * s.k * 4);
+  p.row_token = take(rows_moe * 4);
+  p.inv = take(T * s.k * 4);
+  p.offsets = take((s.E + 1) * 4);
+  p.tiles = take(max_tiles * sizeof(GemmTile));
+  p.n_tiles = take(4);
+  p.h = take(rows_moe * s.de * s.act);
+  p.Y = take(rows_moe * s.d * 4);
+  p.lm_f = take(Tdn * s.nvt * sizeof(float4));
+  p.lm_i = take(Tdn * s.nvt * sizeof(int2));
+  p.logits = take(s.dt == DG_DTYPE_F32 ? Tdn * s.V * 4 : 0);
+  p.e_part = take(kMaxSplit * Tdn * s.d * 4);
+  p.ebar = take(Tdn * s.d * s.act);
+  p.hsc = take(Tdn * s.dsc * s.act);
+  p.sc_out = take(Tdn * s.d * 4);
+  p.total = off;
+  return p;
+}
+
+struct Ctx {
+  Shape s;
+  Plan p;
+  char* ws;
+  hipStream_t st;
+  const dg_weights* w;
+  dg_trace* tr = nullptr;
+  const int32_t* force_ids = nullptr;  // test path: [n_layers][T][k] expert ids
+  template <typename T> T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
+};
+
+// Records a begin/end event pair around a phase when the trace asks for it.
+struct Phase {
+  const Ctx& c;
+  int idx = -1;
+  Phase(const Ctx& ctx, int phase) : c(ctx) {
+    dg_trace* t = c.tr;
+    if (t && (t->mask >> phase & 1u) && t->count + 2 <= t->capacity) {
+      idx = t->count;
+      t->phase[idx / 2] = phase;
+      t->count += 2;
+      hipEventRecord((hipEvent_t)t->events[idx], c.st);
+    }
+  }
+  ~Phase() {
+    if (idx >= 0) hipEventRecord((hipEvent_t)c.tr->events[idx + 1], c.st);
+  }
+};
+
+GemmArgs base_args() {
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.alpha = 1.0f;
+  a.n_split = 1;
+  return a;
+}
+
+int pick_split(int blocks_per_split, int K, int kc, int max_split) {
+  int sp = std::max(1, std::min(max_split, (512 + blocks_per_split - 1) / std::max(1, blocks_per_split)));
+  while (sp > 1 && (K / kc) < sp) --sp;
+  return sp;
+}
+
+// Dense GEMM: out = act[M][K] . W[N][K]^T with the given epilogue.  Only
+// EPI_STORE_F32 may split K (partials at out_f32 + split * split_stride);
+// the split count used is returned in *used_split.
+int dense_gemm(const Ctx& c, GemmArgs a, int M, int N, int K, int max_split, int* used_split = nullptr) {
+  a.M = M; a.N = N; a.K = K;
+  a.n_main = 1;
+  if (used_split) *used_split = 1;
+  if (c.s.dt == DG_DTYPE_BF16) {
+    const int bm = 128, nwt = 1;
+    a.kt_main = K / 32;
+    a.max_tiles = (M + bm - 1) / bm;
+    a.n_fb = (N + 64 * nwt - 1) / (64 * nwt);
+    a.tile_fastest = 1;
+    int sp = (a.epi == EPI_STORE_F32) ? pick_split(a.max_tiles * a.n_fb, K, 64, max_split) : 1;
+    a.k_split = ((K / 64 + sp - 1) / sp) * 64;
+    a.n_split = (K + a.k_split - 1) / a.k_split;
+    if (used_split) *used_split = a.n_split;
+    return launch_wsgemm(a, bm, nwt, 64, a.epi == EPI_GEGLU, c.st);
+  }
+  a.kt_main = K / 32;  // row pitch of plain fp32 weights is kt_main * 32 = K
+  a.max_tiles = (M + kSimpleBM - 1) / kSimpleBM;
+  a.n_split = 1;
+  a.k_split = K;
+  return launch_gemm_simple(a, c.st);
+}
+
+#define DG_TRY(x)                 \
+  do {                            \
+    const int rc_ = (x);          \
+    if (rc_ != 0) return rc_ < 0 ? rc_ : DG_ERR_HIP; \
+  } while (0)
+
+// The layer stack over T = n_seq * seq_len tokens whose embeddings are in
+// x / n.  causal: encode (k, v appended to the cache at rows L..); else the
+// denoiser (canvas k, v kept in the workspace).
+int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, int L, bool causal) {
+  const Shape& s = c.s;
+  const int T = n_seq * seq_len;
+  const bool bf = s.dt == DG_DTYPE_BF16;
+  const int64_t layer_elems = (int64_t)cache->batch * s.nkv * cache->capacity * s.dh;
+  const int64_t c_seq = (int64_t)s.nkv * cache->capacity * s.dh, c_head = (int64_t)cache->capacity * s.dh;
+  const int64_t w_seq = (int64_t)s.nkv * seq_len * s.dh, w_head = (int64_t)seq_len * s.dh;
+  void* xn = c.at<void>(c.p.n);
+  for (int l = 0; l < s.L; ++l) {
+    const dg_layer_weights& lw = c.w->layers[l];
+    char* kc = reinterpret_cast<char*>(cache->k) + (size_t)l * layer_elems * s.act;
+    char* vc = reinterpret_cast<char*>(cache->v) + (size_t)l * layer_elems * s.act;
+    // q, k, v with RoPE
+    {
+      Phase ph(c, DG_PHASE_QKV);
+      GemmArgs a = base_args();
+      a.act = xn; a.act_ld = s.d; a.act_kind = bf ? ACT_BF16 : ACT_F32;
+      a.w0 = lw.wqkv;
+      a.epi = EPI_QKV;
+      QkvEpi& q = a.qkv;
+      q.q = c.at<void>(c.p.q);
+      q.q_dim = s.qdim; q.kv_dim = s.kvdim; q.d_head = s.dh; q.n_kv = s.nkv;
+      if (causal) {
+        q.k = kc; q.v = vc; q.kv_b_stride = c_seq; q.kv_h_stride = c_head; q.kv_row0 = L;
+      } else {
+        q.k = c.at<void>(c.p.ckv_k); q.v = c.at<void>(c.p.ckv_v);
+        q.kv_b_stride = w_seq; q.kv_h_stride = w_head; q.kv_row0 = 0;
+      }
+      q.seq_len = seq_len; q.pos0 = L; q.rope_base = s.rope_base;
+      DG_TRY(dense_gemm(c, a, T, s.qkv, s.d, 1));
+    }
+    // attention
+    {
+      Phase ph(c, DG_PHASE_ATTN);
+      const int n_keys = L + seq_len;
+      int split = 1;
+      if (bf) {
+        split = std::min(kMaxSplit, std::max(1, (n_keys + 255) / 256));
+        split = std::min(split, std::max(1, c.p.att_rows / T));
+        const int G = s.nq / s.nkv;
+        const int base_blocks = n_seq * s.nkv * ((seq_len + 64 / G - 1) / (64 / G));
+        split = std::min(split, std::max(1, (1024 + base_blocks - 1) / base_blocks));
+      }
+      if (causal) {
+        DG_TRY(launch_attention(bf, c.at<void>(c.p.q), s.qdim, kc, vc, c_seq, c_head, L + seq_len, nullptr, nullptr, 0,
+                                0, 0, L, 1, seq_len, n_seq, s.nq, s.nkv, s.dh, split, c.at<float>(c.p.att_o),
+                                c.at<float2>(c.p.att_ml), c.at<void>(c.p.o), c.st));
+      } else {
+        DG_TRY(launch_attention(bf, c.at<void>(c.p.q), s.qdim, kc, vc, c_seq, c_head, L, c.at<void>(c.p.ckv_k),
+                                c.at<void>(c.p.ckv_v), w_seq, w_head, seq_len, L, 0, seq_len, n_seq, s.nq, s.nkv, s.dh,
+                                split, c.at<float>(c.p.att_o), c.at<float2>(c.p.att_ml), c.at<void>(c.p.o), c.st));
+      }
+    }
+    // O projection (split-K partials), residual, RMSNorm
+    {
+      Phase ph(c, DG_PHASE_OPROJ);
+      GemmArgs a = base_args();
+      a.act = c.at<void>(c.p.o); a.act_ld = s.qdim; a.act_kind = bf ? ACT_BF16 : ACT_F32;
+      a.w0 = lw.wo;
+      a.epi = EPI_STORE_F32; a.out_f32 = c.at<float>(c.p.o_part); a.ldo = s.d; a.split_stride = (int64_t)T * s.d;
+      int n_split = 1;
+      DG_TRY(dense_gemm(c, a, T, s.d, s.qdim, 8, &n_split));
+      DG_TRY(launch_resid_norm(bf, c.at<float>(c.p.x), c.at<float>(c.p.o_part), n_split, (int64_t)T * s.d, xn, T, s.d,
+                               s.eps, c.st));
+    }
+    // router logits
+    int r_split = 1;
+    const int bm = bf ? kMoeBM : kSimpleBM;
+    {
+      Phase ph(c, DG_PHASE_ROUTE);
+      GemmArgs a = base_args();
+      a.act = xn; a.act_ld = s.d; a.act_kind = bf ? ACT_BF16 : ACT_F32;
+      a.w0 = lw.wr;
+      a.epi = EPI_STORE_F32; a.out_f32 = c.at<float>(c.p.r_part); a.ldo = s.E; a.split_stride = (int64_t)T * s.E;
+      DG_TRY(dense_gemm(c, a, T, s.E, s.d, 8, &r_split));
+      const int32_t* forced = c.force_ids ? c.force_ids + (int64_t)l * T * s.k : nullptr;
+      DG_TRY(launch_topk(c.at<float>(c.p.r_part), r_split, (int64_t)T * s.E, T, s.E, s.k, forced,
+                         c.at<int32_t>(c.p.ids), c.at<float>(c.p.wts), c.st));
+      DG_TRY(launch_route_sort(c.at<int32_t>(c.p.ids), T, s.k, s.E, s.n_sh, bm, c.at<int32_t>(c.p.row_token),
+                               c.at<int32_t>(c.p.inv), c.at<int32_t>(c.p.offsets), c.at<GemmTile>(c.p.tiles),
+                               c.at<int32_t>(c.p.n_tiles), c.st));
+    }
+    const int max_tiles = T * s.k / bm + s.E + s.n_sh * ((T + bm - 1) / bm);
+    // experts + shared slices: gate/up with GeGLU
+    {
+      Phase ph(c, DG_PHASE_MOE_UP);
+      GemmArgs a = base_args();
+      a.act = xn; a.act_ld = s.d; a.act_kind = bf ? ACT_BF16 : ACT_F32;
+      a.row_map = c.at<int32_t>(c.p.row_token);
+      a.w0 = lw.ex_g; a.w1 = lw.ex_u; a.w_group_stride = (int64_t)s.de * s.d;
+      a.w0_alt = lw.sh_g; a.w1_alt = lw.sh_u; a.w_alt_stride = (int64_t)s.de * s.d;
+      a.n_main = s.E; a.kt_main = s.d / 32; a.kt_alt = s.d / 32; a.kt_off_alt = 0;
+      a.K = s.d; a.N = s.de;
+      a.tiles = c.at<GemmTile>(c.p.tiles); a.n_tiles_dev = c.at<int32_t>(c.p.n_tiles); a.max_tiles = max_tiles;
+      a.M = 0;
+      a.epi = EPI_GEGLU; a.out_act = c.at<void>(c.p.h); a.ldo = s.de;
+      a.n_split = 1; a.k_split = s.d;
+      if (bf) {
+        a.n_fb = (s.de + 63) / 64;
+        a.tile_fastest = 0;
+        DG_TRY(launch_wsgemm(a, kMoeBM, 1, 64, true, c.st));
+      } else {
+        DG_TRY(launch_gemm_simple(a, c.st));
+      }
+    }
+    // down projections
+    {
+      Phase ph(c, DG_PHASE_MOE_DOWN);
+      GemmArgs a = base_args();
+      a.act = c.at<void>(c.p.h); a.act_ld = s.de; a.act_kind = bf ? ACT_BF16 : ACT_F32;
+      a.w0 = lw.ex_d; a.w_group_stride = (int64_t)s.d * s.de;
+      a.w0_alt = lw.sh_d; a.w_alt_stride = 0;
+      a.n_main = s.E; a.kt_main = s.de / 32; a.kt_alt = s.ds / 32; a.kt_off_alt = s.de / 32;
+      a.K = s.de; a.N = s.d;
+      a.tiles = c.at<GemmTile>(c.p.tiles); a.n_tiles_dev = c.at<int32_t>(c.p.n_tiles); a.max_tiles = max_tiles;
+      a.epi = EPI_STORE_F32; a.out_f32 = c.at<float>(c.p.Y); a.ldo = s.d; a.split_stride = 0;
+      a.n_split = 1; a.k_split = s.de;
+      if (bf) {
+        a.n_fb = (s.d + 127) / 128;
+        a.tile_fastest = 0;
+        DG_TRY(launch_wsgemm(a, kMoeBM, 2, 64, false, c.st));
+      } else {
+        DG_TRY(launch_gemm_simple(a, c.st));
+      }
+    }
+    {
+      Phase ph(c, DG_PHASE_COMBINE);
+      DG_TRY(launch_combine_norm(bf, c.at<float>(c.p.x), c.at<float>(c.p.Y), c.at<int32_t>(c.p.inv),
+                                 c.at<float>(c.p.wts), T, s.k, s.n_sh, xn, s.d, s.eps, c.st));
+    }
+  }
+  return DG_OK;
+}
+
+int check_ws(const Plan& p, void* ws, size_t bytes) {
+  if (!ws || bytes < p.total) return DG_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return DG_ERR_INVALID_ARG;
+  return DG_OK;
+}
+
+int check_weights(const dg_model_config* cfg, const dg_weights* w) {
+  if (!w || !w->embed || !w->lm_head || !w->layers) return DG_ERR_INVALID_ARG;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const dg_layer_weights& L = w->layers[l];
+    if (!L.wqkv || !L.wo || !L.wr || !L.sh_g || !L.sh_u || !L.sh_d || !L.ex_g || !L.ex_u || !L.ex_d)
+      return DG_ERR_INVALID_ARG;
+  }
+  return DG_OK;
+}
+
+int check_cache(const dg_model_config* cfg, const dg_kv_cache* c, int batch) {
+  if (!c || !c->k || !c->v || c->batch != batch || c->capacity < 1 || c->length < 0 || c->length > c->capacity)
+    return DG_ERR_INVALID_ARG;
+  (void)cfg;
+  return DG_OK;
+}
+
+int check_canvas(const dg_canvas* cv, bool outputs) {
+  if (!cv || cv->batch < 1 || cv->canvas < 1 || cv->canvas > 1024 || !cv->tokens || !cv->seeds) return DG_ERR_INVALID_ARG;
+  if (outputs && (!cv->entropy || !cv->sample || !cv->argmax || !cv->prev_argmax || !cv->accepted || !cv->n_accepted ||
+                  !cv->mean_entropy || !cv->stop || !cv->flags))
+    return DG_ERR_INVALID_ARG;
+  if ((cv->p_side == nullptr) != (cv->p_scale == nullptr)) return DG_ERR_INVALID_ARG;
+  return DG_OK;
+}
+
+// Embedding + self-conditioning for the canvas tokens -> x, n.
+int embed_canvas(const Ctx& c, const dg_canvas* cv, const dg_step_params* p) {
+  const Shape& s = c.s;
+  const bool bf = s.dt == DG_DTYPE_BF16;
+  const int T = cv->batch * cv->canvas;
+  const bool ext = cv->sc_probs != nullptr;
+  const bool carried = !ext && p->t >= 1 && cv->p_side != nullptr;
+  const float* add = nullptr;
+  if (ext || carried) {
+    if (!c.w->embed_t || !c.w->sc_up || !c.w->sc_down) return DG_ERR_INVALID_ARG;
+    Phase ph(c, DG_PHASE_SELFCOND);
+    // expected embedding e_bar = P E (split over the vocabulary)
+    GemmArgs a = base_args();
+    if (ext) {
+      a.act = cv->sc_probs; a.act_kind = ACT_F32;
+    } else {
+      a.act = cv->p_side; a.act_kind = bf ? ACT_BF16_SCALED : ACT_F32;
+      a.act_scale = cv->p_scale; a.scale_ld = s.nvt;
+    }
+    a.act_ld = s.V;
+    a.w0 = c.w->embed_t;
+    a.epi = EPI_STORE_F32; a.out_f32 = c.at<float>(c.p.e_part); a.ldo = s.d; a.split_stride = (int64_t)T * s.d;
+    a.M = T; a.N = s.d; a.K = s.V; a.n_main = 1; a.kt_main = s.V / 32;
+    int n_split = 1;
+    if (bf) {
+      const int bm = 128, nwt = 2;
+      a.max_tiles = (T + bm - 1) / bm;
+      a.n_fb = (s.d + 64 * nwt - 1) / (64 * nwt);
+      a.tile_fastest = 0;
+      n_split = kMaxSplit;
+      a.k_split = ((s.V / 64 + n_split - 1) / n_split) * 64;
+      n_split = (s.V + a.k_split - 1) / a.k_split;
+      a.n_split = n_split;
+      DG_TRY(launch_wsgemm(a, bm, nwt, 64, false, c.st));
+    } else {
+      a.max_tiles = (T + kSimpleBM - 1) / kSimpleBM;
+      a.n_split = 1; a.k_split = s.V;
+      DG_TRY(launch_gemm_simple(a, c.st));
+    }
+    DG_TRY(launch_reduce_splits(bf, c.at<float>(c.p.e_part), n_split, (int64_t)T * s.d, (int64_t)T * s.d,
+                                c.at<void>(c.p.ebar), c.st));
+    GemmArgs u = base_args();
+    u.act = c.at<void>(c.p.ebar); u.act_ld = s.d; u.act_kind = bf ? ACT_BF16 : ACT_F32;
+    u.w0 = c.w->sc_up;
+    u.epi = EPI_GELU; u.out_act = c.at<void>(c.p.hsc); u.ldo = s.dsc;
+    DG_TRY(dense_gemm(c, u, T, s.dsc, s.d, 1));
+    GemmArgs dn = base_args();
+    dn.act = c.at<void>(c.p.hsc); dn.act_ld = s.dsc; dn.act_kind = bf ? ACT_BF16 : ACT_F32;
+    dn.w0 = c.w->sc_down;
+    dn.epi = EPI_STORE_F32; dn.out_f32 = c.at<float>(c.p.sc_out); dn.ldo = s.d; dn.split_stride = 0;
+    DG_TRY(dense_gemm(c, dn, T, s.d, s.dsc, 1));
+    add = c.at<float>(c.p.sc_out);
+  }
+  Phase ph(c, DG_PHASE_EMBED);
+  return launch_embed_norm(bf, cv->tokens, c.w->embed, add, c.at<float>(c.p.x), c.at<void>(c.p.n), T, s.d, s.eps, c.st);
+}
+
+// LM head + sampler statistics.  logits_out: test path (fp32 z written).
+int lm_head(const Ctx& c, const dg_canvas* cv, const dg_step_params* p, float* logits_out) {
+  Phase ph(c, DG_PHASE_LMHEAD);
+  const Shape& s = c.s;
+  const bool bf = s.dt == DG_DTYPE_BF16;
+  const int T = cv->batch * cv->canvas;
+  LmArgs lm;
+  memset(&lm, 0, sizeof(lm));
+  lm.part_f = c.at<float4>(c.p.lm_f);
+  lm.part_i = c.at<int2>(c.p.lm_i);
+  lm.p_side = logits_out ? nullptr : cv->p_side;
+  lm.p_side_f32 = !bf;
+  lm.logits = logits_out;
+  lm.inv_tau = 1.0f / dg_temperature(p->t, p->n_steps);
+  lm.seeds = cv->seeds;
+  lm.canvas = cv->canvas;
+  lm.step = p->t;
+  lm.block = p->block;
+  lm.vocab = s.V;
+  GemmArgs a = base_args();
+  a.act = c.at<void>(c.p.n); a.act_ld = s.d; a.act_kind = bf ? ACT_BF16 : ACT_F32;
+  a.w0 = c.w->lm_head;
+  a.alpha = c.w->lm_scale;
+  a.M = T; a.N = s.V; a.K = s.d; a.n_main = 1; a.kt_main = s.d / 32;
+  if (bf) {
+    a.max_tiles = (T + 127) / 128;
+    a.n_fb = s.nvt;
+    a.tile_fastest = 1;
+    a.k_split = s.d;
+    return launch_lmhead(a, lm, c.st);
+  }
+  float* z = logits_out ? logits_out : c.at<float>(c.p.logits);
+  a.epi = EPI_STORE_F32; a.out_f32 = z; a.ldo = s.V;
+  DG_TRY(dense_gemm(c, a, T, s.V, s.d, 1));
+  lm.logits = nullptr;
+  return launch_lm_partials_from_logits(z, T, lm, c.st);
+}
+
+int sample_and_select(const Ctx& c, dg_canvas* cv, const dg_step_params* p) {
+  Phase ph(c, DG_PHASE_SAMPLER);
+  const Shape& s = c.s;
+  const int T = cv->batch * cv->canvas;
+  DG_TRY(launch_row_merge(c.at<float4>(c.p.lm_f), c.at<int2>(c.p.lm_i), s.nvt, T, cv->canvas, cv->seeds, p->t,
+                          p->block, cv->entropy, cv->sample, cv->argmax, cv->p_scale, c.st));
+  return launch_select(cv->entropy, cv->sample, cv->argmax, cv->prev_argmax, cv->tokens, cv->accepted, cv->n_accepted,
+                       cv->mean_entropy, cv->stop, cv->flags, cv->seeds, cv->batch, cv->canvas, p->t, p->block, s.V,
+                       p->adaptive, p->entropy_bound, p->stop_threshold, c.st);
+}
+
+int check_step(const dg_step_params* p) {
+  if (!p || p->n_steps < 1 || p->t < 0 || p->t >= p->n_steps || p->block < 0) return DG_ERR_INVALID_ARG;
+  return DG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+float dg_temperature(int32_t t, int32_t n_steps) {
+  if (n_steps <= 1) return 0.8f;
+  return (float)(0.8 + (0.4 - 0.8) * ((double)t / (double)(n_steps - 1)));
+}
+
+size_t dg_workspace_bytes(const dg_model_config* cfg, int32_t batch, int32_t max_canvas) {
+  if (check_config(cfg) != DG_OK || batch < 1 || max_canvas < 1) return 0;
+  return make_plan(shape_of(cfg), batch, max_canvas).total;
+}
+
+int dg_pack_weight_bf16(void* d_dst, const void* d_src, int64_t rows, int64_t cols, void* stream) {
+  if (!d_dst || !d_src || rows <= 0 || cols <= 0 || rows % 16 || cols % 32) return DG_ERR_INVALID_ARG;
+  return launch_pack_bf16((bf16_t*)d_dst, (const bf16_t*)d_src, rows, cols, 0, (hipStream_t)stream) == 0 ? DG_OK
+                                                                                                          : DG_ERR_HIP;
+}
+
+int dg_pack_weight_bf16_transposed(void* d_dst, const void* d_src, int64_t rows, int64_t cols, void* stream) {
+  if (!d_dst || !d_src || rows <= 0 || cols <= 0 || rows % 16 || cols % 32) return DG_ERR_INVALID_ARG;
+  return launch_pack_bf16((bf16_t*)d_dst, (const bf16_t*)d_src, rows, cols, 1, (hipStream_t)stream) == 0 ? DG_OK
+                                                                                                          : DG_ERR_HIP;
+}
+
+int dg_init_canvas(const dg_model_config* cfg, dg_canvas* cv, int32_t block, void* stream) {
+  DG_TRY(check_config(cfg));
+  if (!cv || !cv->tokens || !cv->seeds || cv->batch < 1 || cv->canvas < 1 || block < 0) return DG_ERR_INVALID_ARG;
+  return launch_init_canvas(cv->tokens, cv->seeds, cv->batch, cv->canvas, block, cfg->vocab, (hipStream_t)stream) == 0
+             ? DG_OK
+             : DG_ERR_HIP;
+}
+
+int dg_encode_append(const dg_model_config* cfg, const dg_weights* w, dg_kv_cache* cache, const int32_t* d_tokens,
+                     int32_t batch, int32_t n_tokens, void* d_ws, size_t ws_bytes, void* stream) {
+  return dg_encode_append_traced(cfg, w, cache, d_tokens, batch, n_tokens, d_ws, ws_bytes, stream, nullptr);
+}
+
+int dg_encode_append_traced(const dg_model_config* cfg, const dg_weights* w, dg_kv_cache* cache,
+                            const int32_t* d_tokens, int32_t batch, int32_t n_tokens, void* d_ws, size_t ws_bytes,
+                            void* stream, dg_trace* trace) {
+  DG_TRY(check_config(cfg));
+  DG_TRY(check_weights(cfg, w));
+  if (batch < 1 || n_tokens < 1 || !d_tokens) return DG_ERR_INVALID_ARG;
+  DG_TRY(check_cache(cfg, cache, batch));
+  if ((int64_t)cache->length + n_tokens > cache->capacity) return DG_ERR_KV_CAPACITY;
+  Ctx c;
+  c.s = shape_of(cfg);
+  c.p = make_plan(c.s, batch, 1);
+  DG_TRY(check_ws(c.p, d_ws, ws_bytes));
+  const int chunk = std::max(1, std::min(c.p.T, kMaxRoutePairs / c.s.k) / batch);
+  c.ws = (char*)d_ws;
+  c.st = (hipStream_t)stream;
+  c.w = w;
+  c.tr = trace;
+  for (int done = 0; done < n_tokens; done += chunk) {
+    const int nc = std::min(chunk, n_tokens - done);
+    // gather this chunk's tokens [batch][nc] into the workspace token buffer
+    int32_t* tok = c.at<int32_t>(c.p.ids);  // reused: ids are rewritten per layer after embedding
+    for (int b = 0; b < batch; ++b)
+      DG_TRY(launch_copy_i32(tok + b * nc, d_tokens + (int64_t)b * n_tokens + done, nc, c.st));
+    DG_TRY(launch_embed_norm(c.s.dt == DG_DTYPE_BF16, tok, w->embed, nullptr, c.at<float>(c.p.x), c.at<void>(c.p.n),
+                             batch * nc, c.s.d, c.s.eps, c.st));
+    DG_TRY(run_layers(c, cache, batch, nc, cache->length, true));
+    cache->length += nc;
+  }
+  return DG_OK;
+}
+
+int dg_denoise_step(const dg_model_config* cfg, const dg_weights* w, const dg_kv_cache* cache, dg_canvas* cv,
+                    const dg_step_params* p, void* d_ws, size_t ws_bytes, void* stream) {
+  return dg_denoise_step_traced(cfg, w, cache, cv, p, d_ws, ws_bytes, stream, nullptr);
+}
+
+int dg_denoise_step_traced(const dg_model_config* cfg, const dg_weights* w, const dg_kv_cache* cache, dg_canvas* cv,
+                           const dg_step_params* p, void* d_ws, size_t ws_bytes, void* stream, dg_trace* trace) {
+  DG_TRY(check_config(cfg));
+  DG_TRY(check_weights(cfg, w));
+  DG_TRY(check_canvas(cv, true));
+  DG_TRY(check_step(p));
+  DG_TRY(check_cache(cfg, cache, cv->batch));
+  Ctx c;
+  c.s = shape_of(cfg);
+  c.p = make_plan(c.s, cv->batch, cv->canvas);
+  DG_TRY(check_ws(c.p, d_ws, ws_bytes));
+  if ((int64_t)cv->batch * cv->canvas * c.s.k > kMaxRoutePairs) return DG_ERR_UNSUPPORTED;
+  c.ws = (char*)d_ws;
+  c.st = (hipStream_t)stream;
+  c.w = w;
+  if (trace && (!trace->events || !trace->phase || trace->capacity < 0)) return DG_ERR_INVALID_ARG;
+  c.tr = trace;
+  DG_TRY(embed_canvas(c, cv, p));
+  DG_TRY(run_layers(c, cache, cv->batch, cv->canvas, cache->length, false));
+  DG_TRY(lm_head(c, cv, p, nullptr));
+  return sample_and_select(c, cv, p);
+}
+
+int dg_commit_block(const dg_model_config* cfg, const dg_weights* w, dg_kv_cache* cache, dg_canvas* cv,
+                    const dg_step_params* p, void* d_ws, size_t ws_bytes, void* stream) {
+  DG_TRY(check_config(cfg));
+  DG_TRY(check_canvas(cv, true));
+  DG_TRY(check_step(p));
+  if (!cv->committed) return DG_ERR_INVALID_ARG;
+  DG_TRY(check_cache(cfg, cache, cv->batch));
+  if ((int64_t)cache->length + cv->canvas > cache->capacity) return DG_ERR_KV_CAPACITY;
+  const int T = cv->batch * cv->canvas;
+  DG_TRY(launch_copy_i32(cv->committed, cv->argmax, T, (hipStream_t)stream));
+  DG_TRY(dg_encode_append(cfg, w, cache, cv->committed, cv->batch, cv->canvas, d_ws, ws_bytes, stream));
+  return launch_init_canvas(cv->tokens, cv->seeds, cv->batch, cv->canvas, p->block + 1, cfg->vocab,
+                            (hipStream_t)stream) == 0
+             ? DG_OK
+             : DG_ERR_HIP;
+}
+
+const char* dg_status_string(int status) {
+  switch (status) {
+    case DG_OK: return "ok";
+    case DG_ERR_INVALID_ARG: return "invalid argument";
+    case DG_ERR_UNSUPPORTED: return "unsupported configuration";
+    case DG_ERR_KV_CAPACITY: return "KV cache capacity exceeded";
+    case DG_ERR_WORKSPACE: return "workspace too small";
+    case DG_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int dg_test_sample_from_logits(const dg_model_config* cfg, const float* d_logits, dg_canvas* cv,
+                               const dg_step_params* p, void* d_ws, size_t ws_bytes, void* stream) {
+  DG_TRY(check_config(cfg));
+  DG_TRY(check_canvas(cv, true));
+  DG_TRY(check_step(p));
+  if (!d_logits) return DG_ERR_INVALID_ARG;
+  Ctx c;
+  c.s = shape_of(cfg);
+  c.p = make_plan(c.s, cv->batch, cv->canvas);
+  DG_TRY(check_ws(c.p, d_ws, ws_bytes));
+  c.ws = (char*)d_ws;
+  c.st = (hipStream_t)stream;
+  c.w = nullptr;
+  LmArgs lm;
+  memset(&lm, 0, sizeof(lm));
+  lm.part_f = c.at<float4>(c.p.lm_f);
+  lm.part_i = c.at<int2>(c.p.lm_i);
+  lm.p_side = cv->p_side;
+  lm.p_side_f32 = cfg->dtype != DG_DTYPE_BF16;
+  lm.inv_tau = 1.0f / dg_temperature(p->t, p->n_steps);
+  lm.seeds = cv->seeds;
+  lm.canvas = cv->canvas;
+  lm.step = p->t;
+  lm.block = p->block;
+  lm.vocab = c.s.V;
+  DG_TRY(launch_lm_partials_from_logits(d_logits, cv->batch * cv->canvas, lm, c.st));
+  return sample_and_select(c, cv, p);
+}
+
+int dg_test_route_from_logits(const dg_model_config* cfg, const float* d_logits, int32_t T, int32_t* d_ids, float* d_w,
+                              int32_t* d_row_token, int32_t* d_inv, int32_t* d_offsets, void* d_ws, size_t ws_bytes,
+                              void* stream) {
+  DG_TRY(check_config(cfg));
+  if (!d_logits || !d_ids || !d_w || !d_row_token || !d_inv || !d_offsets || T < 1) return DG_ERR_INVALID_ARG;
+  const Shape s = shape_of(cfg);
+  if ((int64_t)T * s.k > kMaxRoutePairs) return DG_ERR_UNSUPPORTED;
+  const Plan p = make_plan(s, 1, T);
+  DG_TRY(check_ws(p, d_ws, ws_bytes));
+  char* ws = (char*)d_ws;
+  hipStream_t st = (hipStream_t)stream;
+  const int bm = s.dt == DG_DTYPE_BF16 ? kMoeBM : kSimpleBM;
+  DG_TRY(launch_topk(d_logits, 1, 0, T, s.E, s.k, nullptr, d_ids, d_w, st));
+  DG_TRY(launch_route_sort(d_ids, T, s.k, s.E, s.n_sh, bm, d_row_token, d_inv, d_offsets,
+                           reinterpret_cast<GemmTile*>(ws + p.tiles), reinterpret_cast<int32_t*>(ws + p.n_tiles), st));
+  return DG_OK;
+}
+
+int dg_test_forward_logits(const dg_model_config* cfg, const dg_weights* w, const dg_kv_cache* cache, dg_canvas* cv,
+                           const dg_step_params* p, const int32_t* d_force_ids, float* d_logits, void* d_ws,
+                           size_t ws_bytes, void* stream) {
+  DG_TRY(check_config(cfg));
+  DG_TRY(check_weights(cfg, w));
+  DG_TRY(check_canvas(cv, false));
+  DG_TRY(check_step(p));
+  DG_TRY(check_cache(cfg, cache, cv->batch));
+  if (!d_logits) return DG_ERR_INVALID_ARG;
+  Ctx c;
+  c.s = shape_of(cfg);
+  c.p = make_plan(c.s, cv->batch, cv->canvas);
+  DG_TRY(check_ws(c.p, d_ws, ws_bytes));
+  c.ws = (char*)d_ws;
+  c.st = (hipStream_t)stream;
+  c.w = w;
+  c.force_ids = d_force_ids;
+  DG_TRY(embed_canvas(c, cv, p));
+  DG_TRY(run_layers(c, cache, cv->batch, cv->canvas, cache->length, false));
+  return lm_head(c, cv, p, d_logits);
+}
+
+}  // extern "C"

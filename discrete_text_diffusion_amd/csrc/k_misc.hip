@@ -1,0 +1,164 @@
+// Row-wise kernels of the denoising step: token embedding (+ self-conditioning
+// term), RMSNorm (gain 1) fused with residual updates, the fixed-order MoE
+// combine, split-K reductions and the initial canvas noise.
+#include "dg_internal.h"
+
+namespace {
+
+// Deterministic block sum (256 threads): butterfly inside waves, then the 4
+// wave sums in wave order.
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  return ((red[0] + red[1]) + red[2]) + red[3];
+}
+
+template <typename TA>
+__device__ __forceinline__ void write_norm(const float* x, TA* n, int d, float eps, float* red) {
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < d; i += 256) ss = fmaf(x[i], x[i], ss);
+  const float tot = block_sum256(ss, red);
+  const float inv = 1.0f / sqrtf(tot / (float)d + eps);
+  for (int i = threadIdx.x; i < d; i += 256) n[i] = to_act<TA>(x[i] * inv);
+}
+
+// x[t] = E[tok[t]] (+ add[t]); n[t] = RMSNorm(x[t]).
+template <typename TA>
+__global__ __launch_bounds__(256) void k_embed_norm(const int32_t* tok, const TA* emb, const float* add, float* x,
+                                                   TA* n, int d, float eps) {
+  __shared__ float red[4];
+  const int64_t t = blockIdx.x;
+  const TA* e = emb + (int64_t)tok[t] * d;
+  float* xr = x + t * d;
+  for (int i = threadIdx.x; i < d; i += 256) {
+    float v = ld_act<TA>(e + i);
+    if (add) v += add[t * d + i];
+    xr[i] = v;
+  }
+  __syncthreads();
+  write_norm<TA>(xr, n + t * d, d, eps, red);
+}
+
+// x[t] += sum_s part[s][t] (split order); n[t] = RMSNorm(x[t]).
+template <typename TA>
+__global__ __launch_bounds__(256) void k_resid_norm(float* x, const float* part, int n_split, int64_t split_stride,
+                                                   TA* n, int d, float eps) {
+  __shared__ float red[4];
+  const int64_t t = blockIdx.x;
+  float* xr = x + t * d;
+  for (int i = threadIdx.x; i < d; i += 256) {
+    float acc = 0.f;
+    for (int s = 0; s < n_split; ++s) acc += part[(int64_t)s * split_stride + t * d + i];
+    xr[i] += acc;
+  }
+  __syncthreads();
+  write_norm<TA>(xr, n + t * d, d, eps, red);
+}
+
+// y_t = sum_c Y[T*k + c*T + t] (shared-expert slices) + sum_j w[t][j] Y[inv[t*k+j]]
+// in rank order; x[t] += y_t; n[t] = RMSNorm(x[t]).
+template <typename TA>
+__global__ __launch_bounds__(256) void k_combine_norm(float* x, const float* Y, const int32_t* inv, const float* w,
+                                                     int T, int k, int n_sh, TA* n, int d, float eps) {
+  __shared__ float red[4];
+  __shared__ int32_t rows[16];
+  __shared__ float wts[16];
+  const int64_t t = blockIdx.x;
+  if (threadIdx.x < k) {
+    rows[threadIdx.x] = inv[t * k + threadIdx.x];
+    wts[threadIdx.x] = w[t * k + threadIdx.x];
+  }
+  __syncthreads();
+  float* xr = x + t * d;
+  const int64_t sh0 = (int64_t)T * k;
+  for (int i = threadIdx.x; i < d; i += 256) {
+    float y = 0.f;
+    for (int c = 0; c < n_sh; ++c) y += Y[(sh0 + (int64_t)c * T + t) * d + i];
+    for (int j = 0; j < k; ++j) y = fmaf(wts[j], Y[(int64_t)rows[j] * d + i], y);
+    xr[i] += y;
+  }
+  __syncthreads();
+  write_norm<TA>(xr, n + t * d, d, eps, red);
+}
+
+// out[t][i] = act(sum_s part[s][t][i]) (split order).
+template <typename TA>
+__global__ __launch_bounds__(256) void k_reduce_splits(const float* part, int n_split, int64_t split_stride,
+                                                      int64_t n_elems, TA* out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_elems) return;
+  float acc = 0.f;
+  for (int s = 0; s < n_split; ++s) acc += part[(int64_t)s * split_stride + i];
+  out[i] = to_act<TA>(acc);
+}
+
+// tokens[b][i] = uniform token from Philox stream 0 (step field 0) of canvas b.
+__global__ __launch_bounds__(256) void k_init_canvas(int32_t* tokens, const uint64_t* seeds, int B, int C, int block,
+                                                    uint32_t vocab) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= B * C) return;
+  const int b = i / C, pos = i - b * C;
+  const uint64_t sd = seeds[b];
+  const dg_u32x4 w = dg_philox((uint32_t)pos, 0u, (uint32_t)block, DG_STREAM_INIT, (uint32_t)sd, (uint32_t)(sd >> 32));
+  tokens[i] = dg_word_token(w.x, vocab);
+}
+
+// Small device-side copy (kept as a kernel so captured graphs hold no memcpy nodes).
+__global__ __launch_bounds__(256) void k_copy_i32(int32_t* dst, const int32_t* src, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) dst[i] = src[i];
+}
+
+}  // namespace
+
+#define DG_OK_OR_HIP() (hipGetLastError() == hipSuccess ? 0 : -5)
+
+int launch_embed_norm(int dtype, const int32_t* tok, const void* emb, const float* add, float* x, void* n, int T,
+                      int d, float eps, hipStream_t s) {
+  if (dtype == 1)
+    hipLaunchKernelGGL(k_embed_norm<bf16_t>, dim3(T), dim3(256), 0, s, tok, (const bf16_t*)emb, add, x, (bf16_t*)n, d, eps);
+  else
+    hipLaunchKernelGGL(k_embed_norm<float>, dim3(T), dim3(256), 0, s, tok, (const float*)emb, add, x, (float*)n, d, eps);
+  return DG_OK_OR_HIP();
+}
+
+int launch_resid_norm(int dtype, float* x, const float* part, int n_split, int64_t split_stride, void* n, int T, int d,
+                      float eps, hipStream_t s) {
+  if (dtype == 1)
+    hipLaunchKernelGGL(k_resid_norm<bf16_t>, dim3(T), dim3(256), 0, s, x, part, n_split, split_stride, (bf16_t*)n, d, eps);
+  else
+    hipLaunchKernelGGL(k_resid_norm<float>, dim3(T), dim3(256), 0, s, x, part, n_split, split_stride, (float*)n, d, eps);
+  return DG_OK_OR_HIP();
+}
+
+int launch_combine_norm(int dtype, float* x, const float* Y, const int32_t* inv, const float* w, int T, int k, int n_sh,
+                        void* n, int d, float eps, hipStream_t s) {
+  if (k > 16) return -1;
+  if (dtype == 1)
+    hipLaunchKernelGGL(k_combine_norm<bf16_t>, dim3(T), dim3(256), 0, s, x, Y, inv, w, T, k, n_sh, (bf16_t*)n, d, eps);
+  else
+    hipLaunchKernelGGL(k_combine_norm<float>, dim3(T), dim3(256), 0, s, x, Y, inv, w, T, k, n_sh, (float*)n, d, eps);
+  return DG_OK_OR_HIP();
+}
+
+int launch_reduce_splits(int dtype, const float* part, int n_split, int64_t split_stride, int64_t n_elems, void* out,
+                         hipStream_t s) {
+  const dim3 g((unsigned)DG_CEIL_DIV(n_elems, 256));
+  if (dtype == 1) hipLaunchKernelGGL(k_reduce_splits<bf16_t>, g, dim3(256), 0, s, part, n_split, split_stride, n_elems, (bf16_t*)out);
+  else hipLaunchKernelGGL(k_reduce_splits<float>, g, dim3(256), 0, s, part, n_split, split_stride, n_elems, (float*)out);
+  return DG_OK_OR_HIP();
+}
+
+int launch_init_canvas(int32_t* tokens, const uint64_t* seeds, int B, int C, int block, int vocab, hipStream_t s) {
+  hipLaunchKernelGGL(k_init_canvas, dim3(DG_CEIL_DIV(B * C, 256)), dim3(256), 0, s, tokens, seeds, B, C, block,
+                     (uint32_t)vocab);
+  return DG_OK_OR_HIP();
+}
+
+int launch_copy_i32(int32_t* dst, const int32_t* src, int n, hipStream_t s) {
+  hipLaunchKernelGGL(k_copy_i32, dim3(DG_CEIL_DIV(n, 256)), dim3(256), 0, s, dst, src, n);
+  return DG_OK_OR_HIP();
+}

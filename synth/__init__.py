@@ -143,3 +143,58 @@ def tokens_np(seed: int, tensor: int, n: int, vocab: int, start: int = 0) -> np.
     hi = z >> np.uint64(32)
     with np.errstate(over="ignore"):
         return ((hi * np.uint64(vocab)) >> np.uint64(32)).astype(np.int32)
+
+
+# ---- device twin (gen_dev.hip): fills device buffers in place ----
+_DEV_LIB_PATH = os.path.join(_HERE, "libdgsynth_dev.so")
+_dev_lib = None
+
+
+def build_dev(arch: str = "gfx950") -> str:
+    src = os.path.join(_HERE, "gen_dev.hip")
+    subprocess.check_call(["/opt/rocm/bin/hipcc", f"--offload-arch={arch}", "-O3", "-fPIC", "-shared",
+                           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                           src, "-o", _DEV_LIB_PATH + ".tmp"])
+    os.replace(_DEV_LIB_PATH + ".tmp", _DEV_LIB_PATH)
+    return _DEV_LIB_PATH
+
+
+def _get_dev_lib():
+    global _dev_lib
+    if _dev_lib is None:
+        if not os.path.exists(_DEV_LIB_PATH):
+            raise ImportError(f"{_DEV_LIB_PATH} missing: run synth.build_dev()")
+        lib = ctypes.CDLL(_DEV_LIB_PATH)
+        u64, vp = ctypes.c_uint64, ctypes.c_void_p
+        lib.synth_dev_normal_bf16.argtypes = [vp, u64, u64, u64, u64, ctypes.c_float, vp]
+        lib.synth_dev_normal_f32.argtypes = [vp, u64, u64, u64, u64, ctypes.c_float, vp]
+        lib.synth_dev_tokens.argtypes = [vp, u64, u64, u64, u64, ctypes.c_uint32, vp]
+        lib.synth_dev_normal_f32_transposed.argtypes = [vp, u64, u64, u64, u64, ctypes.c_float, vp]
+        for f in (lib.synth_dev_normal_bf16, lib.synth_dev_normal_f32, lib.synth_dev_tokens,
+                  lib.synth_dev_normal_f32_transposed):
+            f.restype = ctypes.c_int
+        _dev_lib = lib
+    return _dev_lib
+
+
+def dev_normal(ptr: int, count: int, seed: int, tensor: int, std: float, dtype: str, stream: int,
+               start: int = 0) -> None:
+    """Fill `count` elements at device address `ptr` (bf16 bits or fp32)."""
+    lib = _get_dev_lib()
+    sc = ctypes.c_float(scale_for_std(std))
+    f = lib.synth_dev_normal_bf16 if dtype == "bf16" else lib.synth_dev_normal_f32
+    if f(ptr, seed, tensor, start, count, sc, stream) != 0:
+        raise RuntimeError("synth device fill failed")
+
+
+def dev_tokens(ptr: int, count: int, seed: int, tensor: int, vocab: int, stream: int, start: int = 0) -> None:
+    if _get_dev_lib().synth_dev_tokens(ptr, seed, tensor, start, count, vocab, stream) != 0:
+        raise RuntimeError("synth device tokens failed")
+
+
+def dev_normal_f32_transposed(ptr: int, rows: int, cols: int, seed: int, tensor: int, std: float,
+                              stream: int) -> None:
+    """fp32 fill of the transpose of the logical [rows][cols] tensor `tensor`."""
+    sc = ctypes.c_float(scale_for_std(std))
+    if _get_dev_lib().synth_dev_normal_f32_transposed(ptr, seed, tensor, rows, cols, sc, stream) != 0:
+        raise RuntimeError("synth device fill failed")

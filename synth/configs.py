@@ -93,6 +93,12 @@ FULL_30 = replace(FULL_LAYER, n_layers=30)
 
 FULL_LAYER_FP8 = replace(FULL_LAYER, expert_dtype="fp8", lm_dtype="fp8")
 
+# Small bf16 shape for parity tests of the MFMA path: several K chunks, 16
+# vocabulary tiles, ragged expert segments, a shared expert split in two
+# d_expert-wide slices.  Not one of the pages' workloads.
+MINI_BF16 = ModelShape(n_layers=2, d_model=256, n_q_heads=2, n_kv_heads=1, d_head=256, n_experts=16,
+                       top_k=4, d_expert=128, d_shared=256, vocab=4096, d_selfcond=128)
+
 WORKLOADS = {
     # 2-layer fp32 denoiser; prefix 64 encoded causally; canvas 32; <=48 adaptive steps.
     "tiny": Workload("tiny", TINY, batch=1, canvas=32, prefix=64, n_steps=48, adaptive=True,
