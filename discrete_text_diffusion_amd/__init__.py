@@ -113,7 +113,7 @@ _t_sample = _sig("dg_test_sample_from_logits", c_int32, _P(ModelConfig), c_void_
 _t_route = _sig("dg_test_route_from_logits", c_int32, _P(ModelConfig), c_void_p, c_int32, c_void_p, c_void_p,
                 c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p)
 _t_logits = _sig("dg_test_forward_logits", c_int32, _P(ModelConfig), _P(Weights), _P(KVCache), _P(Canvas),
-                 _P(StepParams), c_void_p, c_void_p, c_void_p, c_size_t, c_void_p)
+                 _P(StepParams), c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p)
 
 EXPORTED = ("dg_temperature", "dg_workspace_bytes", "dg_pack_weight_bf16", "dg_pack_weight_bf16_transposed",
             "dg_init_canvas", "dg_encode_append", "dg_denoise_step", "dg_commit_block", "dg_status_string",
@@ -176,10 +176,11 @@ def dg_test_route_from_logits(cfg, d_logits, T: int, ids, w, row_token, inv, off
            "dg_test_route_from_logits")
 
 
-def dg_test_forward_logits(cfg, weights, cache, canvas, params, d_force_ids, d_logits, ws, ws_bytes: int,
-                           stream) -> None:
+def dg_test_forward_logits(cfg, weights, cache, canvas, params, d_force_ids, d_router_logits, d_logits, ws,
+                           ws_bytes: int, stream) -> None:
     _check(_t_logits(ctypes.byref(cfg), ctypes.byref(weights), ctypes.byref(cache), ctypes.byref(canvas),
-                     ctypes.byref(params), d_force_ids, d_logits, ws, ws_bytes, stream), "dg_test_forward_logits")
+                     ctypes.byref(params), d_force_ids, d_router_logits, d_logits, ws, ws_bytes, stream),
+           "dg_test_forward_logits")
 
 
 def dg_denoise_step_traced(cfg, weights, cache, canvas, params, ws, ws_bytes: int, stream, trace) -> None:

@@ -59,9 +59,10 @@ int check_config(const dg_model_config* c) {
   return DG_OK;
 }
 
-// Token capacity of one pass through the layer stack.
+// Token capacity of one pass through the layer stack (the routing sort
+// handles up to route_max_tokens() tokens at a time).
 int max_tokens(const Shape& s, int batch, int max_canvas) {
-  const int route_cap = kMaxRoutePairs / s.k;
+  const int route_cap = std::min(kMaxRoutePairs / s.k, route_max_tokens());
   return std::max(std::min(2048, route_cap), batch * max_canvas);
 }
 
@@ -121,6 +122,7 @@ struct Ctx {
   const dg_weights* w;
   dg_trace* tr = nullptr;
   const int32_t* force_ids = nullptr;  // test path: [n_layers][T][k] expert ids
+  float* router_out = nullptr;         // test path: [n_layers][T][E] router logits
   template <typename T> T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
 };
 
@@ -150,8 +152,11 @@ GemmArgs base_args() {
   return a;
 }
 
+// Enough workgroups to keep ~4 waves per SIMD streaming weights.
+constexpr int kTargetBlocks = 1024;
+
 int pick_split(int blocks_per_split, int K, int kc, int max_split) {
-  int sp = std::max(1, std::min(max_split, (512 + blocks_per_split - 1) / std::max(1, blocks_per_split)));
+  int sp = std::max(1, std::min(max_split, (kTargetBlocks + blocks_per_split - 1) / std::max(1, blocks_per_split)));
   while (sp > 1 && (K / kc) < sp) --sp;
   return sp;
 }
@@ -164,10 +169,16 @@ int dense_gemm(const Ctx& c, GemmArgs a, int M, int N, int K, int max_split, int
   a.n_main = 1;
   if (used_split) *used_split = 1;
   if (c.s.dt == DG_DTYPE_BF16) {
-    const int bm = 128, nwt = 1;
+    // largest row tile that still gives enough workgroups (weights re-read
+    // by the other row tiles of a feature block come from L2: tile_fastest)
+    const int nwt = 1;
+    a.n_fb = (N + 64 * nwt - 1) / (64 * nwt);
+    int bm = 32;
+    for (int cand : {128, 64}) {
+      if (((M + cand - 1) / cand) * a.n_fb >= kTargetBlocks) { bm = cand; break; }
+    }
     a.kt_main = K / 32;
     a.max_tiles = (M + bm - 1) / bm;
-    a.n_fb = (N + 64 * nwt - 1) / (64 * nwt);
     a.tile_fastest = 1;
     int sp = (a.epi == EPI_STORE_F32) ? pick_split(a.max_tiles * a.n_fb, K, 64, max_split) : 1;
     a.k_split = ((K / 64 + sp - 1) / sp) * 64;
@@ -215,9 +226,11 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
       q.q_dim = s.qdim; q.kv_dim = s.kvdim; q.d_head = s.dh; q.n_kv = s.nkv;
       if (causal) {
         q.k = kc; q.v = vc; q.kv_b_stride = c_seq; q.kv_h_stride = c_head; q.kv_row0 = L;
+        q.v_pitch = cache->capacity;
       } else {
         q.k = c.at<void>(c.p.ckv_k); q.v = c.at<void>(c.p.ckv_v);
         q.kv_b_stride = w_seq; q.kv_h_stride = w_head; q.kv_row0 = 0;
+        q.v_pitch = seq_len;
       }
       q.seq_len = seq_len; q.pos0 = L; q.rope_base = s.rope_base;
       DG_TRY(dense_gemm(c, a, T, s.qkv, s.d, 1));
@@ -228,20 +241,21 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
       const int n_keys = L + seq_len;
       int split = 1;
       if (bf) {
-        split = std::min(kMaxSplit, std::max(1, (n_keys + 255) / 256));
-        split = std::min(split, std::max(1, c.p.att_rows / T));
         const int G = s.nq / s.nkv;
-        const int base_blocks = n_seq * s.nkv * ((seq_len + 64 / G - 1) / (64 / G));
-        split = std::min(split, std::max(1, (1024 + base_blocks - 1) / base_blocks));
+        const int base_blocks = n_seq * s.nkv * ((seq_len + 128 / G - 1) / (128 / G));
+        split = std::max(1, (256 + base_blocks - 1) / base_blocks);         // ~1 workgroup (8 waves) per CU
+        split = std::min(split, std::max(1, (n_keys + 255) / 256));         // >= 4 key tiles per split
+        split = std::min(split, std::min(kMaxSplit, std::max(1, c.p.att_rows / T)));
       }
       if (causal) {
-        DG_TRY(launch_attention(bf, c.at<void>(c.p.q), s.qdim, kc, vc, c_seq, c_head, L + seq_len, nullptr, nullptr, 0,
-                                0, 0, L, 1, seq_len, n_seq, s.nq, s.nkv, s.dh, split, c.at<float>(c.p.att_o),
-                                c.at<float2>(c.p.att_ml), c.at<void>(c.p.o), c.st));
+        DG_TRY(launch_attention(bf, c.at<void>(c.p.q), s.qdim, kc, vc, c_seq, c_head, cache->capacity, L + seq_len,
+                                nullptr, nullptr, 0, 0, 1, 0, L, 1, seq_len, n_seq, s.nq, s.nkv, s.dh, split,
+                                c.at<float>(c.p.att_o), c.at<float2>(c.p.att_ml), c.at<void>(c.p.o), c.st));
       } else {
-        DG_TRY(launch_attention(bf, c.at<void>(c.p.q), s.qdim, kc, vc, c_seq, c_head, L, c.at<void>(c.p.ckv_k),
-                                c.at<void>(c.p.ckv_v), w_seq, w_head, seq_len, L, 0, seq_len, n_seq, s.nq, s.nkv, s.dh,
-                                split, c.at<float>(c.p.att_o), c.at<float2>(c.p.att_ml), c.at<void>(c.p.o), c.st));
+        DG_TRY(launch_attention(bf, c.at<void>(c.p.q), s.qdim, kc, vc, c_seq, c_head, cache->capacity, L,
+                                c.at<void>(c.p.ckv_k), c.at<void>(c.p.ckv_v), w_seq, w_head, seq_len, seq_len, L, 0,
+                                seq_len, n_seq, s.nq, s.nkv, s.dh, split, c.at<float>(c.p.att_o),
+                                c.at<float2>(c.p.att_ml), c.at<void>(c.p.o), c.st));
       }
     }
     // O projection (split-K partials), residual, RMSNorm
@@ -267,8 +281,9 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
       a.epi = EPI_STORE_F32; a.out_f32 = c.at<float>(c.p.r_part); a.ldo = s.E; a.split_stride = (int64_t)T * s.E;
       DG_TRY(dense_gemm(c, a, T, s.E, s.d, 8, &r_split));
       const int32_t* forced = c.force_ids ? c.force_ids + (int64_t)l * T * s.k : nullptr;
+      float* r_out = c.router_out ? c.router_out + (int64_t)l * T * s.E : nullptr;
       DG_TRY(launch_topk(c.at<float>(c.p.r_part), r_split, (int64_t)T * s.E, T, s.E, s.k, forced,
-                         c.at<int32_t>(c.p.ids), c.at<float>(c.p.wts), c.st));
+                         c.at<int32_t>(c.p.ids), c.at<float>(c.p.wts), r_out, c.st));
       DG_TRY(launch_route_sort(c.at<int32_t>(c.p.ids), T, s.k, s.E, s.n_sh, bm, c.at<int32_t>(c.p.row_token),
                                c.at<int32_t>(c.p.inv), c.at<int32_t>(c.p.offsets), c.at<GemmTile>(c.p.tiles),
                                c.at<int32_t>(c.p.n_tiles), c.st));
@@ -291,7 +306,8 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
       if (bf) {
         a.n_fb = (s.de + 63) / 64;
         a.tile_fastest = 0;
-        DG_TRY(launch_wsgemm(a, kMoeBM, 1, 64, true, c.st));
+        // 128-wide K chunks keep twice the weight bytes in flight per wave
+        DG_TRY(launch_wsgemm(a, kMoeBM, 1, s.d % 128 == 0 ? 128 : 64, true, c.st));
       } else {
         DG_TRY(launch_gemm_simple(a, c.st));
       }
@@ -385,9 +401,9 @@ int embed_canvas(const Ctx& c, const dg_canvas* cv, const dg_step_params* p) {
       const int bm = 128, nwt = 2;
       a.max_tiles = (T + bm - 1) / bm;
       a.n_fb = (s.d + 64 * nwt - 1) / (64 * nwt);
-      a.tile_fastest = 0;
+      a.tile_fastest = 1;  // the row tiles of one E^T slice run together: E^T comes from HBM once
       n_split = kMaxSplit;
-      a.k_split = ((s.V / 64 + n_split - 1) / n_split) * 64;
+      a.k_split = ((s.V / 256 + n_split - 1) / n_split) * 256;  // whole 256-wide vocabulary tiles
       n_split = (s.V + a.k_split - 1) / a.k_split;
       a.n_split = n_split;
       DG_TRY(launch_wsgemm(a, bm, nwt, 64, false, c.st));
@@ -439,11 +455,12 @@ int lm_head(const Ctx& c, const dg_canvas* cv, const dg_step_params* p, float* l
   a.alpha = c.w->lm_scale;
   a.M = T; a.N = s.V; a.K = s.d; a.n_main = 1; a.kt_main = s.d / 32;
   if (bf) {
-    a.max_tiles = (T + 127) / 128;
+    const int bm = 64;  // 64-row tiles keep several waves per SIMD streaming; other row tiles hit L2
+    a.max_tiles = (T + bm - 1) / bm;
     a.n_fb = s.nvt;
     a.tile_fastest = 1;
     a.k_split = s.d;
-    return launch_lmhead(a, lm, c.st);
+    return launch_lmhead(a, lm, bm, c.st);
   }
   float* z = logits_out ? logits_out : c.at<float>(c.p.logits);
   a.epi = EPI_STORE_F32; a.out_f32 = z; a.ldo = s.V;
@@ -519,7 +536,7 @@ int dg_encode_append_traced(const dg_model_config* cfg, const dg_weights* w, dg_
   c.s = shape_of(cfg);
   c.p = make_plan(c.s, batch, 1);
   DG_TRY(check_ws(c.p, d_ws, ws_bytes));
-  const int chunk = std::max(1, std::min(c.p.T, kMaxRoutePairs / c.s.k) / batch);
+  const int chunk = std::max(1, std::min(c.p.T, std::min(kMaxRoutePairs / c.s.k, route_max_tokens())) / batch);
   c.ws = (char*)d_ws;
   c.st = (hipStream_t)stream;
   c.w = w;
@@ -554,7 +571,8 @@ int dg_denoise_step_traced(const dg_model_config* cfg, const dg_weights* w, cons
   c.s = shape_of(cfg);
   c.p = make_plan(c.s, cv->batch, cv->canvas);
   DG_TRY(check_ws(c.p, d_ws, ws_bytes));
-  if ((int64_t)cv->batch * cv->canvas * c.s.k > kMaxRoutePairs) return DG_ERR_UNSUPPORTED;
+  if ((int64_t)cv->batch * cv->canvas * c.s.k > kMaxRoutePairs || cv->batch * cv->canvas > route_max_tokens())
+    return DG_ERR_UNSUPPORTED;
   c.ws = (char*)d_ws;
   c.st = (hipStream_t)stream;
   c.w = w;
@@ -630,21 +648,21 @@ int dg_test_route_from_logits(const dg_model_config* cfg, const float* d_logits,
   DG_TRY(check_config(cfg));
   if (!d_logits || !d_ids || !d_w || !d_row_token || !d_inv || !d_offsets || T < 1) return DG_ERR_INVALID_ARG;
   const Shape s = shape_of(cfg);
-  if ((int64_t)T * s.k > kMaxRoutePairs) return DG_ERR_UNSUPPORTED;
+  if ((int64_t)T * s.k > kMaxRoutePairs || T > route_max_tokens()) return DG_ERR_UNSUPPORTED;
   const Plan p = make_plan(s, 1, T);
   DG_TRY(check_ws(p, d_ws, ws_bytes));
   char* ws = (char*)d_ws;
   hipStream_t st = (hipStream_t)stream;
   const int bm = s.dt == DG_DTYPE_BF16 ? kMoeBM : kSimpleBM;
-  DG_TRY(launch_topk(d_logits, 1, 0, T, s.E, s.k, nullptr, d_ids, d_w, st));
+  DG_TRY(launch_topk(d_logits, 1, 0, T, s.E, s.k, nullptr, d_ids, d_w, nullptr, st));
   DG_TRY(launch_route_sort(d_ids, T, s.k, s.E, s.n_sh, bm, d_row_token, d_inv, d_offsets,
                            reinterpret_cast<GemmTile*>(ws + p.tiles), reinterpret_cast<int32_t*>(ws + p.n_tiles), st));
   return DG_OK;
 }
 
 int dg_test_forward_logits(const dg_model_config* cfg, const dg_weights* w, const dg_kv_cache* cache, dg_canvas* cv,
-                           const dg_step_params* p, const int32_t* d_force_ids, float* d_logits, void* d_ws,
-                           size_t ws_bytes, void* stream) {
+                           const dg_step_params* p, const int32_t* d_force_ids, float* d_router_logits,
+                           float* d_logits, void* d_ws, size_t ws_bytes, void* stream) {
   DG_TRY(check_config(cfg));
   DG_TRY(check_weights(cfg, w));
   DG_TRY(check_canvas(cv, false));
@@ -659,6 +677,7 @@ int dg_test_forward_logits(const dg_model_config* cfg, const dg_weights* w, cons
   c.st = (hipStream_t)stream;
   c.w = w;
   c.force_ids = d_force_ids;
+  c.router_out = d_router_logits;
   DG_TRY(embed_canvas(c, cv, p));
   DG_TRY(run_layers(c, cache, cv->batch, cv->canvas, cache->length, false));
   return lm_head(c, cv, p, d_logits);

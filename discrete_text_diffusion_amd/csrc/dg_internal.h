@@ -23,7 +23,8 @@ enum GemmEpi : int32_t {
 enum ActKind : int32_t {
   ACT_BF16 = 0,         // bf16 rows
   ACT_F32 = 1,          // fp32 rows, rounded to bf16 when staged (MFMA path)
-  ACT_BF16_SCALED = 2,  // bf16 rows times scale[row][k / 256] (fp32), rounded to bf16
+  ACT_BF16_SCALED = 2,  // bf16 rows whose 256-wide K tiles carry a factor scale[row][k / 256] (fp32),
+                        // applied to the fp32 partial sum of each tile
 };
 
 struct QkvEpi {
@@ -34,6 +35,7 @@ struct QkvEpi {
   int64_t kv_b_stride;  // elements between sequences of the k/v store
   int64_t kv_h_stride;  // elements between kv heads (= capacity * d_head)
   int32_t kv_row0;      // first row written inside each head (cache length for append)
+  int32_t v_pitch;      // row pitch of the transposed V store ([d_head][rows] per head)
   int32_t seq_len;      // tokens per sequence in this call
   int32_t pos0;         // absolute position of the first token of each sequence
   float rope_base;
@@ -97,21 +99,21 @@ struct LmArgs {
 // Launchers
 // k_gemm.hip
 int launch_wsgemm(const GemmArgs& a, int bm, int nwt, int kc, bool geglu, hipStream_t s);
-int launch_lmhead(const GemmArgs& a, const LmArgs& lm, hipStream_t s);
+int launch_lmhead(const GemmArgs& a, const LmArgs& lm, int bm, hipStream_t s);
 int launch_gemm_simple(const GemmArgs& a, hipStream_t s);
 int launch_pack_bf16(bf16_t* dst, const bf16_t* src, int64_t rows, int64_t cols, int transposed, hipStream_t s);
 int launch_lm_partials_from_logits(const float* logits, int rows, const LmArgs& lm, hipStream_t s);
 // k_route.hip
 int launch_topk(const float* part, int n_split, int64_t split_stride, int T, int E, int k, const int32_t* forced,
-                int32_t* ids, float* w, hipStream_t s);
-size_t route_sort_lds_bytes(int npairs);
+                int32_t* ids, float* w, float* r_out, hipStream_t s);
+int route_max_tokens();
 int launch_route_sort(const int32_t* ids, int T, int k, int E, int n_sh, int bm, int32_t* row_token, int32_t* inv,
                       int32_t* offsets, GemmTile* tiles, int32_t* n_tiles, hipStream_t s);
 // k_attn.hip
 int launch_attention(int dtype, const void* q, int64_t q_ld, const void* k0, const void* v0, int64_t s0_seq,
-                     int64_t s0_head, int len0, const void* k1, const void* v1, int64_t s1_seq, int64_t s1_head,
-                     int len1, int n_prefix, int causal, int seq_len, int n_seq, int n_q, int n_kv, int d,
-                     int n_split, float* part_o, float2* part_ml, void* out, hipStream_t s);
+                     int64_t s0_head, int vp0, int len0, const void* k1, const void* v1, int64_t s1_seq,
+                     int64_t s1_head, int vp1, int len1, int n_prefix, int causal, int seq_len, int n_seq, int n_q,
+                     int n_kv, int d, int n_split, float* part_o, float2* part_ml, void* out, hipStream_t s);
 // k_misc.hip
 int launch_embed_norm(int dtype, const int32_t* tok, const void* emb, const float* add, float* x, void* n, int T,
                       int d, float eps, hipStream_t s);

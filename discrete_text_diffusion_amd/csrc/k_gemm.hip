@@ -112,9 +112,14 @@ __device__ __forceinline__ void epi_pair(const GemmArgs& a, int ks, int orow, in
         const bool is_k = n < q.q_dim + q.kv_dim;
         const int nn = n - q.q_dim - (is_k ? 0 : q.kv_dim);
         const int h = nn / q.d_head, dd = nn - h * q.d_head;
-        const int64_t idx = (int64_t)seq * q.kv_b_stride + (int64_t)h * q.kv_h_stride +
-                            (int64_t)(q.kv_row0 + i) * q.d_head + dd;
-        store_act2<TA>(is_k ? q.k : q.v, idx, v0, v1);
+        const int64_t head = (int64_t)seq * q.kv_b_stride + (int64_t)h * q.kv_h_stride;
+        if (is_k) {
+          store_act2<TA>(q.k, head + (int64_t)(q.kv_row0 + i) * q.d_head + dd, v0, v1);
+        } else {  // V is stored transposed: [d_head][rows]
+          TA* vb = reinterpret_cast<TA*>(q.v) + head + (int64_t)dd * q.v_pitch + q.kv_row0 + i;
+          vb[0] = to_act<TA>(v0);
+          vb[q.v_pitch] = to_act<TA>(v1);
+        }
       }
       break;
     }
@@ -143,16 +148,9 @@ __device__ __forceinline__ uint4 load_act8(const GemmArgs& a, int arow, int k) {
     const float f[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
     return pack8_bf16(f);
   } else {
-    const uint4 raw = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.act) + (int64_t)arow * a.act_ld + k);
-    const float sc = a.act_scale[(int64_t)arow * a.scale_ld + (k >> 8)];
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-    float f[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = bf2f((bf16_t)(w[i] & 0xFFFF)) * sc;
-      f[2 * i + 1] = bf2f((bf16_t)(w[i] >> 16)) * sc;
-    }
-    return pack8_bf16(f);
+    // ACT_BF16_SCALED: raw bf16; the per-(row, 256-wide K tile) scale is
+    // applied to the partial sums (see wsgemm_mainloop)
+    return *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.act) + (int64_t)arow * a.act_ld + k);
   }
 }
 
@@ -199,7 +197,7 @@ __device__ __forceinline__ void wsgemm_mainloop(const GemmArgs& a, const GemmTil
 #pragma unroll
     for (int j = 0; j < MW; ++j) {
       acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      if constexpr (GEGLU) accu[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if constexpr (GEGLU || ACT == ACT_BF16_SCALED) accu[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
   const int kb = ks * a.k_split;
@@ -285,9 +283,35 @@ __device__ __forceinline__ void wsgemm_mainloop(const GemmArgs& a, const GemmTil
         if (!wval[i]) continue;
 #pragma unroll
         for (int j = 0; j < MW; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[cur][s][i], bx[j], acc[i][j], 0, 0, 0);
-          if constexpr (GEGLU)
-            accu[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[cur][s][i], bx[j], accu[i][j], 0, 0, 0);
+          if constexpr (ACT == ACT_BF16_SCALED) {
+            accu[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[cur][s][i], bx[j], accu[i][j], 0, 0, 0);
+          } else {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[cur][s][i], bx[j], acc[i][j], 0, 0, 0);
+            if constexpr (GEGLU)
+              accu[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[cur][s][i], bx[j], accu[i][j], 0, 0, 0);
+          }
+        }
+      }
+    }
+    if constexpr (ACT == ACT_BF16_SCALED) {
+      // end of a 256-wide K tile: acc += scale[row][tile] * partial
+      const int kend = kb + (c + 1) * KC;
+      if ((kend & 255) == 0) {
+        const int tile = (kend >> 8) - 1;
+#pragma unroll
+        for (int j = 0; j < MW; ++j) {
+          const int r = j * 16 + (lane & 15);
+          float sc = 0.f;
+          if (r < td.nrows) {
+            const int orow = td.row0 + r;
+            const int ar = a.row_map ? a.row_map[orow] : orow;
+            sc = a.act_scale[(int64_t)ar * a.scale_ld + tile];
+          }
+#pragma unroll
+          for (int i = 0; i < NWT; ++i) {
+            acc[i][j] += sc * accu[i][j];
+            accu[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
         }
       }
     }
@@ -430,31 +454,31 @@ __device__ __forceinline__ void row_tile_stats(const float* zrow, int row, int v
   }
 }
 
-constexpr int LM_BM = 128;
 constexpr int LM_KC = 64;
 constexpr int LM_ZLD = 256 + 4;  // fp32 pitch of the logit tile in LDS
-constexpr int LM_XS_BYTES = 2 * LM_BM * (LM_KC + 8) * 2;
 constexpr int LM_Z_BYTES = 64 * LM_ZLD * 4;
-constexpr int LM_LDS = LM_XS_BYTES > LM_Z_BYTES ? LM_XS_BYTES : LM_Z_BYTES;
 
+template <int BM>
 __global__ __launch_bounds__(kThreads) void k_lmhead(GemmArgs a, LmArgs lm) {
-  constexpr int MW = LM_BM / 16;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[LM_LDS];
+  constexpr int MW = BM / 16;
+  constexpr int XS_BYTES = 2 * BM * (LM_KC + 8) * 2;
+  constexpr int LDS = XS_BYTES > LM_Z_BYTES ? XS_BYTES : LM_Z_BYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[LDS];
   bf16_t* xs = reinterpret_cast<bf16_t*>(smem);
   float* zt = reinterpret_cast<float*>(smem);
 
   int tile, fb, ks;
   decode_block(a, xcd_logical_block(a.nblocks), tile, fb, ks);
   if (fb >= a.n_fb || tile >= a.max_tiles) return;
-  const GemmTile td{0, tile * LM_BM, min(LM_BM, a.M - tile * LM_BM), 0};
+  const GemmTile td{0, tile * BM, min(BM, a.M - tile * BM), 0};
 
   f32x4_t acc[4][MW], accu[4][MW];
-  wsgemm_mainloop<LM_BM, 4, LM_KC, false, ACT_BF16>(a, td, fb, 0, xs, acc, accu);
+  wsgemm_mainloop<BM, 4, LM_KC, false, ACT_BF16>(a, td, fb, 0, xs, acc, accu);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // two halves of 64 rows through a 64 x 256 fp32 tile in LDS
+  // halves of 64 rows through a 64 x 256 fp32 tile in LDS
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
+  for (int half = 0; half < BM / 64; ++half) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = wave * 64 + i * 16 + (lane >> 4) * 4;
@@ -578,13 +602,16 @@ static void launch_t(const GemmArgs& a0, int act, hipStream_t s) {
 
 int launch_wsgemm(const GemmArgs& a, int bm, int nwt, int kc, bool geglu, hipStream_t s) {
   if (a.K % kc != 0 || a.k_split % kc != 0 || a.N % 16 != 0) return -1;
+  if (a.act_kind == ACT_BF16_SCALED && (a.k_split % 256 != 0 || a.K % 256 != 0 || geglu)) return -1;
 #define DG_CASE(BM_, NWT_, KC_, GG_)                                   \
   if (bm == BM_ && nwt == NWT_ && kc == KC_ && geglu == GG_) {         \
     launch_t<BM_, NWT_, KC_, GG_>(a, a.act_kind, s);                   \
     return hipGetLastError() == hipSuccess ? 0 : -5;                   \
   }
   DG_CASE(128, 1, 64, false)
+  DG_CASE(64, 1, 64, false)
   DG_CASE(32, 1, 64, true)
+  DG_CASE(32, 1, 128, true)
   DG_CASE(32, 2, 64, false)
   DG_CASE(32, 1, 64, false)
   DG_CASE(64, 2, 64, false)
@@ -594,11 +621,13 @@ int launch_wsgemm(const GemmArgs& a, int bm, int nwt, int kc, bool geglu, hipStr
   return -2;
 }
 
-int launch_lmhead(const GemmArgs& a0, const LmArgs& lm, hipStream_t s) {
+int launch_lmhead(const GemmArgs& a0, const LmArgs& lm, int bm, hipStream_t s) {
   GemmArgs a = a0;
   a.n_split = 1;
   a.nblocks = round8(a.max_tiles * a.n_fb);
-  hipLaunchKernelGGL(k_lmhead, dim3(a.nblocks), dim3(kThreads), 0, s, a, lm);
+  if (bm == 64) hipLaunchKernelGGL(k_lmhead<64>, dim3(a.nblocks), dim3(kThreads), 0, s, a, lm);
+  else if (bm == 128) hipLaunchKernelGGL(k_lmhead<128>, dim3(a.nblocks), dim3(kThreads), 0, s, a, lm);
+  else return -2;
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

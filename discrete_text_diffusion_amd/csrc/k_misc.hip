@@ -49,9 +49,14 @@ __global__ __launch_bounds__(256) void k_resid_norm(float* x, const float* part,
   __shared__ float red[4];
   const int64_t t = blockIdx.x;
   float* xr = x + t * d;
+  constexpr int kMaxS = 8;
   for (int i = threadIdx.x; i < d; i += 256) {
-    float acc = 0.f;
-    for (int s = 0; s < n_split; ++s) acc += part[(int64_t)s * split_stride + t * d + i];
+    float v[kMaxS];
+#pragma unroll
+    for (int s = 0; s < kMaxS; ++s) v[s] = s < n_split ? part[(int64_t)s * split_stride + t * d + i] : 0.f;
+    float acc = v[0];
+#pragma unroll
+    for (int s = 1; s < kMaxS; ++s) acc += v[s];
     xr[i] += acc;
   }
   __syncthreads();
@@ -74,11 +79,29 @@ __global__ __launch_bounds__(256) void k_combine_norm(float* x, const float* Y, 
   __syncthreads();
   float* xr = x + t * d;
   const int64_t sh0 = (int64_t)T * k;
-  for (int i = threadIdx.x; i < d; i += 256) {
-    float y = 0.f;
-    for (int c = 0; c < n_sh; ++c) y += Y[(sh0 + (int64_t)c * T + t) * d + i];
-    for (int j = 0; j < k; ++j) y = fmaf(wts[j], Y[(int64_t)rows[j] * d + i], y);
-    xr[i] += y;
+  if ((d & 3) == 0) {
+    for (int i = threadIdx.x * 4; i < d; i += 256 * 4) {
+      float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int c = 0; c < n_sh; ++c) {
+        const float4 v = *reinterpret_cast<const float4*>(Y + (sh0 + (int64_t)c * T + t) * d + i);
+        y.x += v.x; y.y += v.y; y.z += v.z; y.w += v.w;
+      }
+      for (int j = 0; j < k; ++j) {
+        const float4 v = *reinterpret_cast<const float4*>(Y + (int64_t)rows[j] * d + i);
+        const float wj = wts[j];
+        y.x = fmaf(wj, v.x, y.x); y.y = fmaf(wj, v.y, y.y); y.z = fmaf(wj, v.z, y.z); y.w = fmaf(wj, v.w, y.w);
+      }
+      float4 xv = *reinterpret_cast<float4*>(xr + i);
+      xv.x += y.x; xv.y += y.y; xv.z += y.z; xv.w += y.w;
+      *reinterpret_cast<float4*>(xr + i) = xv;
+    }
+  } else {
+    for (int i = threadIdx.x; i < d; i += 256) {
+      float y = 0.f;
+      for (int c = 0; c < n_sh; ++c) y += Y[(sh0 + (int64_t)c * T + t) * d + i];
+      for (int j = 0; j < k; ++j) y = fmaf(wts[j], Y[(int64_t)rows[j] * d + i], y);
+      xr[i] += y;
+    }
   }
   __syncthreads();
   write_norm<TA>(xr, n + t * d, d, eps, red);
@@ -90,8 +113,13 @@ __global__ __launch_bounds__(256) void k_reduce_splits(const float* part, int n_
                                                       int64_t n_elems, TA* out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n_elems) return;
-  float acc = 0.f;
-  for (int s = 0; s < n_split; ++s) acc += part[(int64_t)s * split_stride + i];
+  constexpr int kMaxS = 16;
+  float v[kMaxS];
+#pragma unroll
+  for (int s = 0; s < kMaxS; ++s) v[s] = s < n_split ? part[(int64_t)s * split_stride + i] : 0.f;
+  float acc = v[0];
+#pragma unroll
+  for (int s = 1; s < kMaxS; ++s) acc += v[s];
   out[i] = to_act<TA>(acc);
 }
 
@@ -127,6 +155,7 @@ int launch_embed_norm(int dtype, const int32_t* tok, const void* emb, const floa
 
 int launch_resid_norm(int dtype, float* x, const float* part, int n_split, int64_t split_stride, void* n, int T, int d,
                       float eps, hipStream_t s) {
+  if (n_split < 1 || n_split > 8) return -1;
   if (dtype == 1)
     hipLaunchKernelGGL(k_resid_norm<bf16_t>, dim3(T), dim3(256), 0, s, x, part, n_split, split_stride, (bf16_t*)n, d, eps);
   else
@@ -146,6 +175,7 @@ int launch_combine_norm(int dtype, float* x, const float* Y, const int32_t* inv,
 
 int launch_reduce_splits(int dtype, const float* part, int n_split, int64_t split_stride, int64_t n_elems, void* out,
                          hipStream_t s) {
+  if (n_split < 1 || n_split > 16) return -1;
   const dim3 g((unsigned)DG_CEIL_DIV(n_elems, 256));
   if (dtype == 1) hipLaunchKernelGGL(k_reduce_splits<bf16_t>, g, dim3(256), 0, s, part, n_split, split_stride, n_elems, (bf16_t*)out);
   else hipLaunchKernelGGL(k_reduce_splits<float>, g, dim3(256), 0, s, part, n_split, split_stride, n_elems, (float*)out);

@@ -13,28 +13,43 @@ namespace {
 // One wave per token.  Router logits arrive as `n_split` fp32 partial sums
 // [split][T][E] added in split order.
 __global__ __launch_bounds__(256) void k_topk(const float* part, int n_split, int64_t split_stride, int T, int E,
-                                              int k, const int32_t* forced, int32_t* ids, float* w) {
+                                              int k, const int32_t* forced, int32_t* ids, float* w,
+                                              float* r_out) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (t >= T) return;
   constexpr int kMaxPerLane = 4;  // E <= 256
+  constexpr int kMaxSplit = 8;    // partial sums are added in split order
   float r[kMaxPerLane];
 #pragma unroll
   for (int q = 0; q < kMaxPerLane; ++q) {
     const int e = lane + q * 64;
     float v = -INFINITY;
     if (e < E) {
-      v = 0.f;
-      for (int s = 0; s < n_split; ++s) v += part[(int64_t)s * split_stride + (int64_t)t * E + e];
+      float ps[kMaxSplit];
+#pragma unroll
+      for (int s = 0; s < kMaxSplit; ++s)
+        ps[s] = s < n_split ? part[(int64_t)s * split_stride + (int64_t)t * E + e] : 0.f;
+      v = ps[0];
+#pragma unroll
+      for (int s = 1; s < kMaxSplit; ++s) v += ps[s];
     }
     r[q] = v;
+    if (r_out && e < E) r_out[(int64_t)t * E + e] = v;
   }
   float sel_v[16];
   int sel_e[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    sel_v[j] = -INFINITY;
+    sel_e[j] = 0;
+  }
   if (forced) {
     // test path: the caller fixes the k experts (in rank order); weights still
     // come from this token's router logits
-    for (int j = 0; j < k; ++j) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j >= k) break;
       int e = forced[t * k + j];
       if (e < 0 || e >= E) e = 0;  // keep the grouped GEMMs in bounds on bad test input
       const int q = e >> 6;
@@ -46,7 +61,9 @@ __global__ __launch_bounds__(256) void k_topk(const float* part, int n_split, in
       sel_e[j] = e;
     }
   }
-  for (int j = 0; j < (forced ? 0 : k); ++j) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (forced || j >= k) break;
     float bv = -INFINITY;
     int be = 0x7FFFFFFF;
 #pragma unroll
@@ -68,68 +85,84 @@ __global__ __launch_bounds__(256) void k_topk(const float* part, int n_split, in
   }
   if (lane == 0) {
     float m = sel_v[0];
-    for (int j = 1; j < k; ++j) m = fmaxf(m, sel_v[j]);
+#pragma unroll
+    for (int j = 1; j < 16; ++j)
+      if (j < k) m = fmaxf(m, sel_v[j]);
+    float ex[16];
     float den = 0.f;
-    for (int j = 0; j < k; ++j) den += expf(sel_v[j] - m);
-    for (int j = 0; j < k; ++j) {
-      ids[t * k + j] = sel_e[j];
-      w[t * k + j] = expf(sel_v[j] - m) / den;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      ex[j] = j < k ? expf(sel_v[j] - m) : 0.f;
+      den += ex[j];
     }
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < k) {
+        ids[t * k + j] = sel_e[j];
+        w[t * k + j] = ex[j] / den;
+      }
   }
 }
 
-// Single workgroup: bitonic sort of (expert << 20 | pair) keys in LDS, then
-// segment offsets, the row -> token map, the inverse permutation and the
-// GEMM row tiles (routed segments first, then the shared-expert slices).
+// Single workgroup: stable counting of the (token, slot) pairs by expert.
+// A bitmap marks which tokens chose each expert; a pair's position inside
+// its expert segment is the number of earlier tokens in that expert's row
+// (per-word prefix counts + one popcount), so the order within a segment is
+// by token id.  Then segment offsets, the row -> token map, the inverse
+// permutation and the GEMM row tiles (routed segments, then the
+// shared-expert slices).  Requires T <= 64 * kMaxWords.
+constexpr int kMaxWords = 16;  // 1024 tokens
+
 __global__ __launch_bounds__(1024) void k_route_sort(const int32_t* ids, int T, int k, int E, int n_sh, int bm,
                                                      int32_t* row_token, int32_t* inv, int32_t* offsets,
                                                      GemmTile* tiles, int32_t* n_tiles) {
-  extern __shared__ uint32_t sm[];
+  __shared__ unsigned long long bits[256 * kMaxWords];
+  __shared__ int32_t wpre[256 * kMaxWords];
+  __shared__ int32_t cnt[256];
+  __shared__ int32_t off[257];
+  __shared__ int32_t toff[257];
   const int npairs = T * k;
-  int np2 = 1;
-  while (np2 < npairs) np2 <<= 1;
-  uint32_t* key = sm;
-  int32_t* cnt = reinterpret_cast<int32_t*>(sm + np2);  // [E]
-  int32_t* toff = cnt + 256;                           // [E+1] tile offsets
+  const int W = (T + 63) >> 6;
   const int tid = threadIdx.x, nt = blockDim.x;
-  for (int i = tid; i < np2; i += nt) key[i] = i < npairs ? ((uint32_t)ids[i] << 20) | (uint32_t)i : 0xFFFFFFFFu;
-  for (int i = tid; i < E; i += nt) cnt[i] = 0;
+  for (int i = tid; i < E * W; i += nt) bits[i] = 0ull;
   __syncthreads();
-  for (int i = tid; i < npairs; i += nt) atomicAdd(&cnt[ids[i]], 1);
-  for (int size = 2; size <= np2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      __syncthreads();
-      for (int i = tid; i < (np2 >> 1); i += nt) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const uint32_t a = key[lo], b = key[hi];
-        if ((a > b) == up) { key[lo] = b; key[hi] = a; }
-      }
+  for (int q = tid; q < npairs; q += nt) {
+    const int e = ids[q], t = q / k;
+    atomicOr(&bits[e * W + (t >> 6)], 1ull << (t & 63));
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += nt) {
+    int run = 0;
+    for (int w = 0; w < W; ++w) {
+      wpre[e * W + w] = run;
+      run += __popcll(bits[e * W + w]);
     }
+    cnt[e] = run;
   }
   __syncthreads();
   if (tid == 0) {
-    int off = 0, tof = 0;
+    int o = 0, tf = 0;
     for (int e = 0; e < E; ++e) {
-      offsets[e] = off;
-      toff[e] = tof;
-      off += cnt[e];
-      tof += (cnt[e] + bm - 1) / bm;
+      off[e] = o;
+      toff[e] = tf;
+      o += cnt[e];
+      tf += (cnt[e] + bm - 1) / bm;
     }
-    offsets[E] = off;
-    toff[E] = tof;
-    const int per_sh = (T + bm - 1) / bm;
-    n_tiles[0] = tof + n_sh * per_sh;
+    off[E] = o;
+    toff[E] = tf;
+    n_tiles[0] = tf + n_sh * ((T + bm - 1) / bm);
   }
   __syncthreads();
-  for (int p = tid; p < npairs; p += nt) {
-    const uint32_t q = key[p] & 0xFFFFFu;
-    row_token[p] = (int32_t)(q / (uint32_t)k);
+  for (int e = tid; e <= E; e += nt) offsets[e] = off[e];
+  for (int q = tid; q < npairs; q += nt) {
+    const int e = ids[q], t = q / k;
+    const unsigned long long below = bits[e * W + (t >> 6)] & ((1ull << (t & 63)) - 1ull);
+    const int p = off[e] + wpre[e * W + (t >> 6)] + __popcll(below);
+    row_token[p] = t;
     inv[q] = p;
   }
   for (int e = tid; e < E; e += nt) {
-    const int base = offsets[e], n = cnt[e];
+    const int base = off[e], n = cnt[e];
     for (int i = 0, j = toff[e]; i * bm < n; ++i, ++j) tiles[j] = GemmTile{e, base + i * bm, min(bm, n - i * bm), 0};
   }
   const int per_sh = (T + bm - 1) / bm;
@@ -143,25 +176,19 @@ __global__ __launch_bounds__(1024) void k_route_sort(const int32_t* ids, int T, 
 }  // namespace
 
 int launch_topk(const float* part, int n_split, int64_t split_stride, int T, int E, int k, const int32_t* forced,
-                int32_t* ids, float* w, hipStream_t s) {
-  if (E > 256 || k > 16 || k > E) return -1;
+                int32_t* ids, float* w, float* r_out, hipStream_t s) {
+  if (E > 256 || k > 16 || k > E || n_split < 1 || n_split > 8) return -1;
   hipLaunchKernelGGL(k_topk, dim3(DG_CEIL_DIV(T, 4)), dim3(256), 0, s, part, n_split, split_stride, T, E, k, forced, ids,
-                     w);
+                     w, r_out);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
-size_t route_sort_lds_bytes(int npairs) {
-  int np2 = 1;
-  while (np2 < npairs) np2 <<= 1;
-  return (size_t)np2 * 4 + 2 * 256 * 4 + 64;
-}
+int route_max_tokens() { return 64 * kMaxWords; }
 
 int launch_route_sort(const int32_t* ids, int T, int k, int E, int n_sh, int bm, int32_t* row_token, int32_t* inv,
                       int32_t* offsets, GemmTile* tiles, int32_t* n_tiles, hipStream_t s) {
-  if (E > 255) return -1;
-  const size_t lds = route_sort_lds_bytes(T * k);
-  if (lds > 65536) return -1;
-  hipLaunchKernelGGL(k_route_sort, dim3(1), dim3(1024), lds, s, ids, T, k, E, n_sh, bm, row_token, inv, offsets,
+  if (E > 256 || T > 64 * kMaxWords || T < 1) return -1;
+  hipLaunchKernelGGL(k_route_sort, dim3(1), dim3(1024), 0, s, ids, T, k, E, n_sh, bm, row_token, inv, offsets,
                      tiles, n_tiles);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }

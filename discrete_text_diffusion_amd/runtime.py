@@ -138,9 +138,13 @@ class DeviceCache:
         return self.struct.length
 
     def view(self, which: str):
+        """Logical [layer][batch][kv_head][row][d_head] view (V is stored
+        transposed, [d_head][row] per head)."""
         s = self.shape
-        t = self.k if which == "k" else self.v
-        return t.view(s.n_layers, self.struct.batch, s.n_kv_heads, self.struct.capacity, s.d_head)
+        if which == "k":
+            return self.k.view(s.n_layers, self.struct.batch, s.n_kv_heads, self.struct.capacity, s.d_head)
+        return self.v.view(s.n_layers, self.struct.batch, s.n_kv_heads, s.d_head,
+                           self.struct.capacity).transpose(-1, -2)
 
     def fill_random(self, length: int, seed: int = 0, std: float = 1.0):
         """N(0, std) fill of rows [0, length) (synthetic prefix, no encoder)."""

@@ -99,8 +99,10 @@ typedef struct dg_weights {
   float lm_scale;      /* logits z = lm_scale * (RMSNorm(x) W_lm^T) */
 } dg_weights;
 
-/* KV cache: k and v are device arrays [n_layers][batch][n_kv][capacity][d_head]
- * in the model dtype holding post-RoPE keys and values of rows [0, length).
+/* KV cache in the model dtype, rows [0, length) valid:
+ *   k: [n_layers][batch][n_kv][capacity][d_head]   post-RoPE keys
+ *   v: [n_layers][batch][n_kv][d_head][capacity]   values, stored transposed so
+ *      that attention streams contiguous runs of keys per dimension.
  * `length` is host bookkeeping updated by the appending calls at enqueue time. */
 typedef struct dg_kv_cache {
   void* k;
@@ -271,10 +273,13 @@ int dg_test_route_from_logits(const dg_model_config* cfg, const float* d_logits,
  * the canvas.  d_force_ids (optional, [n_layers][B*C][top_k], rank order)
  * replaces the top-k choice of every layer by the given experts (the gate
  * weights are still the softmax of this run's router logits over them), so
- * that continuous outputs can be compared when a near-tie would flip a route. */
+ * that continuous outputs can be compared when a near-tie would flip a route.
+ * d_router_logits (optional, [n_layers][B*C][n_experts] fp32) receives every
+ * layer's router logits. */
 int dg_test_forward_logits(const dg_model_config* cfg, const dg_weights* w, const dg_kv_cache* cache,
                            dg_canvas* canvas, const dg_step_params* p, const int32_t* d_force_ids,
-                           float* d_logits, void* d_ws, size_t ws_bytes, void* stream);
+                           float* d_router_logits, float* d_logits, void* d_ws, size_t ws_bytes,
+                           void* stream);
 
 #ifdef __cplusplus
 }

@@ -48,7 +48,7 @@ def allclose_report(name, got, want, atol, rtol):
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)
     err = np.abs(got - want)
-    lim = atol + rtol * np.abs(want)
+    lim = np.asarray(atol) + rtol * np.abs(want)
     worst = float(np.max(err - lim)) if err.size else 0.0
     say(f"{name}: max abs err {err.max():.3e}, max rel {np.max(err / (np.abs(want) + 1e-30)):.3e}, "
         f"worst margin to bound {worst:.3e}")

@@ -77,10 +77,11 @@ def mini(env):
     return pb
 
 
-def _forward_logits(pb, t, n_steps, sc_probs=None, force_ids=None):
+def _forward_logits(pb, t, n_steps, sc_probs=None, force_ids=None, want_router=False):
     torch, dg, rt = pb.env
     T = pb.B * pb.C
     out = torch.empty(T * pb.shape.vocab, dtype=torch.float32, device="cuda")
+    rout = torch.empty(pb.shape.n_layers * T * pb.shape.n_experts, dtype=torch.float32, device="cuda")
     if sc_probs is not None:
         pb.canvas.set_sc_probs(torch.from_numpy(sc_probs.astype(np.float32).reshape(-1)).cuda())
     d_force = None
@@ -88,10 +89,61 @@ def _forward_logits(pb, t, n_steps, sc_probs=None, force_ids=None):
         d_force = torch.from_numpy(np.ascontiguousarray(force_ids, dtype=np.int32).reshape(-1)).cuda()
     dg.dg_test_forward_logits(pb.cfg, pb.model.weights, pb.cache.struct, pb.canvas.struct,
                               rt.step_params(t, n_steps), d_force.data_ptr() if d_force is not None else None,
-                              out.data_ptr(), pb.ws.ptr, pb.ws.size, pb.st)
+                              rout.data_ptr(), out.data_ptr(), pb.ws.ptr, pb.ws.size, pb.st)
     torch.cuda.synchronize()
     pb.canvas.set_sc_probs(None)
-    return out.cpu().numpy().reshape(pb.B, pb.C, pb.shape.vocab)
+    z = out.cpu().numpy().reshape(pb.B, pb.C, pb.shape.vocab)
+    if want_router:
+        return z, rout.cpu().numpy().reshape(pb.shape.n_layers, T, pb.shape.n_experts)
+    return z
+
+
+def _err_summary(name, got, want):
+    e = np.abs(np.asarray(got, dtype=np.float64) - np.asarray(want, dtype=np.float64)).reshape(-1)
+    q = np.quantile(e, [0.5, 0.99, 0.9999]) if e.size else [0, 0, 0]
+    say(f"{name}: |err| median {q[0]:.2e}  p99 {q[1]:.2e}  p99.99 {q[2]:.2e}  max {e.max():.2e}")
+    return float(e.max())
+
+
+# Router-logit margin below which a route decision counts as a near-tie: a few
+# times the largest GPU-vs-oracle router-logit error measured with the
+# oracle's routes forced (fp32: ~5e-7; bf16: ~2e-3, the tail where a bf16
+# rounding of an activation fell on the other side of a boundary and
+# propagated).
+ROUTE_EPS = {"f32": 1e-5, "bf16": 5e-3}
+# Typical (median) router-logit error bound with forced routes.
+ROUTE_MEDIAN = {"f32": 1e-6, "bf16": 1e-4}
+
+
+def check_sampler_invariants(pb, t, n_steps, prev_before, adaptive=True):
+    """Properties every step must satisfy, checked on the GPU's own outputs
+    against the sampler's definition (entropy-bounded acceptance, Philox
+    re-noise, stop rule)."""
+    B, C, V = pb.B, pb.C, pb.shape.vocab
+    H = pb.canvas.entropy.cpu().numpy().reshape(B, C).astype(np.float64)
+    acc = pb.canvas.accepted.cpu().numpy().reshape(B, C).astype(bool)
+    samp = pb.canvas.sample.cpu().numpy().reshape(B, C)
+    am = pb.canvas.argmax.cpu().numpy().reshape(B, C)
+    nxt = pb.canvas.tokens.cpu().numpy().reshape(B, C)
+    nacc = pb.canvas.n_accepted.cpu().numpy()
+    stop = pb.canvas.stop.cpu().numpy()
+    mean = pb.canvas.mean_entropy.cpu().numpy()
+    for b in range(B):
+        K = int(acc[b].sum())
+        assert K == nacc[b] >= 1
+        order = np.lexsort((np.arange(C), H[b]))
+        assert set(np.nonzero(acc[b])[0]) == set(order[:K])      # the K lowest entropies
+        if K > 1:
+            assert H[b][acc[b]].sum() <= 0.1 + 1e-5
+        if K < C:
+            assert np.sort(H[b])[:K + 1].sum() > 0.1 - 1e-5      # one more would break the bound
+        fresh = smp.renoise_tokens(pb.seeds[b], t, 0, C, V)
+        assert np.array_equal(nxt[b], np.where(acc[b], samp[b], fresh))
+        assert abs(mean[b] - H[b].mean()) < 1e-5
+        want_stop = adaptive and t >= 1 and mean[b] < 0.005 and prev_before is not None and \
+            np.array_equal(am[b], prev_before[b])
+        assert int(stop[b]) == int(want_stop)
+    return am.copy()
 
 
 def _route_margins(shape, trace):
@@ -102,6 +154,19 @@ def _route_margins(shape, trace):
         out.append(srt[:, shape.top_k - 1] - srt[:, shape.top_k] if shape.top_k < shape.n_experts
                    else np.full(r.shape[0], np.inf))
     return np.stack(out)
+
+
+def entropy_tolerance(z_oracle, tau):
+    """Per-row entropy bar: the pages' 1e-3 nats, or the first-order entropy
+    change the logit bar allows, whichever is larger.  With a = z/tau,
+    dH = -sum_v p_v (a_v - E_p[a]) da_v, so |dH| <= E_p[|a - E_p a| (2e-2 + 1e-2|z|)] / tau.
+    For the pages' workloads (near-uniform rows) this is below 1e-3; sharp
+    test shapes need the propagated bound."""
+    p, _, _ = smp.row_statistics(z_oracle, tau)
+    a = z_oracle / tau
+    abar = (p * a).sum(-1, keepdims=True)
+    prop = (p * np.abs(a - abar) * (ATOL + RTOL * np.abs(z_oracle))).sum(-1) / tau
+    return np.maximum(1e-3, prop)
 
 
 def _forced_ids(trace):
@@ -130,14 +195,28 @@ def test_forward_logits_match_oracle(which, request):
     margins = _route_margins(pb.shape, tr)
     say(f"oracle routing margins: min {margins.min():.3e}, #<1e-3: {int((margins < 1e-3).sum())}")
     # routes forced to the oracle's choice: continuous outputs must match
-    z = _forward_logits(pb, 0, 48, force_ids=_forced_ids(tr))
+    z, rg = _forward_logits(pb, 0, 48, force_ids=_forced_ids(tr), want_router=True)
     assert torch.equal(k_before, pb.cache.k), "denoiser wrote the cache"
-    allclose_report(f"logits {which} (oracle routes)", z, zo, ATOL, RTOL)
+    ro = np.stack(tr["router_logits"])
+    rerr = _err_summary(f"router logits {which} (oracle routes)", rg, ro)
+    assert float(np.median(np.abs(rg - ro))) < ROUTE_MEDIAN[pb.shape.dtype]
+    assert rerr < ROUTE_EPS[pb.shape.dtype]
+    _err_summary(f"logits {which} (oracle routes)", z, zo)
     _, Hg, _ = smp.row_statistics(z.reshape(-1, pb.shape.vocab), smp.temperature(0, 48))
     _, Ho, _ = smp.row_statistics(zo.reshape(-1, pb.shape.vocab), smp.temperature(0, 48))
-    allclose_report(f"entropy of logits {which} (oracle routes)", Hg, Ho, 1e-3, 0.0)
-    # unforced: report how far routing near-ties move the result
-    zu = _forward_logits(pb, 0, 48)
+    _err_summary(f"entropy {which} (oracle routes)", Hg, Ho)
+    allclose_report(f"logits {which} (oracle routes)", z, zo, ATOL, RTOL)
+    allclose_report(f"entropy of logits {which} (oracle routes)", Hg, Ho,
+                    entropy_tolerance(zo.reshape(-1, pb.shape.vocab), smp.temperature(0, 48)), 0.0)
+    # unforced: the first layer sees the same inputs; any route that differs
+    # there must be an oracle near-tie
+    zu, ru = _forward_logits(pb, 0, 48, want_router=True)
+    k = pb.shape.top_k
+    gtop = np.sort(np.argsort(-ru[0], axis=1, kind="stable")[:, :k], axis=1)
+    otop = np.sort(tr["expert_ids"][0], axis=1)
+    flips = np.nonzero(np.any(gtop != otop, axis=1))[0]
+    say(f"unforced: layer-0 route flips {flips.size} (oracle margins {margins[0][flips]})")
+    assert np.all(margins[0][flips] < ROUTE_EPS[pb.shape.dtype])
     du = np.abs(zu - zo).max(axis=-1).reshape(-1)
     say(f"unforced: rows with max|dz| > {ATOL}: {int((du > ATOL).sum())} of {du.size}; max {du.max():.3e}")
     # self-conditioning from an external distribution
@@ -153,10 +232,13 @@ def test_forward_logits_match_oracle(which, request):
 
 @pytest.mark.parametrize("which", ["tiny", "mini"])
 def test_denoise_loop_and_commit_match_oracle(which, request):
-    """Up to 48 adaptive steps compared step by step (canvas, entropies,
-    argmax, accepted set, next tokens, stop), then the commit.  The comparison
-    stops early only at a reported near-tie (a routing margin or a decision
-    margin below the fp32/bf16 error), where both trajectories are valid."""
+    """48 adaptive steps on the GPU.  Every step is checked against the
+    sampler's definition (check_sampler_invariants).  The oracle runs the same
+    trajectory and is compared step by step (canvas, entropies, argmax,
+    accepted set, next tokens, stop) until the first near-tie (a routing or
+    decision margin below the measured GPU-vs-oracle error), after which both
+    trajectories are valid and only the invariants are checked.  Then the
+    commit is compared with the oracle's encode & append of the same tokens."""
     pb = request.getfixturevalue(which)
     torch, dg, rt = pb.env
     say(f"denoise loop {which}")
@@ -166,58 +248,69 @@ def test_denoise_loop_and_commit_match_oracle(which, request):
     pb.canvas.prev_argmax.fill_(-1)
     torch.cuda.synchronize()
     otok = np.stack([smp.initial_canvas(s, 0, pb.C, pb.shape.vocab) for s in pb.seeds])
-    oprev = None
-    osc = None
-    steps = 0
+    oprev, osc = None, None
+    tracking = True
+    compared = 0
+    gprev = None
+    t_last = 0
     for t in range(n_steps):
-        tr = {}
-        z, outs = ost.denoise_step(pb.shape, pb.W, pb.ocache, otok, osc, t, n_steps, pb.seeds, 0, pb.lm_scale,
-                                   oprev, True, trace=tr)
-        rmin = float(_route_margins(pb.shape, tr).min())
-        if rmin < 2e-3:
-            say(f"step {t}: oracle routing margin {rmin:.2e} is a near-tie; stopping the step-by-step comparison")
-            break
+        if tracking:
+            tr = {}
+            z, outs = ost.denoise_step(pb.shape, pb.W, pb.ocache, otok, osc, t, n_steps, pb.seeds, 0, pb.lm_scale,
+                                       oprev, True, trace=tr)
+            rmin = float(_route_margins(pb.shape, tr).min())
+            if rmin < ROUTE_EPS[pb.shape.dtype]:
+                say(f"step {t}: oracle routing margin {rmin:.2e} is a near-tie; oracle comparison ends here")
+                tracking = False
         gtok_in = pb.canvas.tokens.cpu().numpy().reshape(pb.B, pb.C)
-        assert np.array_equal(gtok_in, otok), f"canvas diverged before step {t}"
+        if tracking:
+            assert np.array_equal(gtok_in, otok), f"canvas diverged before step {t}"
         dg.dg_denoise_step(pb.cfg, pb.model.weights, pb.cache.struct, pb.canvas.struct,
                            rt.step_params(t, n_steps, block=0, adaptive=True), pb.ws.ptr, pb.ws.size, pb.st)
         torch.cuda.synchronize()
-        H = pb.canvas.entropy.cpu().numpy().reshape(pb.B, pb.C)
-        am = pb.canvas.argmax.cpu().numpy().reshape(pb.B, pb.C)
-        acc = pb.canvas.accepted.cpu().numpy().reshape(pb.B, pb.C).astype(bool)
-        stop = pb.canvas.stop.cpu().numpy()
-        gnext = pb.canvas.tokens.cpu().numpy().reshape(pb.B, pb.C)
-        ties = 0
-        for b, o in enumerate(outs):
-            herr = np.abs(H[b] - o["H"]).max()
-            assert herr < 1e-3, f"step {t}: entropy error {herr}"
-            ties += compare_decisions(f"t{t} argmax", am[b], o["argmax"], o["margin_argmax"], 2 * ATOL, max_ties=2)
-            ties += compare_decisions(f"t{t} accepted", acc[b], o["accepted"], o["margin_accept"], 2e-3, max_ties=2)
-            ties += compare_decisions(f"t{t} next tokens", gnext[b], o["next_tokens"],
-                                      np.where(o["accepted"], o["margin_sample"], 1.0), 1e-5, max_ties=1)
-            assert int(stop[b]) == int(o["stop"]) or o["margin_stop"] < 1e-3
-        steps = t + 1
-        oprev = np.stack([o["argmax"] for o in outs])
-        otok = np.stack([o["next_tokens"] for o in outs])
-        osc = np.stack([o["p"] for o in outs])
-        if ties:
-            say(f"near-tie decision at step {t}; stopping the step-by-step comparison")
-            if not np.array_equal(am, oprev):
-                return
-            break
-        if all(o["stop"] for o in outs):
+        am = check_sampler_invariants(pb, t, n_steps, gprev)
+        gprev = am
+        t_last = t
+        if tracking:
+            H = pb.canvas.entropy.cpu().numpy().reshape(pb.B, pb.C)
+            acc = pb.canvas.accepted.cpu().numpy().reshape(pb.B, pb.C).astype(bool)
+            gnext = pb.canvas.tokens.cpu().numpy().reshape(pb.B, pb.C)
+            stop = pb.canvas.stop.cpu().numpy()
+            ties = 0
+            for b, o in enumerate(outs):
+                herr = np.abs(H[b] - o["H"])
+                tol = entropy_tolerance(z[b], o["tau"])
+                assert np.all(herr <= tol), f"step {t}: entropy error {herr.max()} (bar {tol.min()})"
+                ties += compare_decisions(f"t{t} argmax", am[b], o["argmax"], o["margin_argmax"], 2 * ATOL, max_ties=2)
+                ties += compare_decisions(f"t{t} accepted", acc[b], o["accepted"], o["margin_accept"], 2e-3,
+                                          max_ties=2)
+                ties += compare_decisions(f"t{t} next tokens", gnext[b], o["next_tokens"],
+                                          np.where(o["accepted"], o["margin_sample"], 1.0), 1e-5, max_ties=1)
+                assert int(stop[b]) == int(o["stop"]) or o["margin_stop"] < 1e-3
+            compared = t + 1
+            oprev = np.stack([o["argmax"] for o in outs])
+            otok = np.stack([o["next_tokens"] for o in outs])
+            osc = np.stack([o["p"] for o in outs])
+            if ties:
+                say(f"near-tie decision at step {t}; oracle comparison ends here")
+                tracking = False
+        if int(pb.canvas.stop.cpu().numpy().min()) == 1:
             say(f"{which}: adaptive stop at step {t}")
             break
-    say(f"{which}: {steps} steps compared")
-    assert steps >= 1
-    # commit: argmax of the last step appended by the causal encoder
+    say(f"{which}: {t_last + 1} GPU steps checked against the definition, {compared} compared with the oracle")
+    # commit: the last step's argmax is appended by the causal encoder.  The
+    # tokens come from the oracle's trajectory (its last compared argmax, or
+    # its initial canvas), written into the GPU's argmax slot, so the cache
+    # comparison uses no GPU-derived input on the oracle side.
+    ocom = oprev if oprev is not None else otok
+    pb.canvas.argmax.copy_(torch.from_numpy(np.ascontiguousarray(ocom, dtype=np.int32).reshape(-1)))
     dg.dg_commit_block(pb.cfg, pb.model.weights, pb.cache.struct, pb.canvas.struct,
-                       rt.step_params(steps - 1, n_steps, block=0), pb.ws.ptr, pb.ws.size, pb.st)
+                       rt.step_params(t_last, n_steps, block=0), pb.ws.ptr, pb.ws.size, pb.st)
     torch.cuda.synchronize()
     com = pb.canvas.committed.cpu().numpy().reshape(pb.B, pb.C)
-    assert np.array_equal(com, oprev)
+    assert np.array_equal(com, ocom)
     assert pb.cache.length == L0 + pb.C
-    ost.encode_append(pb.shape, pb.W, pb.ocache, com)
+    ost.encode_append(pb.shape, pb.W, pb.ocache, ocom)
     pb.compare_cache(pb.cache.length)
     nxt = pb.canvas.tokens.cpu().numpy().reshape(pb.B, pb.C)
     for b in range(pb.B):
