@@ -115,10 +115,13 @@ _t_route = _sig("dg_test_route_from_logits", c_int32, _P(ModelConfig), c_void_p,
 _t_logits = _sig("dg_test_forward_logits", c_int32, _P(ModelConfig), _P(Weights), _P(KVCache), _P(Canvas),
                  _P(StepParams), c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p)
 
+_t_encode = _sig("dg_test_encode_append", c_int32, _P(ModelConfig), _P(Weights), _P(KVCache), c_void_p, c_int32,
+                 c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p)
+
 EXPORTED = ("dg_temperature", "dg_workspace_bytes", "dg_pack_weight_bf16", "dg_pack_weight_bf16_transposed",
             "dg_init_canvas", "dg_encode_append", "dg_denoise_step", "dg_commit_block", "dg_status_string",
             "dg_test_sample_from_logits", "dg_test_route_from_logits", "dg_test_forward_logits",
-            "dg_denoise_step_traced", "dg_encode_append_traced")
+            "dg_denoise_step_traced", "dg_encode_append_traced", "dg_test_encode_append")
 
 
 def _check(rc: int, where: str):
@@ -194,3 +197,9 @@ def dg_encode_append_traced(cfg, weights, cache, d_tokens, batch: int, n_tokens:
     _check(_encode_tr(ctypes.byref(cfg), ctypes.byref(weights), ctypes.byref(cache), d_tokens, batch, n_tokens, ws,
                       ws_bytes, stream, ctypes.byref(trace) if trace is not None else None),
            "dg_encode_append_traced")
+
+
+def dg_test_encode_append(cfg, weights, cache, d_tokens, batch: int, n_tokens: int, d_force_ids, d_router_logits, ws,
+                          ws_bytes: int, stream) -> None:
+    _check(_t_encode(ctypes.byref(cfg), ctypes.byref(weights), ctypes.byref(cache), d_tokens, batch, n_tokens,
+                     d_force_ids, d_router_logits, ws, ws_bytes, stream), "dg_test_encode_append")

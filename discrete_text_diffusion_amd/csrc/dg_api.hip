@@ -15,6 +15,7 @@ constexpr int kMoeBM = 32;        // row tile of the grouped expert GEMMs (bf16)
 constexpr int kSimpleBM = 16;     // row tile of the fp32 GEMMs
 constexpr int kMaxRoutePairs = 8192;
 constexpr int kMaxSplit = 16;
+constexpr int kRowPartRows = 2048;  // rows of the split-epilogue partial buffer (x split)
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
@@ -71,7 +72,7 @@ struct Plan {
   int Tdn;      // denoise tokens
   int att_rows; // attention partial rows (split x tokens)
   size_t x, n, q, ckv_k, ckv_v, o, att_o, att_ml, o_part, r_part, ids, wts, row_token, inv, offsets, tiles,
-      n_tiles, h, Y, lm_f, lm_i, logits, e_part, ebar, hsc, sc_out, total;
+      n_tiles, h, Y, lm_f, lm_i, logits, e_part, ebar, hsc, g_part, total;
 };
 
 Plan make_plan(const Shape& s, int batch, int max_canvas) {
@@ -109,7 +110,7 @@ Plan make_plan(const Shape& s, int batch, int max_canvas) {
   p.e_part = take(kMaxSplit * Tdn * s.d * 4);
   p.ebar = take(Tdn * s.d * s.act);
   p.hsc = take(Tdn * s.dsc * s.act);
-  p.sc_out = take(Tdn * s.d * 4);
+  p.g_part = take((size_t)kRowPartRows * std::max(s.qkv, s.dsc) * 4);  // widest split-epilogue GEMM
   p.total = off;
   return p;
 }
@@ -152,8 +153,18 @@ GemmArgs base_args() {
   return a;
 }
 
+#define DG_TRY(x)                 \
+  do {                            \
+    const int rc_ = (x);          \
+    if (rc_ != 0) return rc_ < 0 ? rc_ : DG_ERR_HIP; \
+  } while (0)
+
 // Enough workgroups to keep ~4 waves per SIMD streaming weights.
 constexpr int kTargetBlocks = 1024;
+// Row-resident GEMM: one 4-wave workgroup per CU; K-split partials of the
+// non-store epilogues use at most kRowPartRows rows x N of workspace.
+constexpr int kRowTargetBlocks = 256;
+constexpr int kRowMaxSplit = 16;
 
 int pick_split(int blocks_per_split, int K, int kc, int max_split) {
   int sp = std::max(1, std::min(max_split, (kTargetBlocks + blocks_per_split - 1) / std::max(1, blocks_per_split)));
@@ -161,13 +172,45 @@ int pick_split(int blocks_per_split, int K, int kc, int max_split) {
   return sp;
 }
 
-// Dense GEMM: out = act[M][K] . W[N][K]^T with the given epilogue.  Only
-// EPI_STORE_F32 may split K (partials at out_f32 + split * split_stride);
-// the split count used is returned in *used_split.
+// K split of the row-resident GEMM: about one workgroup per CU, at most
+// max_split, and at least two 64-wide K chunks per split.
+int row_split(int M, int N, int K, int max_split) {
+  const int base = ((M + 255) / 256) * ((N + 255) / 256);
+  int sp = std::max(1, std::min(max_split, (kRowTargetBlocks + base - 1) / base));
+  while (sp > 1 && K / 64 < 2 * sp) --sp;
+  return sp;
+}
+
+// Dense GEMM: out = act[M][K] . W[N][K]^T with the given epilogue.
+// EPI_STORE_F32 may split K up to max_split ways (partials at out_f32 +
+// split * split_stride; the split count used is returned in *used_split);
+// the other epilogues split K through fp32 partials in the workspace and a
+// summing epilogue kernel.
 int dense_gemm(const Ctx& c, GemmArgs a, int M, int N, int K, int max_split, int* used_split = nullptr) {
   a.M = M; a.N = N; a.K = K;
   a.n_main = 1;
   if (used_split) *used_split = 1;
+  if (c.s.dt == DG_DTYPE_BF16 && K % 64 == 0 && a.act_kind != ACT_BF16_SCALED && a.epi != EPI_GEGLU &&
+      a.epi != EPI_RESID) {
+    a.kt_main = K / 32;
+    a.n_fb = (N + 255) / 256;
+    const bool store = a.epi == EPI_STORE_F32;
+    // non-store epilogues: the partials must fit the split-epilogue buffer
+    const int64_t part_cap = (int64_t)kRowPartRows * std::max(c.s.qkv, c.s.dsc) / ((int64_t)M * N);
+    const int cap = store ? max_split : (int)std::min<int64_t>(kRowMaxSplit, part_cap);
+    const int sp = row_split(M, N, K, std::max(1, cap));
+    a.k_split = ((K / 64 + sp - 1) / sp) * 64;
+    a.n_split = (K + a.k_split - 1) / a.k_split;
+    if (store) {
+      if (used_split) *used_split = a.n_split;
+      return launch_rowgemm(a, nullptr, c.st);
+    }
+    GemmArgs pa = a;
+    pa.epi = EPI_STORE_F32; pa.out_f32 = c.at<float>(c.p.g_part); pa.ldo = N; pa.split_stride = (int64_t)M * N;
+    pa.alpha = 1.0f;
+    DG_TRY(launch_rowgemm(pa, nullptr, c.st));
+    return launch_split_epilogue(a, pa.out_f32, a.n_split, pa.split_stride, N, c.st);
+  }
   if (c.s.dt == DG_DTYPE_BF16) {
     // largest row tile that still gives enough workgroups (weights re-read
     // by the other row tiles of a feature block come from L2: tile_fastest)
@@ -193,11 +236,6 @@ int dense_gemm(const Ctx& c, GemmArgs a, int M, int N, int K, int max_split, int
   return launch_gemm_simple(a, c.st);
 }
 
-#define DG_TRY(x)                 \
-  do {                            \
-    const int rc_ = (x);          \
-    if (rc_ != 0) return rc_ < 0 ? rc_ : DG_ERR_HIP; \
-  } while (0)
 
 // The layer stack over T = n_seq * seq_len tokens whose embeddings are in
 // x / n.  causal: encode (k, v appended to the cache at rows L..); else the
@@ -266,7 +304,7 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
       a.w0 = lw.wo;
       a.epi = EPI_STORE_F32; a.out_f32 = c.at<float>(c.p.o_part); a.ldo = s.d; a.split_stride = (int64_t)T * s.d;
       int n_split = 1;
-      DG_TRY(dense_gemm(c, a, T, s.d, s.qdim, 8, &n_split));
+      DG_TRY(dense_gemm(c, a, T, s.d, s.qdim, std::min(16, 8 * c.p.T / T), &n_split));
       DG_TRY(launch_resid_norm(bf, c.at<float>(c.p.x), c.at<float>(c.p.o_part), n_split, (int64_t)T * s.d, xn, T, s.d,
                                s.eps, c.st));
     }
@@ -381,6 +419,7 @@ int embed_canvas(const Ctx& c, const dg_canvas* cv, const dg_step_params* p) {
   const bool ext = cv->sc_probs != nullptr;
   const bool carried = !ext && p->t >= 1 && cv->p_side != nullptr;
   const float* add = nullptr;
+  int add_split = 0;
   if (ext || carried) {
     if (!c.w->embed_t || !c.w->sc_up || !c.w->sc_down) return DG_ERR_INVALID_ARG;
     Phase ph(c, DG_PHASE_SELFCOND);
@@ -422,12 +461,14 @@ int embed_canvas(const Ctx& c, const dg_canvas* cv, const dg_step_params* p) {
     GemmArgs dn = base_args();
     dn.act = c.at<void>(c.p.hsc); dn.act_ld = s.dsc; dn.act_kind = bf ? ACT_BF16 : ACT_F32;
     dn.w0 = c.w->sc_down;
-    dn.epi = EPI_STORE_F32; dn.out_f32 = c.at<float>(c.p.sc_out); dn.ldo = s.d; dn.split_stride = 0;
-    DG_TRY(dense_gemm(c, dn, T, s.d, s.dsc, 1));
-    add = c.at<float>(c.p.sc_out);
+    // partials in e_part (free again after the reduction above), summed by the embedding kernel
+    dn.epi = EPI_STORE_F32; dn.out_f32 = c.at<float>(c.p.e_part); dn.ldo = s.d; dn.split_stride = (int64_t)T * s.d;
+    DG_TRY(dense_gemm(c, dn, T, s.d, s.dsc, kMaxSplit, &add_split));
+    add = c.at<float>(c.p.e_part);
   }
   Phase ph(c, DG_PHASE_EMBED);
-  return launch_embed_norm(bf, cv->tokens, c.w->embed, add, c.at<float>(c.p.x), c.at<void>(c.p.n), T, s.d, s.eps, c.st);
+  return launch_embed_norm(bf, cv->tokens, c.w->embed, add, add_split, (int64_t)T * s.d, c.at<float>(c.p.x),
+                           c.at<void>(c.p.n), T, s.d, s.eps, c.st);
 }
 
 // LM head + sampler statistics.  logits_out: test path (fp32 z written).
@@ -454,6 +495,12 @@ int lm_head(const Ctx& c, const dg_canvas* cv, const dg_step_params* p, float* l
   a.w0 = c.w->lm_head;
   a.alpha = c.w->lm_scale;
   a.M = T; a.N = s.V; a.K = s.d; a.n_main = 1; a.kt_main = s.d / 32;
+  if (bf && s.d % 64 == 0) {
+    a.n_fb = s.nvt;
+    a.n_split = 1;
+    a.k_split = s.d;
+    return launch_rowgemm(a, &lm, c.st);
+  }
   if (bf) {
     const int bm = 64;  // 64-row tiles keep several waves per SIMD streaming; other row tiles hit L2
     a.max_tiles = (T + bm - 1) / bm;
@@ -486,6 +533,10 @@ int check_step(const dg_step_params* p) {
 }
 
 }  // namespace
+
+static int encode_impl(const dg_model_config* cfg, const dg_weights* w, dg_kv_cache* cache, const int32_t* d_tokens,
+                       int32_t batch, int32_t n_tokens, void* d_ws, size_t ws_bytes, void* stream, dg_trace* trace,
+                       const int32_t* force_ids, float* router_out);
 
 extern "C" {
 
@@ -527,6 +578,21 @@ int dg_encode_append(const dg_model_config* cfg, const dg_weights* w, dg_kv_cach
 int dg_encode_append_traced(const dg_model_config* cfg, const dg_weights* w, dg_kv_cache* cache,
                             const int32_t* d_tokens, int32_t batch, int32_t n_tokens, void* d_ws, size_t ws_bytes,
                             void* stream, dg_trace* trace) {
+  return encode_impl(cfg, w, cache, d_tokens, batch, n_tokens, d_ws, ws_bytes, stream, trace, nullptr, nullptr);
+}
+
+int dg_test_encode_append(const dg_model_config* cfg, const dg_weights* w, dg_kv_cache* cache,
+                          const int32_t* d_tokens, int32_t batch, int32_t n_tokens, const int32_t* d_force_ids,
+                          float* d_router_logits, void* d_ws, size_t ws_bytes, void* stream) {
+  return encode_impl(cfg, w, cache, d_tokens, batch, n_tokens, d_ws, ws_bytes, stream, nullptr, d_force_ids,
+                     d_router_logits);
+}
+
+}  // extern "C"
+
+static int encode_impl(const dg_model_config* cfg, const dg_weights* w, dg_kv_cache* cache, const int32_t* d_tokens,
+                       int32_t batch, int32_t n_tokens, void* d_ws, size_t ws_bytes, void* stream, dg_trace* trace,
+                       const int32_t* force_ids, float* router_out) {
   DG_TRY(check_config(cfg));
   DG_TRY(check_weights(cfg, w));
   if (batch < 1 || n_tokens < 1 || !d_tokens) return DG_ERR_INVALID_ARG;
@@ -541,19 +607,26 @@ int dg_encode_append_traced(const dg_model_config* cfg, const dg_weights* w, dg_
   c.st = (hipStream_t)stream;
   c.w = w;
   c.tr = trace;
+  // test path: per-layer routes and router logits are indexed by the token
+  // rows of one chunk, so the whole encode must fit in one
+  if ((force_ids || router_out) && n_tokens > chunk) return DG_ERR_UNSUPPORTED;
+  c.force_ids = force_ids;
+  c.router_out = router_out;
   for (int done = 0; done < n_tokens; done += chunk) {
     const int nc = std::min(chunk, n_tokens - done);
     // gather this chunk's tokens [batch][nc] into the workspace token buffer
     int32_t* tok = c.at<int32_t>(c.p.ids);  // reused: ids are rewritten per layer after embedding
     for (int b = 0; b < batch; ++b)
       DG_TRY(launch_copy_i32(tok + b * nc, d_tokens + (int64_t)b * n_tokens + done, nc, c.st));
-    DG_TRY(launch_embed_norm(c.s.dt == DG_DTYPE_BF16, tok, w->embed, nullptr, c.at<float>(c.p.x), c.at<void>(c.p.n),
-                             batch * nc, c.s.d, c.s.eps, c.st));
+    DG_TRY(launch_embed_norm(c.s.dt == DG_DTYPE_BF16, tok, w->embed, nullptr, 0, 0, c.at<float>(c.p.x),
+                             c.at<void>(c.p.n), batch * nc, c.s.d, c.s.eps, c.st));
     DG_TRY(run_layers(c, cache, batch, nc, cache->length, true));
     cache->length += nc;
   }
   return DG_OK;
 }
+
+extern "C" {
 
 int dg_denoise_step(const dg_model_config* cfg, const dg_weights* w, const dg_kv_cache* cache, dg_canvas* cv,
                     const dg_step_params* p, void* d_ws, size_t ws_bytes, void* stream) {

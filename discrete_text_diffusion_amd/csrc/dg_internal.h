@@ -100,6 +100,13 @@ struct LmArgs {
 // k_gemm.hip
 int launch_wsgemm(const GemmArgs& a, int bm, int nwt, int kc, bool geglu, hipStream_t s);
 int launch_lmhead(const GemmArgs& a, const LmArgs& lm, int bm, hipStream_t s);
+// Row-resident GEMM (M rows in groups of 256, 256-feature blocks; 128 with
+// scaled activations): fp32 partials (EPI_STORE_F32), or with lm != null the
+// LM-head statistics epilogue.
+int launch_rowgemm(const GemmArgs& a, const LmArgs* lm, hipStream_t s);
+// Sum of K-split fp32 partials part[s][row][n] (pitch ldp), then a.epi.
+int launch_split_epilogue(const GemmArgs& a, const float* part, int n_split, int64_t split_stride, int ldp,
+                          hipStream_t s);
 int launch_gemm_simple(const GemmArgs& a, hipStream_t s);
 int launch_pack_bf16(bf16_t* dst, const bf16_t* src, int64_t rows, int64_t cols, int transposed, hipStream_t s);
 int launch_lm_partials_from_logits(const float* logits, int rows, const LmArgs& lm, hipStream_t s);
@@ -115,8 +122,8 @@ int launch_attention(int dtype, const void* q, int64_t q_ld, const void* k0, con
                      int64_t s1_head, int vp1, int len1, int n_prefix, int causal, int seq_len, int n_seq, int n_q,
                      int n_kv, int d, int n_split, float* part_o, float2* part_ml, void* out, hipStream_t s);
 // k_misc.hip
-int launch_embed_norm(int dtype, const int32_t* tok, const void* emb, const float* add, float* x, void* n, int T,
-                      int d, float eps, hipStream_t s);
+int launch_embed_norm(int dtype, const int32_t* tok, const void* emb, const float* add, int n_add, int64_t add_stride,
+                      float* x, void* n, int T, int d, float eps, hipStream_t s);
 int launch_resid_norm(int dtype, float* x, const float* part, int n_split, int64_t split_stride, void* n, int T, int d,
                       float eps, hipStream_t s);
 int launch_combine_norm(int dtype, float* x, const float* Y, const int32_t* inv, const float* w, int T, int k, int n_sh,

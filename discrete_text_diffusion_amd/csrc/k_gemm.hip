@@ -20,6 +20,8 @@
 // Block ids are remapped so that blocks sharing data (the feature blocks of
 // one row tile, or the row tiles of one feature block) sit on the same XCD:
 // hardware dispatches block b to XCD b % 8.
+#include <string.h>
+
 #include <type_traits>
 
 #include "dg_internal.h"
@@ -375,82 +377,162 @@ __global__ __launch_bounds__(kThreads) void k_wsgemm(GemmArgs a) {
 // zmax_k / argmax (first index), and the in-tile inverse-CDF candidate at the
 // row's u2 (first id whose in-tile cumulative mass exceeds u2 * S_k).  The
 // logits themselves are never written (except on the test path).
-__device__ __forceinline__ void row_tile_stats(const float* zrow, int row, int vt, const LmArgs& lm) {
-  const int lane = threadIdx.x & 63;
-  const float4 z4 = *reinterpret_cast<const float4*>(zrow + lane * 4);
-  const float z[4] = {z4.x, z4.y, z4.z, z4.w};
-  // argmax of z, lowest id on ties
-  float bz = z[0];
-  int bi = 0;
-#pragma unroll
-  for (int e = 1; e < 4; ++e)
-    if (z[e] > bz) { bz = z[e]; bi = e; }
-  bi += lane * 4;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float oz = __shfl_xor(bz, o, 64);
-    const int oi = __shfl_xor(bi, o, 64);
-    if (oz > bz || (oz == bz && oi < bi)) { bz = oz; bi = oi; }
-  }
-  float av[4], ex[4];
-  float mloc = -INFINITY;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    av[e] = z[e] * lm.inv_tau;
-    mloc = fmaxf(mloc, av[e]);
-  }
-  const float m = wave_max(mloc);
-  float s = 0.f, t = 0.f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    ex[e] = expf(av[e] - m);
-    s += ex[e];
-    t += ex[e] * (av[e] - m);
-  }
-  const float incl = wave_incl_scan(s);
-  const float S = __shfl(incl, 63, 64);
-  const float T = wave_sum(t);
-  // u2 of this row: Philox stream 2, word 1
-  const int canvas_id = row / lm.canvas, pos = row - canvas_id * lm.canvas;
-  const uint64_t seed = lm.seeds[canvas_id];
+// u2 of a row: Philox stream 2 (sampling), word 1, at (position, step, block).
+__device__ __forceinline__ float row_u2_seeded(int row, uint64_t seed, const LmArgs& lm) {
+  const int pos = row % lm.canvas;
   const dg_u32x4 w = dg_philox((uint32_t)pos, (uint32_t)lm.step, (uint32_t)lm.block, DG_STREAM_SAMPLE,
                                (uint32_t)seed, (uint32_t)(seed >> 32));
-  const float thr = dg_word_unit(w.y) * S;
-  float run = incl - s;
-  int hit = -1, lastpos = -1;
+  return dg_word_unit(w.y);
+}
+__device__ __forceinline__ float row_u2(int row, const LmArgs& lm) {
+  return row_u2_seeded(row, lm.seeds[row / lm.canvas], lm);
+}
+
+// Cross-lane steps inside one 16-lane DPP row.  The butterfly pairs (xor 1,
+// xor 2, then the half-row and row mirrors) combine groups that already hold
+// identical partials, so every lane of the row ends with the bitwise-same
+// result.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, true);
+}
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+constexpr int DPP_SHR1 = 0x111, DPP_SHR2 = 0x112, DPP_SHR4 = 0x114, DPP_SHR8 = 0x118;
+
+__device__ __forceinline__ float row16_sum(float x) {
+  x = x + dpp_f<DPP_XOR1>(x);
+  x = x + dpp_f<DPP_XOR2>(x);
+  x = x + dpp_f<DPP_HALF_MIRROR>(x);
+  return x + dpp_f<DPP_MIRROR>(x);
+}
+__device__ __forceinline__ int row16_max(int x) {
+  x = max(x, dpp_i<DPP_XOR1>(x));
+  x = max(x, dpp_i<DPP_XOR2>(x));
+  x = max(x, dpp_i<DPP_HALF_MIRROR>(x));
+  return max(x, dpp_i<DPP_MIRROR>(x));
+}
+// inclusive prefix sum over the lanes of a row (lanes before the row's first read 0)
+__device__ __forceinline__ float row16_incl_scan(float x) {
+  x = x + dpp_f<DPP_SHR1>(x);
+  x = x + dpp_f<DPP_SHR2>(x);
+  x = x + dpp_f<DPP_SHR4>(x);
+  return x + dpp_f<DPP_SHR8>(x);
+}
+
+// Statistics of four rows x one 256-id tile per wave: lane l works on row
+// l / 16 and the 16 ids 64 q + 4 (l % 16) + e (q, e < 4), read as four
+// float4 whose 16 lanes cover 256 contiguous bytes each.  z0: row 0 of the
+// group, rows `pitch` floats apart; rows >= nrows are not written.  u2: the
+// sampling uniform of this lane's row.
+__device__ __forceinline__ void tile_stats4(const float* z0, int64_t pitch, int nrows, int row0, int vt,
+                                            const LmArgs& lm, float u2) {
+  const int lane = threadIdx.x & 63, r = lane >> 4, sl = lane & 15;
+  const float* zr = z0 + (int64_t)min(r, nrows - 1) * pitch + 4 * sl;
+  float z[16];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    run += ex[e];
-    if (hit < 0 && run > thr) hit = e;
-    if (ex[e] > 0.f) lastpos = e;
+  for (int q = 0; q < 4; ++q) {
+    const float4 v = *reinterpret_cast<const float4*>(zr + 64 * q);
+    z[4 * q] = v.x; z[4 * q + 1] = v.y; z[4 * q + 2] = v.z; z[4 * q + 3] = v.w;
   }
-  const uint64_t hb = __ballot(hit >= 0);
-  int cand;
-  if (hb) {
-    const int src = __builtin_ctzll(hb);
-    cand = __shfl(lane * 4 + hit, src, 64);
-  } else {
-    const uint64_t pb = __ballot(lastpos >= 0);
-    const int src = 63 - __builtin_clzll(pb);
-    cand = __shfl(lane * 4 + lastpos, src, 64);
+  // zmax and its first id (k runs over this lane's ids in increasing order)
+  float bz = z[0];
+  int bc = 4 * sl;
+#pragma unroll
+  for (int k = 1; k < 16; ++k)
+    if (z[k] > bz) { bz = z[k]; bc = 64 * (k >> 2) + 4 * sl + (k & 3); }
+  auto argmax_step = [&](float oz, int oc) {
+    if (oz > bz || (oz == bz && oc < bc)) { bz = oz; bc = oc; }
+  };
+  argmax_step(dpp_f<DPP_XOR1>(bz), dpp_i<DPP_XOR1>(bc));
+  argmax_step(dpp_f<DPP_XOR2>(bz), dpp_i<DPP_XOR2>(bc));
+  argmax_step(dpp_f<DPP_HALF_MIRROR>(bz), dpp_i<DPP_HALF_MIRROR>(bc));
+  argmax_step(dpp_f<DPP_MIRROR>(bz), dpp_i<DPP_MIRROR>(bc));
+  // a = z / tau (tau > 0, so max a = round(zmax / tau)); exp(a - m) and moments
+  const float m = bz * lm.inv_tau;
+  float ex[16], w[4];
+  float t = 0.f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const float d = z[k] * lm.inv_tau - m;
+    ex[k] = expf(d);
+    t = fmaf(ex[k], d, t);
   }
-  const int64_t col = (int64_t)vt * 256;
-  if (lm.p_side) {
-    const int64_t pidx = (int64_t)row * lm.vocab + col + lane * 4;
-    if (lm.p_side_f32) {
-      *reinterpret_cast<float4*>(reinterpret_cast<float*>(lm.p_side) + pidx) = make_float4(ex[0], ex[1], ex[2], ex[3]);
-    } else {
-      const uint32_t lo = (uint32_t)f2bf(ex[0]) | ((uint32_t)f2bf(ex[1]) << 16);
-      const uint32_t hi = (uint32_t)f2bf(ex[2]) | ((uint32_t)f2bf(ex[3]) << 16);
-      *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(lm.p_side) + pidx) = make_uint2(lo, hi);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) w[q] = (ex[4 * q] + ex[4 * q + 1]) + (ex[4 * q + 2] + ex[4 * q + 3]);
+  const float S = row16_sum((w[0] + w[1]) + (w[2] + w[3]));
+  const float T = row16_sum(t);
+  // inverse CDF inside the tile: first id whose cumulative mass exceeds u2 S,
+  // walking 64-id blocks, then lanes, then the lane's four ids
+  const float thr = u2 * S;
+  float base = 0.f;
+  int qs = -1;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float bq = row16_sum(w[q]);
+    if (qs < 0) {
+      if (base + bq > thr) qs = q;
+      else base += bq;
     }
   }
-  if (lm.logits)
-    *reinterpret_cast<float4*>(lm.logits + (int64_t)row * lm.vocab + col + lane * 4) = z4;
-  if (lane == 0) {
+  int cand = -1;
+  if (qs >= 0) {
+    const float wq = qs == 0 ? w[0] : qs == 1 ? w[1] : qs == 2 ? w[2] : w[3];
+    const float incl = row16_incl_scan(wq);
+    const uint64_t hits = __ballot(base + incl > thr);
+    const uint32_t rowhits = (uint32_t)(hits >> (16 * r)) & 0xFFFFu;
+    if (rowhits && sl == __builtin_ctz(rowhits)) {
+      float run = base + (incl - wq);
+      int e_hit = -1, e_last = -1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = qs == 0 ? ex[e] : qs == 1 ? ex[4 + e] : qs == 2 ? ex[8 + e] : ex[12 + e];
+        run += x;
+        if (e_hit < 0 && run > thr) e_hit = e;
+        if (x > 0.f) e_last = e;
+      }
+      const int e = e_hit >= 0 ? e_hit : e_last;
+      if (e >= 0) cand = 64 * qs + 4 * sl + e;
+    }
+    cand = row16_max(cand);
+  }
+  if (cand < 0) {  // mass never exceeded u2 S (rounding): last id with mass
+    int lastc = -1;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (ex[k] > 0.f) lastc = max(lastc, 64 * (k >> 2) + 4 * sl + (k & 3));
+    cand = row16_max(lastc);
+  }
+  if (r >= nrows) return;
+  const int row = row0 + r;
+  const int64_t col = (int64_t)vt * 256;
+  if (lm.p_side) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t pidx = (int64_t)row * lm.vocab + col + 64 * q + 4 * sl;
+      if (lm.p_side_f32) {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(lm.p_side) + pidx) =
+            make_float4(ex[4 * q], ex[4 * q + 1], ex[4 * q + 2], ex[4 * q + 3]);
+      } else {
+        const uint32_t lo = (uint32_t)f2bf(ex[4 * q]) | ((uint32_t)f2bf(ex[4 * q + 1]) << 16);
+        const uint32_t hi = (uint32_t)f2bf(ex[4 * q + 2]) | ((uint32_t)f2bf(ex[4 * q + 3]) << 16);
+        *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(lm.p_side) + pidx) = make_uint2(lo, hi);
+      }
+    }
+  }
+  if (lm.logits) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<float4*>(lm.logits + (int64_t)row * lm.vocab + col + 64 * q + 4 * sl) =
+          make_float4(z[4 * q], z[4 * q + 1], z[4 * q + 2], z[4 * q + 3]);
+  }
+  if (sl == 0) {
     const int nvt = lm.vocab >> 8;
     lm.part_f[(int64_t)row * nvt + vt] = make_float4(m, S, T, bz);
-    lm.part_i[(int64_t)row * nvt + vt] = make_int2((int)col + cand, (int)col + bi);
+    lm.part_i[(int64_t)row * nvt + vt] = make_int2((int)col + cand, (int)col + bc);
   }
 }
 
@@ -492,22 +574,248 @@ __global__ __launch_bounds__(kThreads) void k_lmhead(GemmArgs a, LmArgs lm) {
       }
     }
     __syncthreads();
-    for (int rr = wave; rr < 64; rr += 4) {
+    for (int rr = wave * 4; rr < 64; rr += 16) {
       const int r = half * 64 + rr;
-      if (r < td.nrows) row_tile_stats(zt + rr * LM_ZLD, td.row0 + r, fb, lm);
+      if (r < td.nrows) {
+        const int nr = min(4, td.nrows - r);
+        tile_stats4(zt + rr * LM_ZLD, LM_ZLD, nr, td.row0 + r, fb, lm,
+                    row_u2(td.row0 + r + min((int)(threadIdx.x & 63) >> 4, nr - 1), lm));
+      }
     }
     __syncthreads();
   }
 }
 
+// ---------------------------------------------------------------------------
+// Row-resident GEMM for dense weights and few rows (the denoiser's canvas):
+// one workgroup of 8 waves holds all (up to 256) rows of a row group for a
+// block of 256 features, so a weight byte is read once per row group and K
+// split.  Wave w covers rows [128 (w / 4), +128) and features
+// [64 (w % 4), +64) of the block (8 x 4 accumulator tiles, two waves per
+// SIMD).  Per 32-wide K chunk a wave reads 8 KiB of activations and 4 KiB of
+// weights from LDS for 32 MFMAs.
+//
+// Both operands go straight from memory into a ring of RG_AHEAD + 1 LDS
+// stages with global_load_lds_dwordx4 (lane l of an instruction lands at
+// base + 16 l), RG_AHEAD chunks ahead of the MFMAs:
+//  * activations: one instruction fills 16 rows x 64 B; the 16-byte column
+//    groups of a row are XOR-swizzled by (row / 2) % 4, which keeps the
+//    B-operand reads free of bank conflicts;
+//  * weights: one instruction moves one packed 16 x 32 tile (1 KiB), already
+//    in A-operand lane order.
+// Memory counters complete in issue order, so one wait per chunk (for the
+// loads issued RG_AHEAD chunks earlier) and one barrier (the other waves'
+// parts of that stage) cover both.  Every load is unconditional (out-of-range
+// rows and chunks load clamped, in-bounds addresses that are never used),
+// which keeps the counts exact.
+//
+// Output: fp32 partials out_f32[split][row][n] = alpha * acc (EPI_STORE_F32),
+// or the LM-head statistics.
+constexpr int RG_THREADS = 512;
+constexpr int RG_ROWS = 256;
+constexpr int RG_KC = 32;
+constexpr int RG_AHEAD = 3;                          // prefetch distance (chunks)
+constexpr int RG_SLOTS = RG_AHEAD + 1;
+constexpr int RG_ROW_BYTES = RG_KC * 2;              // 64 B, no padding (swizzled)
+constexpr int RG_X_BYTES = RG_ROWS * RG_ROW_BYTES;   // activations of one chunk (16 KiB)
+constexpr int RG_STAGE_BYTES = RG_X_BYTES + 16 * 1024;  // + 16 weight tiles
+constexpr int RG_XDMA = RG_ROWS / 16 / 8;            // activation instructions per wave per chunk
+constexpr int RG_WDMA = 16 / 8;                      // weight tiles per wave per chunk
+constexpr int RG_NWT = 4;
+constexpr int RG_LOADS_PER_CHUNK = RG_XDMA + RG_WDMA;
+constexpr int RG_ZROWS = 128;                        // LM head: logit rows staged at a time
+constexpr int RG_LDS_BYTES = RG_SLOTS * RG_STAGE_BYTES > RG_ZROWS * LM_ZLD * 4 ? RG_SLOTS * RG_STAGE_BYTES
+                                                                                 : RG_ZROWS * LM_ZLD * 4;
+
+__device__ __forceinline__ int rg_swz(int row) { return (row >> 1) & 3; }
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <bool LMHEAD>
+__global__ __launch_bounds__(RG_THREADS, 1) void k_rowgemm(GemmArgs a, LmArgs lm) {
+  constexpr int MW = 8;
+  constexpr int NWT = RG_NWT;
+  // one LDS object (stages / logit tile, then the LM head's per-row sampling
+  // uniforms): a second object makes the compiler wait for every in-flight
+  // LDS DMA before each LDS read
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[RG_LDS_BYTES + (LMHEAD ? RG_ROWS * 4 : 0)];
+  float* u2s = reinterpret_cast<float*>(smem + RG_LDS_BYTES);
+
+  const int lb = xcd_logical_block(a.nblocks);
+  // order: row group fastest (shares the weights), then feature block (shares
+  // the activations of one K split), then split
+  const int tile = lb % a.max_tiles;
+  const int fb = (lb / a.max_tiles) % a.n_fb;
+  const int ks = lb / (a.max_tiles * a.n_fb);
+  if (ks >= a.n_split) return;
+  const int row0 = tile * RG_ROWS;
+  const int nrows = min(RG_ROWS, a.M - row0);
+  if (nrows <= 0) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rh = wave >> 2, cg = wave & 3;
+  const int kb = ks * a.k_split;
+  const int ke = min(a.K, kb + a.k_split);
+  const int nch = (ke - kb) / RG_KC;
+  if (nch <= 0) return;
+
+  f32x4_t acc[NWT][MW];
+#pragma unroll
+  for (int i = 0; i < NWT; ++i)
+#pragma unroll
+    for (int j = 0; j < MW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  bool wval[NWT];
+#pragma unroll
+  for (int i = 0; i < NWT; ++i) wval[i] = (fb * 16 + cg * NWT + i) * 16 < a.N;
+  // weight tiles moved by this wave: block tiles 2 wave + e (tiles past N reload tile 0)
+  const bf16_t* wsrc[RG_WDMA];
+#pragma unroll
+  for (int e = 0; e < RG_WDMA; ++e) {
+    const int ft = fb * 16 + wave * RG_WDMA + e;
+    wsrc[e] = reinterpret_cast<const bf16_t*>(a.w0) + ((int64_t)(ft * 16 < a.N ? ft : 0) * a.kt_main + (kb >> 5)) * 512 +
+              lane * 8;
+  }
+  // activation instruction d of this wave fills rows (wave*RG_XDMA + d)*16 + lane/4,
+  // physical column group lane%4 <- logical group (lane%4) ^ swz(row)
+  const bf16_t* xsrc[RG_XDMA];
+#pragma unroll
+  for (int d = 0; d < RG_XDMA; ++d) {
+    const int r = (wave * RG_XDMA + d) * 16 + (lane >> 2);
+    const int g = (lane & 3) ^ rg_swz(r);
+    xsrc[d] = reinterpret_cast<const bf16_t*>(a.act) + (int64_t)(row0 + min(r, nrows - 1)) * a.act_ld + kb + g * 8;
+  }
+
+  // chunk c's loads (clamped to the last chunk) into stage c % RG_SLOTS
+  auto issue = [&](int c) {
+    const int cc = min(c, nch - 1);
+    unsigned char* st = smem + (c % RG_SLOTS) * RG_STAGE_BYTES;
+#pragma unroll
+    for (int d = 0; d < RG_XDMA; ++d)
+      __builtin_amdgcn_global_load_lds(xsrc[d] + cc * RG_KC, (lds_void_t*)(st + (wave * RG_XDMA + d) * 1024), 16, 0,
+                                       0);
+#pragma unroll
+    for (int e = 0; e < RG_WDMA; ++e)
+      __builtin_amdgcn_global_load_lds(wsrc[e] + (int64_t)cc * 512,
+                                       (lds_void_t*)(st + RG_X_BYTES + (wave * RG_WDMA + e) * 1024), 16, 0, 0);
+  };
+
+  // LM head: each row's seed is loaded before the first chunks and used
+  // after the main loop has drained, so no wait for it stalls the pipeline
+  uint64_t seed = 0;
+  if constexpr (LMHEAD) {
+    seed = lm.seeds[(row0 + min(tid, nrows - 1)) / lm.canvas];
+    asm volatile("" ::: "memory");  // issue it before the chunk loads
+  }
+  for (int c = 0; c < RG_AHEAD; ++c) issue(c);
+  for (int c = 0; c < nch; ++c) {
+    // own loads of chunk c done, then a plain barrier: every wave's part of
+    // the stage is in LDS and every wave is done reading chunk c - 1 (its
+    // MFMAs consumed those reads), so that stage can be refilled.  No fence:
+    // it would wait for the loads still in flight.  The asm memory clobber
+    // keeps the compiler from moving LDS accesses across.
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((RG_AHEAD - 1) * RG_LOADS_PER_CHUNK) : "memory");
+    issue(c + RG_AHEAD);
+    const unsigned char* st = smem + (c % RG_SLOTS) * RG_STAGE_BYTES;
+    bf16x8_t wf[NWT];
+#pragma unroll
+    for (int i = 0; i < NWT; ++i)
+      wf[i] = *reinterpret_cast<const bf16x8_t*>(st + RG_X_BYTES + (cg * NWT + i) * 1024 + lane * 16);
+#pragma unroll
+    for (int j = 0; j < MW; ++j) {
+      const int r = rh * 128 + j * 16 + (lane & 15);
+      const bf16x8_t bx =
+          *reinterpret_cast<const bf16x8_t*>(st + r * RG_ROW_BYTES + (((lane >> 4) ^ rg_swz(r)) << 4));
+#pragma unroll
+      for (int i = 0; i < NWT; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[i], bx, acc[i][j], 0, 0, 0);
+    }
+  }
+  // drain the clamped prefetches before the LDS is reused or the wave ends
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  if constexpr (LMHEAD) {
+    if (tid < nrows) u2s[tid] = row_u2_seeded(row0 + tid, seed, lm);  // read after the next barrier
+  }
+
+  if constexpr (!LMHEAD) {
+#pragma unroll
+    for (int i = 0; i < NWT; ++i) {
+      if (!wval[i]) continue;
+      const int n = (fb * 16 + cg * NWT + i) * 16 + (lane >> 4) * 4;
+#pragma unroll
+      for (int j = 0; j < MW; ++j) {
+        const int r = rh * 128 + j * 16 + (lane & 15);
+        if (r < nrows) {
+          const f32x4_t g = acc[i][j];
+          *reinterpret_cast<float4*>(a.out_f32 + (int64_t)ks * a.split_stride + (int64_t)(row0 + r) * a.ldo + n) =
+              make_float4(a.alpha * g[0], a.alpha * g[1], a.alpha * g[2], a.alpha * g[3]);
+        }
+      }
+    }
+  } else {
+    // logits of 128 rows x 256 ids through LDS (one row half at a time), then
+    // one wave per row for the sampler statistics
+    float* zt = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (rh == half) {
+#pragma unroll
+        for (int i = 0; i < NWT; ++i) {
+          const int col = (cg * NWT + i) * 16 + (lane >> 4) * 4;
+#pragma unroll
+          for (int j = 0; j < MW; ++j) {
+            const f32x4_t v = acc[i][j];
+            *reinterpret_cast<float4*>(zt + (j * 16 + (lane & 15)) * LM_ZLD + col) =
+                make_float4(a.alpha * v[0], a.alpha * v[1], a.alpha * v[2], a.alpha * v[3]);
+          }
+        }
+      }
+      __syncthreads();
+      for (int rr = wave * 4; rr < RG_ZROWS; rr += 4 * (RG_THREADS / 64)) {
+        const int r = half * RG_ZROWS + rr;
+        if (r < nrows) {
+          const int nr = min(4, nrows - r);
+          tile_stats4(zt + rr * LM_ZLD, LM_ZLD, nr, row0 + r, fb, lm, u2s[r + min(lane >> 4, nr - 1)]);
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Sum of K-split partials, then the epilogue (QKV, GELU, activation store).
+__global__ __launch_bounds__(kThreads) void k_split_epilogue(GemmArgs a, const float* part, int n_split,
+                                                            int64_t split_stride, int ldp) {
+  const int64_t pairs = (int64_t)a.M * (a.N >> 1);
+  const int64_t p = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (p >= pairs) return;
+  const int row = (int)(p / (a.N >> 1));
+  const int n = (int)(p - (int64_t)row * (a.N >> 1)) * 2;
+  constexpr int kMaxS = 16;
+  float2 v[kMaxS];
+#pragma unroll
+  for (int s = 0; s < kMaxS; ++s)
+    v[s] = s < n_split ? *reinterpret_cast<const float2*>(part + s * split_stride + (int64_t)row * ldp + n)
+                       : make_float2(0.f, 0.f);
+  float g0 = v[0].x, g1 = v[0].y;
+#pragma unroll
+  for (int s = 1; s < kMaxS; ++s) {
+    g0 += v[s].x;
+    g1 += v[s].y;
+  }
+  epi_pair<bf16_t>(a, 0, row, n, g0, g1, g0, g1);
+}
+
 // Per-(row, tile) statistics straight from fp32 logits (fp32 models and the
-// sampler test entry point): one wave per (row, tile).
+// sampler test entry point): one wave per (four rows, tile).
 __global__ __launch_bounds__(kThreads) void k_partials_from_logits(const float* logits, int rows, LmArgs lm) {
   const int nvt = lm.vocab >> 8;
   const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (w >= rows * nvt) return;
-  const int row = w / nvt, vt = w - row * nvt;
-  row_tile_stats(logits + (int64_t)row * lm.vocab + (int64_t)vt * 256, row, vt, lm);
+  const int groups = (rows + 3) / 4;
+  if (w >= groups * nvt) return;
+  const int g = w / nvt, vt = w - g * nvt;
+  const int row0 = g * 4, nr = min(4, rows - row0);
+  const int my_row = row0 + min((int)(threadIdx.x & 63) >> 4, nr - 1);
+  tile_stats4(logits + (int64_t)row0 * lm.vocab + (int64_t)vt * 256, lm.vocab, nr, row0, vt, lm, row_u2(my_row, lm));
 }
 
 // ---------------------------------------------------------------------------
@@ -646,8 +954,36 @@ int launch_pack_bf16(bf16_t* dst, const bf16_t* src, int64_t rows, int64_t cols,
 }
 
 int launch_lm_partials_from_logits(const float* logits, int rows, const LmArgs& lm, hipStream_t s) {
-  const int64_t waves = (int64_t)rows * (lm.vocab >> 8);
+  const int64_t waves = (int64_t)((rows + 3) / 4) * (lm.vocab >> 8);
   hipLaunchKernelGGL(k_partials_from_logits, dim3((unsigned)DG_CEIL_DIV(waves, 4)), dim3(kThreads), 0, s,
                      logits, rows, lm);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+int launch_rowgemm(const GemmArgs& a0, const LmArgs* lm, hipStream_t s) {
+  GemmArgs a = a0;
+  if (a.tiles || a.row_map || a.w1 || a.act_kind != ACT_BF16 || a.M < 1 || a.N % 16 || a.K % RG_KC ||
+      a.k_split % RG_KC || a.act_ld % 8)
+    return -1;
+  if (!lm && (a.epi != EPI_STORE_F32 || !a.out_f32 || a.ldo % 4)) return -1;
+  if (lm && a.N % 256) return -1;
+  if (a.n_fb != (a.N + 255) / 256 || a.n_split < 1 || (int64_t)a.n_split * a.k_split < a.K) return -1;
+  a.max_tiles = (a.M + RG_ROWS - 1) / RG_ROWS;
+  a.nblocks = round8(a.max_tiles * a.n_fb * a.n_split);
+  LmArgs l;
+  if (lm) l = *lm;
+  else memset(&l, 0, sizeof(l));
+  const dim3 grid(a.nblocks), block(RG_THREADS);
+  if (lm) hipLaunchKernelGGL((k_rowgemm<true>), grid, block, 0, s, a, l);
+  else hipLaunchKernelGGL((k_rowgemm<false>), grid, block, 0, s, a, l);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+int launch_split_epilogue(const GemmArgs& a, const float* part, int n_split, int64_t split_stride, int ldp,
+                          hipStream_t s) {
+  if (n_split < 1 || n_split > 16 || a.N % 2) return -1;
+  const int64_t pairs = (int64_t)a.M * (a.N >> 1);
+  hipLaunchKernelGGL(k_split_epilogue, dim3((unsigned)DG_CEIL_DIV(pairs, kThreads)), dim3(kThreads), 0, s, a, part,
+                     n_split, split_stride, ldp);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }

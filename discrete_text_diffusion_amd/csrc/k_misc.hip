@@ -25,17 +25,26 @@ __device__ __forceinline__ void write_norm(const float* x, TA* n, int d, float e
   for (int i = threadIdx.x; i < d; i += 256) n[i] = to_act<TA>(x[i] * inv);
 }
 
-// x[t] = E[tok[t]] (+ add[t]); n[t] = RMSNorm(x[t]).
+// x[t] = E[tok[t]] (+ sum_s add[s][t], split order); n[t] = RMSNorm(x[t]).
 template <typename TA>
-__global__ __launch_bounds__(256) void k_embed_norm(const int32_t* tok, const TA* emb, const float* add, float* x,
-                                                   TA* n, int d, float eps) {
+__global__ __launch_bounds__(256) void k_embed_norm(const int32_t* tok, const TA* emb, const float* add, int n_add,
+                                                   int64_t add_stride, float* x, TA* n, int d, float eps) {
   __shared__ float red[4];
   const int64_t t = blockIdx.x;
   const TA* e = emb + (int64_t)tok[t] * d;
   float* xr = x + t * d;
+  constexpr int kMaxS = 16;
   for (int i = threadIdx.x; i < d; i += 256) {
     float v = ld_act<TA>(e + i);
-    if (add) v += add[t * d + i];
+    if (n_add > 0) {
+      float p[kMaxS];
+#pragma unroll
+      for (int s = 0; s < kMaxS; ++s) p[s] = s < n_add ? add[(int64_t)s * add_stride + t * d + i] : 0.f;
+      float acc = p[0];
+#pragma unroll
+      for (int s = 1; s < kMaxS; ++s) acc += p[s];
+      v += acc;
+    }
     xr[i] = v;
   }
   __syncthreads();
@@ -49,7 +58,7 @@ __global__ __launch_bounds__(256) void k_resid_norm(float* x, const float* part,
   __shared__ float red[4];
   const int64_t t = blockIdx.x;
   float* xr = x + t * d;
-  constexpr int kMaxS = 8;
+  constexpr int kMaxS = 16;
   for (int i = threadIdx.x; i < d; i += 256) {
     float v[kMaxS];
 #pragma unroll
@@ -144,18 +153,21 @@ __global__ __launch_bounds__(256) void k_copy_i32(int32_t* dst, const int32_t* s
 
 #define DG_OK_OR_HIP() (hipGetLastError() == hipSuccess ? 0 : -5)
 
-int launch_embed_norm(int dtype, const int32_t* tok, const void* emb, const float* add, float* x, void* n, int T,
-                      int d, float eps, hipStream_t s) {
+int launch_embed_norm(int dtype, const int32_t* tok, const void* emb, const float* add, int n_add, int64_t add_stride,
+                      float* x, void* n, int T, int d, float eps, hipStream_t s) {
+  if (n_add < 0 || n_add > 16 || (n_add > 0 && !add)) return -1;
   if (dtype == 1)
-    hipLaunchKernelGGL(k_embed_norm<bf16_t>, dim3(T), dim3(256), 0, s, tok, (const bf16_t*)emb, add, x, (bf16_t*)n, d, eps);
+    hipLaunchKernelGGL(k_embed_norm<bf16_t>, dim3(T), dim3(256), 0, s, tok, (const bf16_t*)emb, add, n_add, add_stride,
+                       x, (bf16_t*)n, d, eps);
   else
-    hipLaunchKernelGGL(k_embed_norm<float>, dim3(T), dim3(256), 0, s, tok, (const float*)emb, add, x, (float*)n, d, eps);
+    hipLaunchKernelGGL(k_embed_norm<float>, dim3(T), dim3(256), 0, s, tok, (const float*)emb, add, n_add, add_stride,
+                       x, (float*)n, d, eps);
   return DG_OK_OR_HIP();
 }
 
 int launch_resid_norm(int dtype, float* x, const float* part, int n_split, int64_t split_stride, void* n, int T, int d,
                       float eps, hipStream_t s) {
-  if (n_split < 1 || n_split > 8) return -1;
+  if (n_split < 1 || n_split > 16) return -1;
   if (dtype == 1)
     hipLaunchKernelGGL(k_resid_norm<bf16_t>, dim3(T), dim3(256), 0, s, x, part, n_split, split_stride, (bf16_t*)n, d, eps);
   else

@@ -281,6 +281,16 @@ int dg_test_forward_logits(const dg_model_config* cfg, const dg_weights* w, cons
                            float* d_router_logits, float* d_logits, void* d_ws, size_t ws_bytes,
                            void* stream);
 
+/* Causal encode-and-append as in dg_encode_append, with the routing of every
+ * layer optionally forced and observed as in dg_test_forward_logits:
+ * d_force_ids [n_layers][batch*n_tokens][top_k] (rank order), d_router_logits
+ * [n_layers][batch*n_tokens][n_experts] fp32, rows in [batch][position]
+ * order.  The whole encode must fit in one internal chunk (batch*n_tokens
+ * <= 1024 and batch*n_tokens*top_k <= 8192), else DG_ERR_UNSUPPORTED. */
+int dg_test_encode_append(const dg_model_config* cfg, const dg_weights* w, dg_kv_cache* cache,
+                          const int32_t* d_tokens, int32_t batch, int32_t n_tokens, const int32_t* d_force_ids,
+                          float* d_router_logits, void* d_ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

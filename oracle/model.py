@@ -36,6 +36,8 @@ entries).  fp32 models round nothing.
 """
 from __future__ import annotations
 
+import contextlib
+
 import numpy as np
 
 import synth
@@ -80,9 +82,8 @@ class Weights:
         shp = self._shape_of(name)
         if dt == "fp8":
             raise NotImplementedError("fp8 weights are decoded by oracle.fp8")
-        raw = synth.normal(self.shape.weight_seed, tid, shp, self.shape.weight_std,
-                           "bf16" if dt == "bf16" else "f32")
-        w = (synth.bf16_bits_to_f32(raw) if dt == "bf16" else raw).astype(np.float64)
+        w = synth.normal(self.shape.weight_seed, tid, shp, self.shape.weight_std,
+                         "bf16_f64" if dt == "bf16" else "f32").astype(np.float64, copy=False)
         if self._cache is not None:
             self._cache[key] = w
         return w
@@ -91,6 +92,34 @@ class Weights:
         if self._cache is not None:
             for k in [k for k in self._cache if k[1] == layer]:
                 del self._cache[k]
+
+
+# Every product below is evaluated by mm().  By default it accumulates in
+# float64.  accumulation("f32") evaluates the same definition with float32
+# operands (exact copies of the bf16 values that feed each product) and
+# float32 sums: a second correct evaluation order, used only to measure how
+# far two such evaluations drift apart on a given problem (bf16 rounding of
+# activations turns last-bit differences into whole-ulp ones).  Expected values
+# always come from the float64 default.
+_ACC = ["f64"]
+
+
+@contextlib.contextmanager
+def accumulation(kind: str):
+    if kind not in ("f64", "f32"):
+        raise ValueError(kind)
+    old = _ACC[0]
+    _ACC[0] = kind
+    try:
+        yield
+    finally:
+        _ACC[0] = old
+
+
+def mm(a, b) -> np.ndarray:
+    if _ACC[0] == "f64":
+        return np.asarray(a) @ np.asarray(b)
+    return (np.asarray(a, dtype=np.float32) @ np.asarray(b, dtype=np.float32)).astype(np.float64)
 
 
 def round_act(shape: ModelShape, x: np.ndarray) -> np.ndarray:
@@ -118,9 +147,9 @@ def embed(shape: ModelShape, W: Weights, tokens: np.ndarray, sc_probs=None) -> n
     x = E[np.asarray(tokens)]
     if sc_probs is not None:
         P = round_act(shape, np.asarray(sc_probs, dtype=np.float64))
-        ebar = round_act(shape, P @ E)                       # expected embedding
-        h = round_act(shape, gelu_tanh(ebar @ W.get("sc_up").T))
-        x = x + h @ W.get("sc_down").T
+        ebar = round_act(shape, mm(P, E))                       # expected embedding
+        h = round_act(shape, gelu_tanh(mm(ebar, W.get("sc_up").T)))
+        x = x + mm(h, W.get("sc_down").T)
     return x
 
 
@@ -142,12 +171,12 @@ def attention(shape: ModelShape, q, k_all, v_all, n_prefix: int, causal: bool) -
     scale = 1.0 / np.sqrt(shape.d_head)
     for h in range(shape.n_q_heads):
         hk = h // group
-        s = (q[:, h, :] @ k_all[hk].T) * scale
+        s = mm(q[:, h, :], k_all[hk].T) * scale
         s = np.where(mask, s, -np.inf)
         s = s - s.max(axis=1, keepdims=True)
         e = np.exp(s)
         pr = e / e.sum(axis=1, keepdims=True)
-        out[:, h, :] = pr @ v_all[hk]
+        out[:, h, :] = mm(pr, v_all[hk])
     return out
 
 
@@ -167,15 +196,15 @@ def route(shape: ModelShape, r: np.ndarray):
 
 def geglu(shape: ModelShape, u, wg, wu, wd):
     """Wd (gelu_tanh(Wg u) * (Wu u)), hidden rounded as a GEMM input."""
-    h = round_act(shape, gelu_tanh(u @ wg.T) * (u @ wu.T))
-    return h @ wd.T
+    h = round_act(shape, gelu_tanh(mm(u, wg.T)) * mm(u, wu.T))
+    return mm(h, wd.T)
 
 
 def moe(shape: ModelShape, W: Weights, layer: int, n2: np.ndarray, ret_routing=False):
     """Shared expert + weighted sum of the top-k routed experts, in rank order.
 
     n2: [T, d] (already rounded).  Returns y [T, d]."""
-    r = n2 @ W.get("wr", layer).T
+    r = mm(n2, W.get("wr", layer).T)
     ids, w = route(shape, r)
     y = geglu(shape, n2, W.get("sh_g", layer), W.get("sh_u", layer), W.get("sh_d", layer))
     exg, exu, exd = W.get("ex_g", layer), W.get("ex_u", layer), W.get("ex_d", layer)
@@ -202,7 +231,7 @@ def layer_forward(shape: ModelShape, W: Weights, layer: int, x: np.ndarray, cach
     L = cache.length
     s = shape
     nrm = round_act(s, rmsnorm(x, s.norm_eps))
-    qkv = nrm @ W.get("wqkv", layer).T                           # [B, n, rows]
+    qkv = mm(nrm, W.get("wqkv", layer).T)                           # [B, n, rows]
     q = qkv[..., : s.q_dim].reshape(B, n, s.n_q_heads, s.d_head)
     k = qkv[..., s.q_dim: s.q_dim + s.kv_dim].reshape(B, n, s.n_kv_heads, s.d_head)
     v = qkv[..., s.q_dim + s.kv_dim:].reshape(B, n, s.n_kv_heads, s.d_head)
@@ -219,7 +248,7 @@ def layer_forward(shape: ModelShape, W: Weights, layer: int, x: np.ndarray, cach
         cache.k[layer][:, :, L:L + n] = k.transpose(0, 2, 1, 3)
         cache.v[layer][:, :, L:L + n] = v.transpose(0, 2, 1, 3)
     o = round_act(s, o.reshape(B, n, s.q_dim))
-    x = x + o @ W.get("wo", layer).T
+    x = x + mm(o, W.get("wo", layer).T)
     n2 = round_act(s, rmsnorm(x, s.norm_eps)).reshape(B * n, d)
     y, r, ids, w = moe(s, W, layer, n2, ret_routing=True)
     if trace is not None:
@@ -232,4 +261,4 @@ def layer_forward(shape: ModelShape, W: Weights, layer: int, x: np.ndarray, cach
 def final_logits(shape: ModelShape, W: Weights, x: np.ndarray, lm_scale: float) -> np.ndarray:
     """z = s_lm * (RMSNorm(x) W_lm^T)."""
     nrm = round_act(shape, rmsnorm(x, shape.norm_eps))
-    return lm_scale * (nrm @ W.get("lm_head").T)
+    return lm_scale * mm(nrm, W.get("lm_head").T)

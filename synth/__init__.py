@@ -65,6 +65,7 @@ def _get_lib():
         lib.synth_scale_for_std.restype = f32
         lib.synth_normal_f32.argtypes = [u64, u64, u64, u64, f32, vp]
         lib.synth_normal_bf16.argtypes = [u64, u64, u64, u64, f32, vp]
+        lib.synth_normal_bf16_as_f64.argtypes = [u64, u64, u64, u64, f32, vp]
         lib.synth_tokens.argtypes = [u64, u64, u64, u64, ctypes.c_uint32, vp]
         lib.synth_dirichlet_rows.argtypes = [u64, u64, i64, i64, ctypes.c_double, vp]
         _lib = lib
@@ -78,7 +79,8 @@ def scale_for_std(std: float) -> np.float32:
 def normal(seed: int, tensor: int, shape, std: float, dtype: str = "bf16", start: int = 0):
     """N(0, std^2)-shaped values (Irwin-Hall of 4 uniforms).
 
-    dtype "bf16" returns uint16 bit patterns, "f32" returns float32."""
+    dtype "bf16" returns uint16 bit patterns, "f32" returns float32,
+    "bf16_f64" the bf16 values widened to float64."""
     n = int(np.prod(shape))
     lib = _get_lib()
     sc = ctypes.c_float(scale_for_std(std))
@@ -88,6 +90,9 @@ def normal(seed: int, tensor: int, shape, std: float, dtype: str = "bf16", start
     elif dtype == "f32":
         out = np.empty(n, dtype=np.float32)
         lib.synth_normal_f32(seed, tensor, start, n, sc, out.ctypes.data)
+    elif dtype == "bf16_f64":
+        out = np.empty(n, dtype=np.float64)
+        lib.synth_normal_bf16_as_f64(seed, tensor, start, n, sc, out.ctypes.data)
     else:
         raise ValueError(dtype)
     return out.reshape(shape)

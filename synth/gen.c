@@ -64,6 +64,19 @@ void synth_normal_bf16(uint64_t seed, uint64_t tensor, uint64_t start, uint64_t 
     out[j] = synth_bf16_rne(synth_normal_value(synth_hash(seed, tensor, start + (uint64_t)j), scale));
 }
 
+/* The bf16 values of synth_normal_bf16, widened exactly to double (what an
+ * fp64 consumer of bf16 tensors reads). */
+void synth_normal_bf16_as_f64(uint64_t seed, uint64_t tensor, uint64_t start, uint64_t count, float scale,
+                              double* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < (int64_t)count; ++j) {
+    const uint32_t u = (uint32_t)synth_bf16_rne(synth_normal_value(synth_hash(seed, tensor, start + (uint64_t)j), scale)) << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    out[j] = (double)f;
+  }
+}
+
 void synth_tokens(uint64_t seed, uint64_t tensor, uint64_t start, uint64_t count, uint32_t vocab,
                   int32_t* out) {
   for (uint64_t j = 0; j < count; ++j) {
