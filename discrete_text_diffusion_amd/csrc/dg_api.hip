@@ -428,15 +428,25 @@ int embed_canvas(const Ctx& c, const dg_canvas* cv, const dg_step_params* p) {
     if (ext) {
       a.act = cv->sc_probs; a.act_kind = ACT_F32;
     } else {
+      // carried: bf16 exp(a - m_k) with the tile-major factors exp(m_k - m) / S
       a.act = cv->p_side; a.act_kind = bf ? ACT_BF16_SCALED : ACT_F32;
-      a.act_scale = cv->p_scale; a.scale_ld = s.nvt;
+      a.act_scale = cv->p_scale; a.scale_ld = 1; a.scale_tile_ld = T;
     }
     a.act_ld = s.V;
     a.w0 = c.w->embed_t;
     a.epi = EPI_STORE_F32; a.out_f32 = c.at<float>(c.p.e_part); a.ldo = s.d; a.split_stride = (int64_t)T * s.d;
     a.M = T; a.N = s.d; a.K = s.V; a.n_main = 1; a.kt_main = s.V / 32;
     int n_split = 1;
-    if (bf) {
+    if (bf && !ext) {
+      // row-resident kernel: 128-feature blocks, vocabulary split in whole 256-id tiles
+      a.n_fb = (s.d + 127) / 128;
+      const int rg = (T + 255) / 256;
+      n_split = std::max(1, std::min(kMaxSplit, kRowTargetBlocks / std::max(1, rg * a.n_fb)));
+      a.k_split = ((s.V / 256 + n_split - 1) / n_split) * 256;
+      n_split = (s.V + a.k_split - 1) / a.k_split;
+      a.n_split = n_split;
+      DG_TRY(launch_rowgemm(a, nullptr, c.st));
+    } else if (bf) {
       const int bm = 128, nwt = 2;
       a.max_tiles = (T + bm - 1) / bm;
       a.n_fb = (s.d + 64 * nwt - 1) / (64 * nwt);

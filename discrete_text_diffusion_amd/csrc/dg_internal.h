@@ -46,8 +46,9 @@ struct GemmArgs {
   const void* act;
   int64_t act_ld;
   int32_t act_kind;
-  const float* act_scale;  // ACT_BF16_SCALED: [row][K/256]
+  const float* act_scale;  // ACT_BF16_SCALED: factor of (row, K tile t) at row * scale_ld + t * scale_tile_ld
   int64_t scale_ld;
+  int64_t scale_tile_ld;
   const int32_t* row_map;  // output row -> activation row (null: identity)
   // weights (the MFMA A operand), packed tiles; groups < n_main use w0/w1
   // with w_group_stride, the others use w0_alt/w1_alt.
@@ -101,8 +102,8 @@ struct LmArgs {
 int launch_wsgemm(const GemmArgs& a, int bm, int nwt, int kc, bool geglu, hipStream_t s);
 int launch_lmhead(const GemmArgs& a, const LmArgs& lm, int bm, hipStream_t s);
 // Row-resident GEMM (M rows in groups of 256, 256-feature blocks; 128 with
-// scaled activations): fp32 partials (EPI_STORE_F32), or with lm != null the
-// LM-head statistics epilogue.
+// scaled activations, whose K and k_split are multiples of 256): fp32
+// partials (EPI_STORE_F32), or with lm != null the LM-head statistics.
 int launch_rowgemm(const GemmArgs& a, const LmArgs* lm, hipStream_t s);
 // Sum of K-split fp32 partials part[s][row][n] (pitch ldp), then a.epi.
 int launch_split_epilogue(const GemmArgs& a, const float* part, int n_split, int64_t split_stride, int ldp,

@@ -307,7 +307,7 @@ __device__ __forceinline__ void wsgemm_mainloop(const GemmArgs& a, const GemmTil
           if (r < td.nrows) {
             const int orow = td.row0 + r;
             const int ar = a.row_map ? a.row_map[orow] : orow;
-            sc = a.act_scale[(int64_t)ar * a.scale_ld + tile];
+            sc = a.act_scale[(int64_t)ar * a.scale_ld + (int64_t)tile * a.scale_tile_ld];
           }
 #pragma unroll
           for (int i = 0; i < NWT; ++i) {
@@ -589,11 +589,11 @@ __global__ __launch_bounds__(kThreads) void k_lmhead(GemmArgs a, LmArgs lm) {
 // ---------------------------------------------------------------------------
 // Row-resident GEMM for dense weights and few rows (the denoiser's canvas):
 // one workgroup of 8 waves holds all (up to 256) rows of a row group for a
-// block of 256 features, so a weight byte is read once per row group and K
+// block of BN features, so a weight byte is read once per row group and K
 // split.  Wave w covers rows [128 (w / 4), +128) and features
-// [64 (w % 4), +64) of the block (8 x 4 accumulator tiles, two waves per
-// SIMD).  Per 32-wide K chunk a wave reads 8 KiB of activations and 4 KiB of
-// weights from LDS for 32 MFMAs.
+// [NWT 16 (w % 4), +NWT 16) of the block (8 x NWT accumulator tiles, two
+// waves per SIMD).  Per 32-wide K chunk a wave reads 8 KiB of activations and
+// NWT KiB of weights from LDS for 8 NWT MFMAs.
 //
 // Both operands go straight from memory into a ring of RG_AHEAD + 1 LDS
 // stages with global_load_lds_dwordx4 (lane l of an instruction lands at
@@ -607,10 +607,17 @@ __global__ __launch_bounds__(kThreads) void k_lmhead(GemmArgs a, LmArgs lm) {
 // loads issued RG_AHEAD chunks earlier) and one barrier (the other waves'
 // parts of that stage) cover both.  Every load is unconditional (out-of-range
 // rows and chunks load clamped, in-bounds addresses that are never used),
-// which keeps the counts exact.
+// which keeps the counts exact; a wave with extra loads in flight only waits
+// longer.
 //
-// Output: fp32 partials out_f32[split][row][n] = alpha * acc (EPI_STORE_F32),
-// or the LM-head statistics.
+// Variants:
+//  * plain (NWT 4, 256 features): fp32 partials out_f32[split][row][n] = alpha acc;
+//  * LM head (NWT 4): the sampler statistics of each 256-id tile instead;
+//  * scaled activations (NWT 2, 128 features): bf16 rows whose 256-wide K
+//    tiles carry a per-row factor; the raw products of a K tile accumulate
+//    apart and are folded in as acc += factor * partial at the tile's end.
+//    The factors, stored tile-major ([K/256][rows] fp32), are DMA'd by wave 0
+//    with the first chunk of each K tile into a two-slot LDS ring.
 constexpr int RG_THREADS = 512;
 constexpr int RG_ROWS = 256;
 constexpr int RG_KC = 32;
@@ -618,28 +625,36 @@ constexpr int RG_AHEAD = 3;                          // prefetch distance (chunk
 constexpr int RG_SLOTS = RG_AHEAD + 1;
 constexpr int RG_ROW_BYTES = RG_KC * 2;              // 64 B, no padding (swizzled)
 constexpr int RG_X_BYTES = RG_ROWS * RG_ROW_BYTES;   // activations of one chunk (16 KiB)
-constexpr int RG_STAGE_BYTES = RG_X_BYTES + 16 * 1024;  // + 16 weight tiles
 constexpr int RG_XDMA = RG_ROWS / 16 / 8;            // activation instructions per wave per chunk
-constexpr int RG_WDMA = 16 / 8;                      // weight tiles per wave per chunk
-constexpr int RG_NWT = 4;
-constexpr int RG_LOADS_PER_CHUNK = RG_XDMA + RG_WDMA;
 constexpr int RG_ZROWS = 128;                        // LM head: logit rows staged at a time
-constexpr int RG_LDS_BYTES = RG_SLOTS * RG_STAGE_BYTES > RG_ZROWS * LM_ZLD * 4 ? RG_SLOTS * RG_STAGE_BYTES
-                                                                                 : RG_ZROWS * LM_ZLD * 4;
+
+template <bool LMHEAD, bool SCALED>
+struct RgCfg {
+  static constexpr int NWT = SCALED ? 2 : 4;
+  static constexpr int BN = 4 * NWT * 16;                  // features per workgroup
+  static constexpr int WDMA = BN / 16 / 8;                 // weight tiles per wave per chunk
+  static constexpr int LOADS = RG_XDMA + WDMA;             // loads per wave per chunk
+  static constexpr int STAGE = RG_X_BYTES + BN * 64;       // activations + weight tiles
+  static constexpr int RING = RG_SLOTS * STAGE;
+  static constexpr int BODY = LMHEAD && RG_ZROWS * LM_ZLD * 4 > RING ? RG_ZROWS * LM_ZLD * 4 : RING;
+  static constexpr int EXTRA = LMHEAD ? RG_ROWS * 4 : SCALED ? 2 * RG_ROWS * 4 : 0;  // uniforms / factor ring
+  static constexpr int LDS = BODY + EXTRA;
+};
 
 __device__ __forceinline__ int rg_swz(int row) { return (row >> 1) & 3; }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-template <bool LMHEAD>
+template <bool LMHEAD, bool SCALED>
 __global__ __launch_bounds__(RG_THREADS, 1) void k_rowgemm(GemmArgs a, LmArgs lm) {
+  using C = RgCfg<LMHEAD, SCALED>;
   constexpr int MW = 8;
-  constexpr int NWT = RG_NWT;
-  // one LDS object (stages / logit tile, then the LM head's per-row sampling
-  // uniforms): a second object makes the compiler wait for every in-flight
-  // LDS DMA before each LDS read
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[RG_LDS_BYTES + (LMHEAD ? RG_ROWS * 4 : 0)];
-  float* u2s = reinterpret_cast<float*>(smem + RG_LDS_BYTES);
+  constexpr int NWT = C::NWT;
+  // one LDS object (stages / logit tile, then the per-row uniforms or factor
+  // ring): a second object makes the compiler wait for every in-flight LDS
+  // DMA before each LDS read
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS];
+  float* extra = reinterpret_cast<float*>(smem + C::BODY);
 
   const int lb = xcd_logical_block(a.nblocks);
   // order: row group fastest (shares the weights), then feature block (shares
@@ -660,19 +675,26 @@ __global__ __launch_bounds__(RG_THREADS, 1) void k_rowgemm(GemmArgs a, LmArgs lm
   if (nch <= 0) return;
 
   f32x4_t acc[NWT][MW];
+  f32x4_t accu[NWT][SCALED ? MW : 1];
 #pragma unroll
   for (int i = 0; i < NWT; ++i)
 #pragma unroll
-    for (int j = 0; j < MW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < MW; ++j) {
+      acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if constexpr (SCALED) accu[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
 
   bool wval[NWT];
 #pragma unroll
-  for (int i = 0; i < NWT; ++i) wval[i] = (fb * 16 + cg * NWT + i) * 16 < a.N;
-  // weight tiles moved by this wave: block tiles 2 wave + e (tiles past N reload tile 0)
-  const bf16_t* wsrc[RG_WDMA];
+  for (int i = 0; i < NWT; ++i) wval[i] = (fb * (C::BN / 16) + cg * NWT + i) * 16 < a.N;
+  // weight tiles moved by this wave: block tiles WDMA wave + e (tiles past N reload tile 0)
+  // (fixed-size array: a template-dependent size captured by the lambda below
+  // makes hipcc drop the host-side launch stubs of this kernel)
+  const bf16_t* wsrc[2];
+  static_assert(C::WDMA <= 2, "weight tiles per wave per chunk");
 #pragma unroll
-  for (int e = 0; e < RG_WDMA; ++e) {
-    const int ft = fb * 16 + wave * RG_WDMA + e;
+  for (int e = 0; e < C::WDMA; ++e) {
+    const int ft = fb * (C::BN / 16) + wave * C::WDMA + e;
     wsrc[e] = reinterpret_cast<const bf16_t*>(a.w0) + ((int64_t)(ft * 16 < a.N ? ft : 0) * a.kt_main + (kb >> 5)) * 512 +
               lane * 8;
   }
@@ -689,15 +711,28 @@ __global__ __launch_bounds__(RG_THREADS, 1) void k_rowgemm(GemmArgs a, LmArgs lm
   // chunk c's loads (clamped to the last chunk) into stage c % RG_SLOTS
   auto issue = [&](int c) {
     const int cc = min(c, nch - 1);
-    unsigned char* st = smem + (c % RG_SLOTS) * RG_STAGE_BYTES;
+    unsigned char* st = smem + (c % RG_SLOTS) * C::STAGE;
 #pragma unroll
     for (int d = 0; d < RG_XDMA; ++d)
       __builtin_amdgcn_global_load_lds(xsrc[d] + cc * RG_KC, (lds_void_t*)(st + (wave * RG_XDMA + d) * 1024), 16, 0,
                                        0);
 #pragma unroll
-    for (int e = 0; e < RG_WDMA; ++e)
+    for (int e = 0; e < C::WDMA; ++e)
       __builtin_amdgcn_global_load_lds(wsrc[e] + (int64_t)cc * 512,
-                                       (lds_void_t*)(st + RG_X_BYTES + (wave * RG_WDMA + e) * 1024), 16, 0, 0);
+                                       (lds_void_t*)(st + RG_X_BYTES + (wave * C::WDMA + e) * 1024), 16, 0, 0);
+    if constexpr (SCALED) {
+      // first chunk of a K tile: wave 0 fetches the tile's 256 row factors
+      const int k0 = kb + cc * RG_KC;
+      if (wave == 0 && c == cc && (k0 & 255) == 0) {
+        const int kt = k0 >> 8;
+        float* slot = extra + (kt & 1) * RG_ROWS;
+#pragma unroll
+        for (int i = 0; i < RG_ROWS / 64; ++i)
+          __builtin_amdgcn_global_load_lds(
+              a.act_scale + (int64_t)kt * a.scale_tile_ld + (int64_t)(row0 + min(64 * i + lane, nrows - 1)) * a.scale_ld,
+              (lds_void_t*)(slot + 64 * i), 4, 0, 0);
+      }
+    }
   };
 
   // LM head: each row's seed is loaded before the first chunks and used
@@ -714,9 +749,9 @@ __global__ __launch_bounds__(RG_THREADS, 1) void k_rowgemm(GemmArgs a, LmArgs lm
     // MFMAs consumed those reads), so that stage can be refilled.  No fence:
     // it would wait for the loads still in flight.  The asm memory clobber
     // keeps the compiler from moving LDS accesses across.
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((RG_AHEAD - 1) * RG_LOADS_PER_CHUNK) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((RG_AHEAD - 1) * C::LOADS) : "memory");
     issue(c + RG_AHEAD);
-    const unsigned char* st = smem + (c % RG_SLOTS) * RG_STAGE_BYTES;
+    const unsigned char* st = smem + (c % RG_SLOTS) * C::STAGE;
     bf16x8_t wf[NWT];
 #pragma unroll
     for (int i = 0; i < NWT; ++i)
@@ -727,20 +762,36 @@ __global__ __launch_bounds__(RG_THREADS, 1) void k_rowgemm(GemmArgs a, LmArgs lm
       const bf16x8_t bx =
           *reinterpret_cast<const bf16x8_t*>(st + r * RG_ROW_BYTES + (((lane >> 4) ^ rg_swz(r)) << 4));
 #pragma unroll
-      for (int i = 0; i < NWT; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[i], bx, acc[i][j], 0, 0, 0);
+      for (int i = 0; i < NWT; ++i) {
+        if constexpr (SCALED) accu[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[i], bx, accu[i][j], 0, 0, 0);
+        else acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[i], bx, acc[i][j], 0, 0, 0);
+      }
+    }
+    if constexpr (SCALED) {
+      const int kend = kb + (c + 1) * RG_KC;
+      if ((kend & 255) == 0) {
+        // end of K tile kt: its factors arrived with the tile's first chunk
+        const float* slot = extra + (((kend >> 8) - 1) & 1) * RG_ROWS;
+#pragma unroll
+        for (int j = 0; j < MW; ++j) {
+          const float sc = slot[rh * 128 + j * 16 + (lane & 15)];
+#pragma unroll
+          for (int i = 0; i < NWT; ++i) {
+            acc[i][j] += sc * accu[i][j];
+            accu[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
+        }
+      }
     }
   }
   // drain the clamped prefetches before the LDS is reused or the wave ends
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-  if constexpr (LMHEAD) {
-    if (tid < nrows) u2s[tid] = row_u2_seeded(row0 + tid, seed, lm);  // read after the next barrier
-  }
 
   if constexpr (!LMHEAD) {
 #pragma unroll
     for (int i = 0; i < NWT; ++i) {
       if (!wval[i]) continue;
-      const int n = (fb * 16 + cg * NWT + i) * 16 + (lane >> 4) * 4;
+      const int n = (fb * (C::BN / 16) + cg * NWT + i) * 16 + (lane >> 4) * 4;
 #pragma unroll
       for (int j = 0; j < MW; ++j) {
         const int r = rh * 128 + j * 16 + (lane & 15);
@@ -752,8 +803,10 @@ __global__ __launch_bounds__(RG_THREADS, 1) void k_rowgemm(GemmArgs a, LmArgs lm
       }
     }
   } else {
+    float* u2s = extra;
+    if (tid < nrows) u2s[tid] = row_u2_seeded(row0 + tid, seed, lm);  // read after the next barrier
     // logits of 128 rows x 256 ids through LDS (one row half at a time), then
-    // one wave per row for the sampler statistics
+    // four rows per wave for the sampler statistics
     float* zt = reinterpret_cast<float*>(smem);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -854,9 +907,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_simple(GemmArgs a) {
     const int arow = a.row_map ? a.row_map[orow] : orow;
     const float* x = reinterpret_cast<const float*>(a.act) + (int64_t)arow * a.act_ld;
     const float* xs = a.act_scale ? a.act_scale + (int64_t)arow * a.scale_ld : nullptr;
+    const int64_t xs_t = a.scale_tile_ld;
     float g0 = 0.f, g1 = 0.f, u0 = 0.f, u1 = 0.f;
     for (int k = kb; k < ke; ++k) {
-      const float xv = xs ? x[k] * xs[k >> 8] : x[k];
+      const float xv = xs ? x[k] * xs[(int64_t)(k >> 8) * xs_t] : x[k];
       g0 = fmaf(xv, w0[(int64_t)n * ldw + koff + k], g0);
       g1 = fmaf(xv, w0[(int64_t)(n + 1) * ldw + koff + k], g1);
       if (w1) {
@@ -962,20 +1016,24 @@ int launch_lm_partials_from_logits(const float* logits, int rows, const LmArgs& 
 
 int launch_rowgemm(const GemmArgs& a0, const LmArgs* lm, hipStream_t s) {
   GemmArgs a = a0;
-  if (a.tiles || a.row_map || a.w1 || a.act_kind != ACT_BF16 || a.M < 1 || a.N % 16 || a.K % RG_KC ||
-      a.k_split % RG_KC || a.act_ld % 8)
+  const bool scaled = a.act_kind == ACT_BF16_SCALED;
+  const int bn = scaled ? RgCfg<false, true>::BN : RgCfg<false, false>::BN;
+  if (a.tiles || a.row_map || a.w1 || (a.act_kind != ACT_BF16 && !scaled) || a.M < 1 || a.N % 16 ||
+      a.K % RG_KC || a.k_split % RG_KC || a.act_ld % 8)
     return -1;
   if (!lm && (a.epi != EPI_STORE_F32 || !a.out_f32 || a.ldo % 4)) return -1;
-  if (lm && a.N % 256) return -1;
-  if (a.n_fb != (a.N + 255) / 256 || a.n_split < 1 || (int64_t)a.n_split * a.k_split < a.K) return -1;
+  if (lm && (scaled || a.N % 256)) return -1;
+  if (scaled && (a.K % 256 || a.k_split % 256 || !a.act_scale)) return -1;
+  if (a.n_fb != (a.N + bn - 1) / bn || a.n_split < 1 || (int64_t)a.n_split * a.k_split < a.K) return -1;
   a.max_tiles = (a.M + RG_ROWS - 1) / RG_ROWS;
   a.nblocks = round8(a.max_tiles * a.n_fb * a.n_split);
   LmArgs l;
   if (lm) l = *lm;
   else memset(&l, 0, sizeof(l));
   const dim3 grid(a.nblocks), block(RG_THREADS);
-  if (lm) hipLaunchKernelGGL((k_rowgemm<true>), grid, block, 0, s, a, l);
-  else hipLaunchKernelGGL((k_rowgemm<false>), grid, block, 0, s, a, l);
+  if (lm) hipLaunchKernelGGL((k_rowgemm<true, false>), grid, block, 0, s, a, l);
+  else if (scaled) hipLaunchKernelGGL((k_rowgemm<false, true>), grid, block, 0, s, a, l);
+  else hipLaunchKernelGGL((k_rowgemm<false, false>), grid, block, 0, s, a, l);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

@@ -48,9 +48,9 @@ __device__ __forceinline__ float block_scan256(float v, float* tmp, float& total
   return base + incl;
 }
 
-__global__ __launch_bounds__(256) void k_row_merge(const float4* part_f, const int2* part_i, int n_vt, int C,
-                                                  const uint64_t* seeds, int step, int block, float* H, int32_t* sample,
-                                                  int32_t* argmax, float* p_scale) {
+__global__ __launch_bounds__(256) void k_row_merge(const float4* part_f, const int2* part_i, int n_vt, int rows,
+                                                  int C, const uint64_t* seeds, int step, int block, float* H,
+                                                  int32_t* sample, int32_t* argmax, float* p_scale) {
   __shared__ float tmp[4];
   __shared__ float red[4];
   __shared__ int ired[4];
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256) void k_row_merge(const float4* part_f, const i
   }
   if (p_scale) {
     const float invS = 1.0f / S;
-    for (int k = k0; k < k1; ++k) p_scale[row * n_vt + k] = expf(pf[k].x - M) * invS;
+    for (int k = k0; k < k1; ++k) p_scale[(int64_t)k * rows + row] = expf(pf[k].x - M) * invS;  // tile-major
   }
   (void)ired;
 }
@@ -229,8 +229,8 @@ __global__ __launch_bounds__(1024) void k_select(SelArgs a) {
 
 int launch_row_merge(const float4* part_f, const int2* part_i, int n_vt, int rows, int C, const uint64_t* seeds,
                      int step, int block, float* H, int32_t* sample, int32_t* argmax, float* p_scale, hipStream_t s) {
-  hipLaunchKernelGGL(k_row_merge, dim3(rows), dim3(256), 0, s, part_f, part_i, n_vt, C, seeds, step, block, H, sample,
-                     argmax, p_scale);
+  hipLaunchKernelGGL(k_row_merge, dim3(rows), dim3(256), 0, s, part_f, part_i, n_vt, rows, C, seeds, step, block, H,
+                     sample, argmax, p_scale);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

@@ -115,11 +115,12 @@ typedef struct dg_kv_cache {
  *   seeds        [B]     sampler seed per canvas (Philox4x32-10 key)
  *   sc_probs     [B*C][vocab] fp32, optional external self-conditioning input
  *                (normalised probabilities); used whenever non-NULL
- *   p_side       [B*C][vocab] model dtype, and p_scale [B*C][vocab/256] fp32:
- *                the step's tempered distribution as exp(a - m_k) and per-tile
- *                factor exp(m_k - m)/S, written by every step and read by the
- *                next one (t >= 1) as its self-conditioning input.  NULL: no
- *                self-conditioning carried between steps.
+ *   p_side       [B*C][vocab] model dtype, and p_scale [vocab/256][B*C] fp32
+ *                (tile-major): the step's tempered distribution as
+ *                exp(a - m_k) and per-tile factor exp(m_k - m)/S, written by
+ *                every step and read by the next one (t >= 1) as its
+ *                self-conditioning input.  NULL: no self-conditioning carried
+ *                between steps.
  *   entropy [B*C] fp32, sample/argmax/prev_argmax [B*C] int32, accepted [B*C]
  *   uint8, n_accepted/stop [B] int32, mean_entropy [B] fp32, flags [B] uint32.
  *   prev_argmax holds the previous step's argmax (read by the stop test at
