@@ -71,7 +71,7 @@ struct Plan {
   int T;        // tokens per pass
   int Tdn;      // denoise tokens
   int att_rows; // attention partial rows (split x tokens)
-  size_t x, n, q, ckv_k, ckv_v, o, att_o, att_ml, o_part, r_part, ids, wts, row_token, inv, offsets, tiles,
+  size_t x, n, q, o, att_o, att_ml, o_part, r_part, ids, wts, row_token, inv, offsets, tiles,
       n_tiles, h, Y, lm_f, lm_i, logits, e_part, ebar, hsc, g_part, total;
 };
 
@@ -88,8 +88,6 @@ Plan make_plan(const Shape& s, int batch, int max_canvas) {
   p.x = take(T * s.d * 4);
   p.n = take(T * s.d * s.act);
   p.q = take(T * s.qdim * s.act);
-  p.ckv_k = take(Tdn * s.kvdim * s.act);
-  p.ckv_v = take(Tdn * s.kvdim * s.act);
   p.o = take(T * s.qdim * s.act);
   p.att_o = take((size_t)p.att_rows * s.nq * s.dh * 4);
   p.att_ml = take((size_t)p.att_rows * s.nq * 8);
@@ -246,7 +244,6 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
   const bool bf = s.dt == DG_DTYPE_BF16;
   const int64_t layer_elems = (int64_t)cache->batch * s.nkv * cache->capacity * s.dh;
   const int64_t c_seq = (int64_t)s.nkv * cache->capacity * s.dh, c_head = (int64_t)cache->capacity * s.dh;
-  const int64_t w_seq = (int64_t)s.nkv * seq_len * s.dh, w_head = (int64_t)seq_len * s.dh;
   void* xn = c.at<void>(c.p.n);
   for (int l = 0; l < s.L; ++l) {
     const dg_layer_weights& lw = c.w->layers[l];
@@ -262,14 +259,10 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
       QkvEpi& q = a.qkv;
       q.q = c.at<void>(c.p.q);
       q.q_dim = s.qdim; q.kv_dim = s.kvdim; q.d_head = s.dh; q.n_kv = s.nkv;
-      if (causal) {
-        q.k = kc; q.v = vc; q.kv_b_stride = c_seq; q.kv_h_stride = c_head; q.kv_row0 = L;
-        q.v_pitch = cache->capacity;
-      } else {
-        q.k = c.at<void>(c.p.ckv_k); q.v = c.at<void>(c.p.ckv_v);
-        q.kv_b_stride = w_seq; q.kv_h_stride = w_head; q.kv_row0 = 0;
-        q.v_pitch = seq_len;
-      }
+      // k, v of these tokens go to cache rows [L, L + seq_len): appended by the
+      // encoder; scratch rows for the denoiser, which leaves the length as is
+      q.k = kc; q.v = vc; q.kv_b_stride = c_seq; q.kv_h_stride = c_head; q.kv_row0 = L;
+      q.v_pitch = cache->capacity;
       q.seq_len = seq_len; q.pos0 = L; q.rope_base = s.rope_base;
       DG_TRY(dense_gemm(c, a, T, s.qkv, s.d, 1));
     }
@@ -281,20 +274,13 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
       if (bf) {
         const int G = s.nq / s.nkv;
         const int base_blocks = n_seq * s.nkv * ((seq_len + 128 / G - 1) / (128 / G));
-        split = std::max(1, (256 + base_blocks - 1) / base_blocks);         // ~1 workgroup (8 waves) per CU
+        split = std::max(1, (256 + base_blocks - 1) / base_blocks);         // ~1 workgroup (4 waves) per CU
         split = std::min(split, std::max(1, (n_keys + 255) / 256));         // >= 4 key tiles per split
         split = std::min(split, std::min(kMaxSplit, std::max(1, c.p.att_rows / T)));
       }
-      if (causal) {
-        DG_TRY(launch_attention(bf, c.at<void>(c.p.q), s.qdim, kc, vc, c_seq, c_head, cache->capacity, L + seq_len,
-                                nullptr, nullptr, 0, 0, 1, 0, L, 1, seq_len, n_seq, s.nq, s.nkv, s.dh, split,
-                                c.at<float>(c.p.att_o), c.at<float2>(c.p.att_ml), c.at<void>(c.p.o), c.st));
-      } else {
-        DG_TRY(launch_attention(bf, c.at<void>(c.p.q), s.qdim, kc, vc, c_seq, c_head, cache->capacity, L,
-                                c.at<void>(c.p.ckv_k), c.at<void>(c.p.ckv_v), w_seq, w_head, seq_len, seq_len, L, 0,
-                                seq_len, n_seq, s.nq, s.nkv, s.dh, split, c.at<float>(c.p.att_o),
-                                c.at<float2>(c.p.att_ml), c.at<void>(c.p.o), c.st));
-      }
+      DG_TRY(launch_attention(bf, c.at<void>(c.p.q), s.qdim, kc, vc, c_seq, c_head, cache->capacity, n_keys, L,
+                              causal ? 1 : 0, seq_len, n_seq, s.nq, s.nkv, s.dh, split, c.at<float>(c.p.att_o),
+                              c.at<float2>(c.p.att_ml), c.at<void>(c.p.o), c.st));
     }
     // O projection (split-K partials), residual, RMSNorm
     {
@@ -398,7 +384,15 @@ int check_weights(const dg_model_config* cfg, const dg_weights* w) {
 int check_cache(const dg_model_config* cfg, const dg_kv_cache* c, int batch) {
   if (!c || !c->k || !c->v || c->batch != batch || c->capacity < 1 || c->length < 0 || c->length > c->capacity)
     return DG_ERR_INVALID_ARG;
-  (void)cfg;
+  // bf16 models: V^T rows are read in 16-byte runs of 8 keys
+  if (cfg->dtype == DG_DTYPE_BF16 && c->capacity % 8) return DG_ERR_UNSUPPORTED;
+  return DG_OK;
+}
+
+// The denoiser writes its canvas K/V into rows [length, length + canvas).
+int check_denoise_cache(const dg_model_config* cfg, const dg_kv_cache* c, const dg_canvas* cv) {
+  DG_TRY(check_cache(cfg, c, cv->batch));
+  if ((int64_t)c->length + cv->canvas > c->capacity) return DG_ERR_KV_CAPACITY;
   return DG_OK;
 }
 
@@ -649,7 +643,7 @@ int dg_denoise_step_traced(const dg_model_config* cfg, const dg_weights* w, cons
   DG_TRY(check_weights(cfg, w));
   DG_TRY(check_canvas(cv, true));
   DG_TRY(check_step(p));
-  DG_TRY(check_cache(cfg, cache, cv->batch));
+  DG_TRY(check_denoise_cache(cfg, cache, cv));
   Ctx c;
   c.s = shape_of(cfg);
   c.p = make_plan(c.s, cv->batch, cv->canvas);
@@ -750,7 +744,7 @@ int dg_test_forward_logits(const dg_model_config* cfg, const dg_weights* w, cons
   DG_TRY(check_weights(cfg, w));
   DG_TRY(check_canvas(cv, false));
   DG_TRY(check_step(p));
-  DG_TRY(check_cache(cfg, cache, cv->batch));
+  DG_TRY(check_denoise_cache(cfg, cache, cv));
   if (!d_logits) return DG_ERR_INVALID_ARG;
   Ctx c;
   c.s = shape_of(cfg);

@@ -35,7 +35,7 @@ struct QkvEpi {
   int64_t kv_b_stride;  // elements between sequences of the k/v store
   int64_t kv_h_stride;  // elements between kv heads (= capacity * d_head)
   int32_t kv_row0;      // first row written inside each head (cache length for append)
-  int32_t v_pitch;      // row pitch of the transposed V store ([d_head][rows] per head)
+  int32_t v_pitch;      // row pitch of the transposed V store ([d_head][rows] per head; fp16 for bf16 models)
   int32_t seq_len;      // tokens per sequence in this call
   int32_t pos0;         // absolute position of the first token of each sequence
   float rope_base;
@@ -118,9 +118,8 @@ int route_max_tokens();
 int launch_route_sort(const int32_t* ids, int T, int k, int E, int n_sh, int bm, int32_t* row_token, int32_t* inv,
                       int32_t* offsets, GemmTile* tiles, int32_t* n_tiles, hipStream_t s);
 // k_attn.hip
-int launch_attention(int dtype, const void* q, int64_t q_ld, const void* k0, const void* v0, int64_t s0_seq,
-                     int64_t s0_head, int vp0, int len0, const void* k1, const void* v1, int64_t s1_seq,
-                     int64_t s1_head, int vp1, int len1, int n_prefix, int causal, int seq_len, int n_seq, int n_q,
+int launch_attention(int dtype, const void* q, int64_t q_ld, const void* k, const void* v, int64_t s_seq,
+                     int64_t s_head, int vp, int n_keys, int n_prefix, int causal, int seq_len, int n_seq, int n_q,
                      int n_kv, int d, int n_split, float* part_o, float2* part_ml, void* out, hipStream_t s);
 // k_misc.hip
 int launch_embed_norm(int dtype, const int32_t* tok, const void* emb, const float* add, int n_add, int64_t add_stride,

@@ -1,26 +1,30 @@
-// Canvas attention: every query of a sequence's canvas attends to the joint
-// key list [cached prefix ; canvas].  All prefix keys are visible; canvas key
-// j is visible to canvas query i always (denoising) or only when j <= i
-// (causal encode).  Grouped-query attention: query head h reads KV head
-// h / (n_q / n_kv).  Scale 1/sqrt(d_head).
+// Canvas attention: every query of a sequence's canvas attends to the keys
+// [0, n_keys) of its store: the cached prefix followed by the canvas rows
+// (the denoiser writes the canvas K/V into the cache rows past the cache
+// length, which it does not advance; the causal encode appends there).  All
+// prefix keys are visible; canvas key j is visible to canvas query i always
+// (denoising) or only when j <= i (causal encode).  Grouped-query attention:
+// query head h reads KV head h / (n_q / n_kv).  Scale 1/sqrt(d_head).
 //
-// Keys come from up to two stores: src0 holds keys [0, len0), src1 holds keys
-// [len0, len0 + len1) (the denoiser's transient canvas K/V).  K is stored
-// [seq][kv_head][row][d_head]; V is stored transposed, [seq][kv_head][d_head][row]
-// with a row pitch per store, so that the V^T operand streams as contiguous
-// key runs.  In causal mode the canvas keys are the last n keys of src0
-// (written there by the QKV epilogue before attention runs).
+// K is stored [seq][kv_head][row][d_head]; V is stored transposed,
+// [seq][kv_head][d_head][row] with row pitch vp, so that the V^T operand
+// streams as contiguous key runs.  bf16 models keep K in bf16 and V^T in fp16
+// (every bf16 value of magnitude >= 2^-17 is exact in fp16; V is rounded to
+// bf16 first).
 //
-// bf16 path (d_head = 256): one workgroup of 8 waves = one KV head, 128
-// query rows (the G query heads sharing that KV head x 128/G queries), one
-// KV split.  Tiles of 64 keys are staged in double-buffered LDS (K as rows,
-// V^T as rows of 64 keys converted to fp16; the next tile's loads are in
-// flight during this tile's MFMAs), and each wave computes S^T = K Q^T (keys down, queries across)
-// with v_mfma_f32_16x16x32_bf16, so the exponentiated scores already sit in
-// the B-operand layout of O^T = V^T P^T (v_mfma_f32_16x16x32_f16 with P split
-// into two fp16 parts, so the product keeps fp32 accuracy; V's bf16 values
-// convert to fp16 exactly).  Online softmax in the exp2 domain.  Splits write (m, l, O) partials merged in
-// split order.
+// bf16 path (d_head = 256): one workgroup of 8 waves (two per SIMD) = one KV
+// head, 128 query rows (the G query heads sharing that KV head x 128/G
+// queries), one KV split; each wave owns 16 query rows.  Tiles of 64
+// keys move straight from memory into a double-buffered LDS stage with
+// global_load_lds_dwordx4 (K: 512 B per key row, 16-byte column groups
+// XOR-swizzled; V^T: 128 B per dimension row, likewise swizzled), one tile
+// ahead of the MFMAs.  S^T = K Q^T comes from v_mfma_f32_16x16x32_bf16 with
+// the key rows of each 16-row MFMA chosen so that every lane ends up with 8
+// consecutive keys per 32-key step: the exponentiated scores are directly
+// the B operand of O^T = V^T P^T (v_mfma_f32_16x16x32_f16, P split into two
+// fp16 parts so the product keeps fp32 accuracy), and the V^T operand is one
+// 16-byte read.  Online softmax in the exp2 domain.  Splits write (m, l, O)
+// partials merged in split order.
 #include "dg_internal.h"
 
 namespace {
@@ -28,59 +32,51 @@ namespace {
 struct AttnArgs {
   const void* q;  // [T][n_q * d]
   int64_t q_ld;
-  const void* k0;
-  const void* v0;
-  const void* k1;
-  const void* v1;
-  int64_t s0_seq, s0_head;  // element strides of src0 (seq, head); K row stride = d
-  int64_t s1_seq, s1_head;
-  int32_t vp0, vp1;         // row pitch of the transposed V stores
-  int32_t len0, len1;
-  int32_t n_prefix;   // keys before the canvas (causal boundary)
+  const void* k;  // key store: K [seq][kv_head][row][d], V^T [seq][kv_head][d][row] (pitch vp)
+  const void* v;
+  int64_t s_seq, s_head;  // element strides of the store (seq, head)
+  int32_t vp;             // row pitch of the transposed V store
+  int32_t n_keys;         // keys [0, n_keys) per sequence
+  int32_t n_prefix;       // keys before the canvas (causal boundary)
   int32_t causal;
-  int32_t seq_len;    // queries per sequence
+  int32_t seq_len;        // queries per sequence
   int32_t n_seq, n_q, n_kv, d;
   int32_t n_split, keys_per_split;
-  float scale_log2;   // log2(e) / sqrt(d)
-  float* part_o;      // [split][T][n_q][d] unnormalised
-  float2* part_ml;    // [split][T][n_q] (m in log2 units, l)
-  void* out;          // [T][n_q * d]
+  float scale_log2;       // log2(e) / sqrt(d)
+  float* part_o;          // [split][T][n_q][d] unnormalised
+  float2* part_ml;        // [split][T][n_q] (m in log2 units, l)
+  void* out;              // [T][n_q * d]
 };
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ uint32_t f16x2_bits(float a, float b) {
-  const _Float16 ha = (_Float16)a, hb = (_Float16)b;
-  return (uint32_t)(*reinterpret_cast<const uint16_t*>(&ha)) | ((uint32_t)(*reinterpret_cast<const uint16_t*>(&hb)) << 16);
-}
-
-// 8 bf16 -> 8 fp16 (exact for bf16 values inside fp16's normal range)
-__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 v) {
-  uint4 r;
-  r.x = f16x2_bits(bf2f((bf16_t)(v.x & 0xFFFF)), bf2f((bf16_t)(v.x >> 16)));
-  r.y = f16x2_bits(bf2f((bf16_t)(v.y & 0xFFFF)), bf2f((bf16_t)(v.y >> 16)));
-  r.z = f16x2_bits(bf2f((bf16_t)(v.z & 0xFFFF)), bf2f((bf16_t)(v.z >> 16)));
-  r.w = f16x2_bits(bf2f((bf16_t)(v.w & 0xFFFF)), bf2f((bf16_t)(v.w >> 16)));
-  return r;
-}
-
 constexpr int ATT_D = 256;
-constexpr int ATT_KT = 64;
+constexpr int ATT_KT = 64;                  // keys per tile
 constexpr int ATT_WAVES = 8;
 constexpr int ATT_THREADS = ATT_WAVES * 64;
-constexpr int ATT_ROWS = ATT_WAVES * 16;           // query rows per workgroup
-constexpr int KS_LD = ATT_D + 8;                   // bf16 pitch of a K row in LDS
-constexpr int VT_LD = ATT_KT + 8;                  // fp16 pitch of a V^T row in LDS
-constexpr int KS_ELEMS = ATT_KT * KS_LD;
-constexpr int VT_ELEMS = ATT_D * VT_LD;
-constexpr int ATT_VPT = ATT_KT * ATT_D / 8 / ATT_THREADS;  // 16-byte vectors per thread per tensor
+constexpr int ATT_QT = 1;                   // 16-query MFMA tiles per wave
+constexpr int ATT_QW = 16 * ATT_QT;         // query rows per wave
+constexpr int ATT_ROWS = ATT_WAVES * ATT_QW; // query rows per workgroup
+constexpr int ATT_K_BYTES = ATT_KT * ATT_D * 2;   // 32 KiB
+constexpr int ATT_V_BYTES = ATT_D * ATT_KT * 2;   // 32 KiB
+constexpr int ATT_STAGE = ATT_K_BYTES + ATT_V_BYTES;
+constexpr int ATT_DMA = (ATT_STAGE / 1024) / ATT_WAVES;  // 1 KiB instructions per wave per tile
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// K tile: key row r at r * 512 B; 16-byte group c (dims 8c..8c+7) at physical
+// group c ^ fk(r).  fk separates the 8 rows any 8 lanes read together.
+__device__ __forceinline__ int att_fk(int r) { return (r & 3) | (((r >> 3) & 1) << 2); }
+// S^T MFMA (step kk, half hf): row i <-> key 32 kk + 8 (i / 4) + 4 hf + i % 4,
+// so lane group g of the output holds keys 32 kk + 8 g + 4 hf + e.
+__device__ __forceinline__ int att_krow(int kk, int hf, int i) { return 32 * kk + 8 * (i >> 2) + 4 * hf + (i & 3); }
 
 __global__ __launch_bounds__(ATT_THREADS, 1) void k_attn_mfma(AttnArgs a) {
-  // two buffers of (K tile, V^T tile): the next tile is loaded while this one is used
-  __shared__ __attribute__((aligned(16))) uint16_t sm[2 * (KS_ELEMS + VT_ELEMS)];
+  static_assert(ATT_ROWS == 128, "workgroup covers 128 query rows");
+  __shared__ __attribute__((aligned(1024))) unsigned char sm[2 * ATT_STAGE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = a.n_q / a.n_kv;
-  const int qpb = ATT_ROWS / G;  // queries per block
+  const int qpb = ATT_ROWS / G;  // queries per head in a workgroup
   const int nqb = DG_CEIL_DIV(a.seq_len, qpb);
   int bid = blockIdx.x;
   const int sp = bid % a.n_split;
@@ -91,193 +87,204 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void k_attn_mfma(AttnArgs a) {
   const int seq = bid / a.n_kv;
   if (seq >= a.n_seq) return;
 
-  const int row0 = wave * 16;            // this wave's 16 rows inside the block
-  const int hq = hk * G + row0 / qpb;    // query head
-  const int qi0 = qb * qpb + row0 % qpb; // first query index in the sequence
-  const int my_q = qi0 + (lane & 15);
-  const bool qvalid = my_q < a.seq_len;
-  const int64_t tok = (int64_t)seq * a.seq_len + (qvalid ? my_q : 0);
+  const int row0 = wave * ATT_QW;              // this wave's 32 rows inside the workgroup
+  const int hq = hk * G + row0 / qpb;          // query head (qpb is a multiple of 32)
+  const int qi0 = qb * qpb + row0 % qpb;       // first query index of the wave
+  const int g = lane >> 4, c16 = lane & 15;
+  int my_q[ATT_QT];
+  bool qvalid[ATT_QT];
+  int64_t tok[ATT_QT];
+#pragma unroll
+  for (int qt = 0; qt < ATT_QT; ++qt) {
+    my_q[qt] = qi0 + qt * 16 + c16;
+    qvalid[qt] = my_q[qt] < a.seq_len;
+    tok[qt] = (int64_t)seq * a.seq_len + (qvalid[qt] ? my_q[qt] : 0);
+  }
 
-  // Q fragments (B operand of S^T = K Q^T): lane holds q[my_q][32s + 8g .. +8]
-  bf16x8_t qf[ATT_D / 32];
-  {
-    const bf16_t* qp = reinterpret_cast<const bf16_t*>(a.q) + tok * a.q_ld + (int64_t)hq * ATT_D + (lane >> 4) * 8;
+  // Q fragments (B operand of S^T = K Q^T): q[query][32 s + 8 g .. +8]
+  bf16x8_t qf[ATT_QT][ATT_D / 32];
+#pragma unroll
+  for (int qt = 0; qt < ATT_QT; ++qt) {
+    const bf16_t* qp = reinterpret_cast<const bf16_t*>(a.q) + tok[qt] * a.q_ld + (int64_t)hq * ATT_D + g * 8;
 #pragma unroll
     for (int s = 0; s < ATT_D / 32; ++s) {
-      uint4 v = qvalid ? *reinterpret_cast<const uint4*>(qp + s * 32) : make_uint4(0, 0, 0, 0);
-      qf[s] = *reinterpret_cast<bf16x8_t*>(&v);
+      uint4 v = qvalid[qt] ? *reinterpret_cast<const uint4*>(qp + s * 32) : make_uint4(0, 0, 0, 0);
+      qf[qt][s] = *reinterpret_cast<bf16x8_t*>(&v);
     }
   }
 
-  f32x4_t o[ATT_D / 16];
+  f32x4_t o[ATT_QT][ATT_D / 16];
+  float m_run[ATT_QT], l_run[ATT_QT];
 #pragma unroll
-  for (int t = 0; t < ATT_D / 16; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int qt = 0; qt < ATT_QT; ++qt) {
+#pragma unroll
+    for (int t = 0; t < ATT_D / 16; ++t) o[qt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m_run[qt] = -INFINITY;
+    l_run[qt] = 0.f;
+  }
 
-  const int n_keys = a.len0 + a.len1;
   const int kb = sp * a.keys_per_split;
-  int ke = min(n_keys, kb + a.keys_per_split);
+  int ke = min(a.n_keys, kb + a.keys_per_split);
   if (a.causal) ke = min(ke, a.n_prefix + min(a.seq_len, qb * qpb + qpb));  // later keys are masked for all
-  const int g4 = (lane >> 4) * 4;
+  const int ntiles = ke > kb ? DG_CEIL_DIV(ke - kb, ATT_KT) : 0;
 
-  const bf16_t* kbase0 = reinterpret_cast<const bf16_t*>(a.k0) + (int64_t)seq * a.s0_seq + (int64_t)hk * a.s0_head;
-  const bf16_t* vbase0 = reinterpret_cast<const bf16_t*>(a.v0) + (int64_t)seq * a.s0_seq + (int64_t)hk * a.s0_head;
-  const bf16_t* kbase1 = reinterpret_cast<const bf16_t*>(a.k1) + (int64_t)seq * a.s1_seq + (int64_t)hk * a.s1_head;
-  const bf16_t* vbase1 = reinterpret_cast<const bf16_t*>(a.v1) + (int64_t)seq * a.s1_seq + (int64_t)hk * a.s1_head;
+  const bf16_t* kbase = reinterpret_cast<const bf16_t*>(a.k) + (int64_t)seq * a.s_seq + (int64_t)hk * a.s_head;
+  const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v) + (int64_t)seq * a.s_seq + (int64_t)hk * a.s_head;
 
-  uint4 kreg[ATT_VPT], vreg[ATT_VPT];
-  // K: vector v -> key row v / 32, dims (v % 32) * 8;  V^T: vector v -> dim v / 8, keys (v % 8) * 8
-  auto load_tile = [&](int k0) {
+  // tile i (clamped to the last one) into stage i & 1.  Instruction n of the
+  // workgroup: n < 32 -> K rows 2n, 2n + 1; else V^T rows 8 (n - 32) .. +7.
+  // Keys past the store's end load the last key (masked below).
+  auto issue = [&](int i) {
+    const int ic = min(i, ntiles - 1);
+    const int k0 = kb + ic * ATT_KT;
+    unsigned char* st = sm + (i & 1) * ATT_STAGE;
+    static_assert(ATT_DMA * ATT_WAVES == 64, "32 K and 32 V^T instructions per tile");
+    static_assert(ATT_QW % 16 == 0 && (ATT_ROWS / 4) % ATT_QW == 0, "a wave's rows stay in one head");
+    if (wave < ATT_WAVES / 2) {  // K
 #pragma unroll
-    for (int it = 0; it < ATT_VPT; ++it) {
-      const int v = tid + it * ATT_THREADS;
-      {
-        const int j = k0 + (v >> 5), c8 = (v & 31) * 8;
-        uint4 x = make_uint4(0, 0, 0, 0);
-        if (j < ke) {
-          const bf16_t* kp = j < a.len0 ? kbase0 + (int64_t)j * ATT_D + c8 : kbase1 + (int64_t)(j - a.len0) * ATT_D + c8;
-          x = *reinterpret_cast<const uint4*>(kp);
-        }
-        kreg[it] = x;
+      for (int u = 0; u < ATT_DMA; ++u) {
+        const int n = wave * ATT_DMA + u;
+        const int r = 2 * n + (lane >> 5);
+        const int c = (lane & 31) ^ att_fk(r);
+        const int j = min(k0 + r, a.n_keys - 1);
+        __builtin_amdgcn_global_load_lds(kbase + (int64_t)j * ATT_D + c * 8, (lds_void_t*)(st + n * 1024), 16, 0, 0);
       }
-      {
-        const int dd = v >> 3, j0 = k0 + (v & 7) * 8;
-        const bool full = j0 + 8 <= ke;
-        const bool in0 = j0 + 8 <= a.len0, in1 = j0 >= a.len0;
-        uint4 x = make_uint4(0, 0, 0, 0);
-        if (full && in0 && ((j0 | a.vp0) & 7) == 0) {
-          x = *reinterpret_cast<const uint4*>(vbase0 + (int64_t)dd * a.vp0 + j0);
-        } else if (full && in1 && (((j0 - a.len0) | a.vp1) & 7) == 0) {
-          x = *reinterpret_cast<const uint4*>(vbase1 + (int64_t)dd * a.vp1 + (j0 - a.len0));
-        } else if (j0 < ke) {
-          // tile edge or a store boundary inside these 8 keys: element by element
-          uint32_t w[4] = {0, 0, 0, 0};
-#pragma nounroll
-          for (int e = 0; e < 8; ++e) {
-            const int j = j0 + e;
-            if (j < ke) {
-              const uint32_t b = j < a.len0 ? vbase0[(int64_t)dd * a.vp0 + j] : vbase1[(int64_t)dd * a.vp1 + (j - a.len0)];
-              w[e >> 1] |= b << ((e & 1) * 16);
-            }
-          }
-          x = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-        vreg[it] = x;
+    } else {
+#pragma unroll
+      for (int u = 0; u < ATT_DMA; ++u) {
+        const int n = wave * ATT_DMA + u;
+        const int dd = 8 * (n - 32) + (lane >> 3);
+        const int c = (lane & 7) ^ (dd & 7);
+        const int j = min(k0 + 8 * c, ((a.n_keys - 1) & ~7));
+        __builtin_amdgcn_global_load_lds(vbase + (int64_t)dd * a.vp + j, (lds_void_t*)(st + n * 1024), 16, 0, 0);
       }
     }
   };
-  auto store_tile = [&](int buf) {
-    uint16_t* ks = sm + buf * (KS_ELEMS + VT_ELEMS);
-    uint16_t* vt = ks + KS_ELEMS;
-#pragma unroll
-    for (int it = 0; it < ATT_VPT; ++it) {
-      const int v = tid + it * ATT_THREADS;
-      *reinterpret_cast<uint4*>(ks + (v >> 5) * KS_LD + (v & 31) * 8) = kreg[it];
-      *reinterpret_cast<uint4*>(vt + (v >> 3) * VT_LD + (v & 7) * 8) = bf16x8_to_f16x8(vreg[it]);
-    }
-  };
 
-  if (kb < ke) {
-    load_tile(kb);
-    store_tile(0);
-  }
-  __syncthreads();
-  int buf = 0;
-  for (int k0 = kb; k0 < ke; k0 += ATT_KT, buf ^= 1) {
-    const bool more = k0 + ATT_KT < ke;
-    if (more) load_tile(k0 + ATT_KT);  // in flight during this tile's MFMAs
-    const uint16_t* ks = sm + buf * (KS_ELEMS + VT_ELEMS);
-    const uint16_t* vt = ks + KS_ELEMS;
-    // S^T for four 16-key quarters: lane holds keys 16h + 4g + e, query l%16
-    f32x4_t st[4];
+  if (ntiles > 0) issue(0);
+  for (int i = 0; i < ntiles; ++i) {
+    // tile i's loads are the only ones in flight: wait, then a plain barrier
+    // (every wave's part is in LDS; every wave is done with tile i - 1, whose
+    // stage the next issue refills).  The asm memory clobber keeps LDS
+    // accesses on their side.
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (i + 1 < ntiles) issue(i + 1);
+    const unsigned char* ks = sm + (i & 1) * ATT_STAGE;
+    const unsigned char* vs = ks + ATT_K_BYTES;
+    const int k0 = kb + i * ATT_KT;
+    if (ke - k0 < ATT_KT) {
+      // last, partial tile: its masked keys (P = 0) may sit in rows never
+      // written (up to 7 past the store's last row); zero their V^T entries
+      // so that 0 * V cannot meet a non-finite value
+      const int kv = ke - k0;
+      unsigned char* vw = sm + (i & 1) * ATT_STAGE + ATT_K_BYTES;
+      for (int e = tid; e < ATT_D * ATT_KT; e += ATT_THREADS) {
+        const int dd = e >> 6, kk = e & 63;
+        if (kk >= kv)
+          *reinterpret_cast<uint16_t*>(vw + dd * 128 + ((((kk >> 3) ^ (dd & 7)) << 4) | ((kk & 7) << 1))) = 0;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    // S^T for the four (kk, half) 16-key groups and both query tiles
+    f32x4_t st[ATT_QT][4];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      st[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int x = 0; x < 4; ++x) {
+#pragma unroll
+      for (int qt = 0; qt < ATT_QT; ++qt) st[qt][x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const int r = att_krow(x >> 1, x & 1, c16);
 #pragma unroll
       for (int s = 0; s < ATT_D / 32; ++s) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(ks + (h * 16 + (lane & 15)) * KS_LD + s * 32 + (lane >> 4) * 8);
-        st[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], st[h], 0, 0, 0);
+        const bf16x8_t kf =
+            *reinterpret_cast<const bf16x8_t*>(ks + r * 512 + (((s * 4 + g) ^ att_fk(r)) << 4));
+#pragma unroll
+        for (int qt = 0; qt < ATT_QT; ++qt)
+          st[qt][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qt][s], st[qt][x], 0, 0, 0);
       }
     }
-    float sv[16];
-    float mt = -INFINITY;
+    // online softmax per query column; P^T operands: k index 8 g + e' <-> key 32 kk + 8 g + e'
+    f16x8_t pf[ATT_QT][2], pl[ATT_QT][2];
 #pragma unroll
-    for (int h = 0; h < 4; ++h)
+    for (int qt = 0; qt < ATT_QT; ++qt) {
+      float sv[16];
+      float mt = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = k0 + h * 16 + g4 + e;
-        bool vis = j < ke;
-        if (a.causal) vis = vis && (j <= a.n_prefix + my_q);
-        const float x = vis ? st[h][e] * a.scale_log2 : -INFINITY;
-        sv[h * 4 + e] = x;
-        mt = fmaxf(mt, x);
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = k0 + 32 * (x >> 1) + 8 * g + 4 * (x & 1) + e;
+          bool vis = j < ke;
+          if (a.causal) vis = vis && (j <= a.n_prefix + my_q[qt]);
+          const float xv = vis ? st[qt][x][e] * a.scale_log2 : -INFINITY;
+          sv[x * 4 + e] = xv;
+          mt = fmaxf(mt, xv);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float m_new = fmaxf(m_run[qt], mt);
+      const float shift = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = exp2f(m_run[qt] - shift);
+      m_run[qt] = m_new;
+      float ps = 0.f;
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = exp2f(sv[x * 4 + e] - shift);
+          ps += p;
+          const _Float16 hi = (_Float16)p;
+          const int kk = x >> 1, ep = 4 * (x & 1) + e;
+          pf[qt][kk][ep] = hi;
+          pl[qt][kk][ep] = (_Float16)(p - (float)hi);
+        }
+      l_run[qt] = l_run[qt] * alpha + ps;
+      // alpha == 1 leaves the accumulators as they are: skip the scaling when
+      // the running maximum held for every lane
+      if (__ballot(alpha != 1.f)) {
+#pragma unroll
+        for (int t = 0; t < ATT_D / 16; ++t) o[qt][t] *= alpha;
       }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float m_new = fmaxf(m_run, mt);
-    const float shift = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - shift);
-    m_run = m_new;
-    float ps = 0.f;
-    float pv[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      pv[e] = exp2f(sv[e] - shift);
-      ps += pv[e];
     }
-    l_run = l_run * alpha + ps;
-    // P^T operands for the two 32-key k-steps: k index (g, e) -> key
-    // 32kk + 4g + e (e < 4) or 32kk + 16 + 4g + (e - 4).  P = P_hi + P_lo in
-    // fp16 (relative error ~2^-22): P V is as accurate as an fp32 product.
-    f16x8_t pf[2], pl[2];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = pv[(2 * kk + (e >> 2)) * 4 + (e & 3)];
-        const _Float16 hi = (_Float16)x;
-        pf[kk][e] = hi;
-        pl[kk][e] = (_Float16)(x - (float)hi);
-      }
+    // O^T += V^T P^T: lane reads V^T[dim 16 t + c16][keys 32 kk + 8 g .. +8]
 #pragma unroll
     for (int t = 0; t < ATT_D / 16; ++t) {
-      o[t] *= alpha;
-      const uint16_t* vr = vt + (t * 16 + (lane & 15)) * VT_LD;
+      const int dd = t * 16 + c16;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const uint2 lo = *reinterpret_cast<const uint2*>(vr + kk * 32 + g4);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vr + kk * 32 + 16 + g4);
-        uint4 u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        const f16x8_t vf = *reinterpret_cast<f16x8_t*>(&u);
-        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[kk], o[t], 0, 0, 0);
-        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pl[kk], o[t], 0, 0, 0);
+        const f16x8_t vf = *reinterpret_cast<const f16x8_t*>(vs + dd * 128 + (((4 * kk + g) ^ (dd & 7)) << 4));
+#pragma unroll
+        for (int qt = 0; qt < ATT_QT; ++qt) {
+          o[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[qt][kk], o[qt][t], 0, 0, 0);
+          o[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pl[qt][kk], o[qt][t], 0, 0, 0);
+        }
       }
     }
-    if (more) store_tile(buf ^ 1);
-    __syncthreads();
   }
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
-  if (!qvalid) return;
-  // lane holds O^T[dh = 16t + 4g + e][query l%16]
-  if (a.n_split == 1) {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    bf16_t* op = reinterpret_cast<bf16_t*>(a.out) + tok * (int64_t)(a.n_q * ATT_D) + (int64_t)hq * ATT_D;
 #pragma unroll
-    for (int t = 0; t < ATT_D / 16; ++t) {
-      const int d0 = t * 16 + g4;
-      const uint32_t lo = (uint32_t)f2bf(o[t][0] * inv) | ((uint32_t)f2bf(o[t][1] * inv) << 16);
-      const uint32_t hi = (uint32_t)f2bf(o[t][2] * inv) | ((uint32_t)f2bf(o[t][3] * inv) << 16);
-      *reinterpret_cast<uint2*>(op + d0) = make_uint2(lo, hi);
+  for (int qt = 0; qt < ATT_QT; ++qt) {
+    float l = l_run[qt];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (!qvalid[qt]) continue;
+    // lane holds O^T[dh = 16t + 4g + e][query c16]
+    if (a.n_split == 1) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      bf16_t* op = reinterpret_cast<bf16_t*>(a.out) + tok[qt] * (int64_t)(a.n_q * ATT_D) + (int64_t)hq * ATT_D;
+#pragma unroll
+      for (int t = 0; t < ATT_D / 16; ++t) {
+        const int d0 = t * 16 + 4 * g;
+        const uint32_t lo = (uint32_t)f2bf(o[qt][t][0] * inv) | ((uint32_t)f2bf(o[qt][t][1] * inv) << 16);
+        const uint32_t hi = (uint32_t)f2bf(o[qt][t][2] * inv) | ((uint32_t)f2bf(o[qt][t][3] * inv) << 16);
+        *reinterpret_cast<uint2*>(op + d0) = make_uint2(lo, hi);
+      }
+    } else {
+      const int64_t T = (int64_t)a.n_seq * a.seq_len;
+      const int64_t prow = ((int64_t)sp * T + tok[qt]) * a.n_q + hq;
+      float* pp = a.part_o + prow * ATT_D;
+#pragma unroll
+      for (int t = 0; t < ATT_D / 16; ++t)
+        *reinterpret_cast<float4*>(pp + t * 16 + 4 * g) = make_float4(o[qt][t][0], o[qt][t][1], o[qt][t][2], o[qt][t][3]);
+      if (g == 0) a.part_ml[prow] = make_float2(m_run[qt], l);
     }
-  } else {
-    const int64_t T = (int64_t)a.n_seq * a.seq_len;
-    const int64_t prow = ((int64_t)sp * T + tok) * a.n_q + hq;
-    float* pp = a.part_o + prow * ATT_D;
-#pragma unroll
-    for (int t = 0; t < ATT_D / 16; ++t)
-      *reinterpret_cast<float4*>(pp + t * 16 + g4) = make_float4(o[t][0], o[t][1], o[t][2], o[t][3]);
-    if (lane < 16) a.part_ml[prow] = make_float2(m_run, l_run);
   }
 }
 
@@ -339,7 +346,7 @@ __global__ __launch_bounds__(64) void k_attn_simple(AttnArgs a) {
   __syncthreads();
   float oacc[4] = {0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
-  const int n_keys = a.len0 + a.len1;
+  const int n_keys = a.n_keys;
   const float scale = a.scale_log2;
   for (int k0 = 0; k0 < n_keys; k0 += 64) {
     const int j = k0 + lane;
@@ -347,10 +354,7 @@ __global__ __launch_bounds__(64) void k_attn_simple(AttnArgs a) {
     if (a.causal) vis = vis && (j <= a.n_prefix + qi);
     float sc = -INFINITY;
     if (vis) {
-      const TA* kp = j < a.len0
-                         ? reinterpret_cast<const TA*>(a.k0) + (int64_t)seq * a.s0_seq + (int64_t)hk * a.s0_head + (int64_t)j * d
-                         : reinterpret_cast<const TA*>(a.k1) + (int64_t)seq * a.s1_seq + (int64_t)hk * a.s1_head +
-                               (int64_t)(j - a.len0) * d;
+      const TA* kp = reinterpret_cast<const TA*>(a.k) + (int64_t)seq * a.s_seq + (int64_t)hk * a.s_head + (int64_t)j * d;
       float dot = 0.f;
       for (int i = 0; i < d; ++i) dot = fmaf(qs[i], ld_act<TA>(kp + i), dot);
       sc = dot * scale;
@@ -371,11 +375,8 @@ __global__ __launch_bounds__(64) void k_attn_simple(AttnArgs a) {
       for (int jj = 0; jj < 64 && k0 + jj < n_keys; ++jj) {
         const int j2 = k0 + jj;
         if (ps[jj] == 0.f) continue;
-        const TA* vp = j2 < a.len0
-                           ? reinterpret_cast<const TA*>(a.v0) + (int64_t)seq * a.s0_seq + (int64_t)hk * a.s0_head +
-                                 (int64_t)dd * a.vp0 + j2
-                           : reinterpret_cast<const TA*>(a.v1) + (int64_t)seq * a.s1_seq + (int64_t)hk * a.s1_head +
-                                 (int64_t)dd * a.vp1 + (j2 - a.len0);
+        const TA* vp = reinterpret_cast<const TA*>(a.v) + (int64_t)seq * a.s_seq + (int64_t)hk * a.s_head +
+                       (int64_t)dd * a.vp + j2;
         acc = fmaf(ps[jj], ld_act<TA>(vp), acc);
       }
       oacc[q] = acc;
@@ -391,21 +392,19 @@ __global__ __launch_bounds__(64) void k_attn_simple(AttnArgs a) {
 
 }  // namespace
 
-// Host launcher.  dtype: 0 = fp32 activations (plain path), 1 = bf16 (MFMA path, d = 256).
-int launch_attention(int dtype, const void* q, int64_t q_ld, const void* k0, const void* v0, int64_t s0_seq,
-                     int64_t s0_head, int vp0, int len0, const void* k1, const void* v1, int64_t s1_seq,
-                     int64_t s1_head, int vp1, int len1, int n_prefix, int causal, int seq_len, int n_seq, int n_q,
+// Host launcher.  dtype: 0 = fp32 activations (plain path), 1 = bf16 (MFMA
+// path: d = 256, K bf16, V^T fp16, vp a multiple of 8).
+int launch_attention(int dtype, const void* q, int64_t q_ld, const void* k, const void* v, int64_t s_seq,
+                     int64_t s_head, int vp, int n_keys, int n_prefix, int causal, int seq_len, int n_seq, int n_q,
                      int n_kv, int d, int n_split, float* part_o, float2* part_ml, void* out, hipStream_t s) {
   AttnArgs a;
   a.q = q; a.q_ld = q_ld;
-  a.k0 = k0; a.v0 = v0; a.k1 = k1; a.v1 = v1;
-  a.s0_seq = s0_seq; a.s0_head = s0_head; a.s1_seq = s1_seq; a.s1_head = s1_head;
-  a.vp0 = vp0; a.vp1 = vp1;
-  a.len0 = len0; a.len1 = len1; a.n_prefix = n_prefix; a.causal = causal;
+  a.k = k; a.v = v; a.s_seq = s_seq; a.s_head = s_head; a.vp = vp;
+  a.n_keys = n_keys; a.n_prefix = n_prefix; a.causal = causal;
   a.seq_len = seq_len; a.n_seq = n_seq; a.n_q = n_q; a.n_kv = n_kv; a.d = d;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
   a.part_o = part_o; a.part_ml = part_ml; a.out = out;
-  const int n_keys = len0 + len1;
+  if (n_keys < 1) return -1;
   if (dtype == 0) {
     a.n_split = 1;
     a.keys_per_split = n_keys;
@@ -413,7 +412,7 @@ int launch_attention(int dtype, const void* q, int64_t q_ld, const void* k0, con
     return hipGetLastError() == hipSuccess ? 0 : -5;
   }
   const int G = n_q / n_kv;
-  if (d != ATT_D || (G != 1 && G != 2 && G != 4) || n_q % n_kv) return -2;
+  if (d != ATT_D || (G != 1 && G != 2 && G != 4) || n_q % n_kv || vp % 8 || vp < n_keys) return -2;
   n_split = n_split < 1 ? 1 : n_split;
   int kps = DG_CEIL_DIV(n_keys, n_split);
   kps = DG_CEIL_DIV(kps, ATT_KT) * ATT_KT;

@@ -129,7 +129,8 @@ class DeviceCache:
         n = shape.n_layers * batch * shape.n_kv_heads * capacity * shape.d_head
         dt = _tdtype(shape)
         self.k = torch.zeros(n, dtype=dt, device=device)
-        self.v = torch.zeros(n, dtype=dt, device=device)
+        # bf16 models keep V^T in fp16 (exact for the bf16-rounded values)
+        self.v = torch.zeros(n, dtype=torch.float16 if dt == torch.bfloat16 else dt, device=device)
         self.shape = shape
         self.struct = KVCache(self.k.data_ptr(), self.v.data_ptr(), batch, capacity, 0)
 
@@ -146,6 +147,11 @@ class DeviceCache:
         return self.v.view(s.n_layers, self.struct.batch, s.n_kv_heads, s.d_head,
                            self.struct.capacity).transpose(-1, -2)
 
+    def valid_rows(self):
+        """Copies of K and V rows [0, length) (what the denoiser must leave as is)."""
+        L = self.struct.length
+        return self.view("k")[:, :, :, :L].clone(), self.view("v")[:, :, :, :L].clone()
+
     def fill_random(self, length: int, seed: int = 0, std: float = 1.0):
         """N(0, std) fill of rows [0, length) (synthetic prefix, no encoder)."""
         s = self.shape
@@ -153,7 +159,7 @@ class DeviceCache:
         for name, tid in (("k", synth.TID["kv_k"]), ("v", synth.TID["kv_v"])):
             view = self.view(name)
             tmp = torch.empty(s.n_layers * self.struct.batch * s.n_kv_heads * length * s.d_head,
-                              dtype=view.dtype, device=view.device)
+                              dtype=self.k.dtype, device=view.device)
             synth.dev_normal(tmp.data_ptr(), tmp.numel(), seed, tid, std, s.dtype, st)
             view[:, :, :, :length].copy_(tmp.view(s.n_layers, self.struct.batch, s.n_kv_heads, length, s.d_head))
         self.struct.length = length

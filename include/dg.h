@@ -99,10 +99,15 @@ typedef struct dg_weights {
   float lm_scale;      /* logits z = lm_scale * (RMSNorm(x) W_lm^T) */
 } dg_weights;
 
-/* KV cache in the model dtype, rows [0, length) valid:
- *   k: [n_layers][batch][n_kv][capacity][d_head]   post-RoPE keys
+/* KV cache, rows [0, length) valid:
+ *   k: [n_layers][batch][n_kv][capacity][d_head]   post-RoPE keys, model dtype
  *   v: [n_layers][batch][n_kv][d_head][capacity]   values, stored transposed so
- *      that attention streams contiguous runs of keys per dimension.
+ *      that attention streams contiguous runs of keys per dimension; fp32 for
+ *      fp32 models, fp16 for bf16 models (the bf16-rounded value, exact in
+ *      fp16 from magnitude 2^-17 up).
+ * bf16 models: capacity a multiple of 8 (else DG_ERR_UNSUPPORTED).
+ * Rows [length, capacity) are scratch: the denoiser writes its canvas K/V to
+ * rows [length, length + canvas) without changing `length`.
  * `length` is host bookkeeping updated by the appending calls at enqueue time. */
 typedef struct dg_kv_cache {
   void* k;
@@ -197,7 +202,9 @@ int dg_encode_append(const dg_model_config* cfg, const dg_weights* w, dg_kv_cach
 
 /* One denoising step over the canvases (report Figure 4, stage 2): embedding
  * plus self-conditioning, the layer stack with bidirectional canvas attention
- * over [cache ; canvas] (the cache is not written), final norm, fused LM head
+ * over [cache ; canvas] (the canvas K/V go to the cache's scratch rows
+ * [length, length + canvas); rows below length are not written; capacity
+ * below length + canvas: DG_ERR_KV_CAPACITY), final norm, fused LM head
  * (logits never stored), per-position entropy / sample / argmax, entropy-
  * bounded acceptance, re-noise, stop test.  Writes the canvas outputs. */
 int dg_denoise_step(const dg_model_config* cfg, const dg_weights* w, const dg_kv_cache* cache,

@@ -189,14 +189,14 @@ def test_forward_logits_match_oracle(which, request):
     tok = pb.canvas.tokens.cpu().numpy().reshape(pb.B, pb.C)
     for b in range(pb.B):
         assert np.array_equal(tok[b], smp.initial_canvas(pb.seeds[b], 0, pb.C, pb.shape.vocab))
-    k_before = pb.cache.k.clone()
+    kv_before = pb.cache.valid_rows()
     tr = {}
     zo = ost.denoise_logits(pb.shape, pb.W, pb.ocache, tok, None, pb.lm_scale, trace=tr)
     margins = _route_margins(pb.shape, tr)
     say(f"oracle routing margins: min {margins.min():.3e}, #<1e-3: {int((margins < 1e-3).sum())}")
     # routes forced to the oracle's choice: continuous outputs must match
     z, rg = _forward_logits(pb, 0, 48, force_ids=_forced_ids(tr), want_router=True)
-    assert torch.equal(k_before, pb.cache.k), "denoiser wrote the cache"
+    assert all(torch.equal(x, y) for x, y in zip(kv_before, pb.cache.valid_rows())), "denoiser wrote cache rows < length"
     ro = np.stack(tr["router_logits"])
     rerr = _err_summary(f"router logits {which} (oracle routes)", rg, ro)
     assert float(np.median(np.abs(rg - ro))) < ROUTE_MEDIAN[pb.shape.dtype]
