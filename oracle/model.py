@@ -28,7 +28,8 @@ step's tempered distribution, through a bias-free 2-matrix tanh-GELU MLP,
 added to the token embedding; untied LM head multiplied by the workload's
 LM-head scale.
 
-Storage/rounding contract (bf16 models): weights as stored; residual stream
+Storage/rounding contract (bf16 models): weights as stored (fp8 weights:
+E4M3 code times its output row's fp32 scale, exact in float64); residual stream
 fp32 on the GPU (fp64 here); GEMM inputs (norm outputs, attention output,
 GeGLU hidden, expected embedding, self-cond hidden, self-cond probabilities)
 rounded to bf16; q/k/v rounded to bf16 after RoPE (k, v are the cache
@@ -43,7 +44,7 @@ import numpy as np
 import synth
 from synth.configs import ModelShape
 
-from .numerics import gelu_tanh, rmsnorm, rope, round_bf16
+from .numerics import e4m3_decode, gelu_tanh, rmsnorm, rope, round_bf16
 
 
 class Weights:
@@ -81,7 +82,13 @@ class Weights:
         dt = self._dtype_of(name)
         shp = self._shape_of(name)
         if dt == "fp8":
-            raise NotImplementedError("fp8 weights are decoded by oracle.fp8")
+            # stored codes and per-output-row fp32 scales, dequantised exactly
+            rows = int(np.prod(shp[:-1]))
+            codes, sc = synth.e4m3_rows(self.shape.weight_seed, tid, rows, shp[-1], self.shape.weight_std)
+            w = (e4m3_decode(codes) * sc.astype(np.float64)[:, None]).reshape(shp)
+            if self._cache is not None:
+                self._cache[key] = w
+            return w
         w = synth.normal(self.shape.weight_seed, tid, shp, self.shape.weight_std,
                          "bf16_f64" if dt == "bf16" else "f32").astype(np.float64, copy=False)
         if self._cache is not None:

@@ -80,3 +80,25 @@ def e4m3_round(x: np.ndarray) -> np.ndarray:
     r = np.rint(a / q) * q
     r = np.minimum(r, 448.0)
     return np.sign(x) * r
+
+
+def e4m3_value(code: int) -> float:
+    """Value of one OCP FP8 E4M3 code (OCP 8-bit floating point specification,
+    E4M3 encoding): sign bit, 4 exponent bits with bias 7, 3 mantissa bits;
+    exponent field 0 holds the subnormals m/8 * 2^-6; S.1111.111 is NaN and
+    there are no infinities."""
+    sign = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+_E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """float64 values of an array of E4M3 codes (the 256 values of e4m3_value)."""
+    return _E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]

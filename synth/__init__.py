@@ -68,6 +68,7 @@ def _get_lib():
         lib.synth_normal_bf16_as_f64.argtypes = [u64, u64, u64, u64, f32, vp]
         lib.synth_tokens.argtypes = [u64, u64, u64, u64, ctypes.c_uint32, vp]
         lib.synth_dirichlet_rows.argtypes = [u64, u64, i64, i64, ctypes.c_double, vp]
+        lib.synth_e4m3_rows.argtypes = [u64, u64, i64, i64, f32, vp, vp]
         _lib = lib
     return _lib
 
@@ -108,6 +109,17 @@ def dirichlet_rows(seed: int, tensor: int, rows: int, vocab: int, alpha: float) 
     out = np.empty((rows, vocab), dtype=np.float32)
     _get_lib().synth_dirichlet_rows(seed, tensor, rows, vocab, alpha, out.ctypes.data)
     return out
+
+
+def e4m3_rows(seed: int, tensor: int, rows: int, cols: int, std: float):
+    """fp8 form of the bf16 normal tensor [rows][cols]: per-row scale
+    s_r = fp32(max|w_r| / 448) and OCP E4M3 codes of fp32(w / s_r) (round to
+    nearest even).  Returns (codes uint8 [rows][cols], scales float32 [rows])."""
+    codes = np.empty((rows, cols), dtype=np.uint8)
+    sc = np.empty(rows, dtype=np.float32)
+    _get_lib().synth_e4m3_rows(seed, tensor, rows, cols, ctypes.c_float(scale_for_std(std)), codes.ctypes.data,
+                               sc.ctypes.data)
+    return codes, sc
 
 
 def bf16_bits_to_f32(u16: np.ndarray) -> np.ndarray:
@@ -175,8 +187,9 @@ def _get_dev_lib():
         lib.synth_dev_normal_f32.argtypes = [vp, u64, u64, u64, u64, ctypes.c_float, vp]
         lib.synth_dev_tokens.argtypes = [vp, u64, u64, u64, u64, ctypes.c_uint32, vp]
         lib.synth_dev_normal_f32_transposed.argtypes = [vp, u64, u64, u64, u64, ctypes.c_float, vp]
+        lib.synth_dev_e4m3_rows.argtypes = [vp, vp, u64, u64, u64, u64, ctypes.c_float, vp]
         for f in (lib.synth_dev_normal_bf16, lib.synth_dev_normal_f32, lib.synth_dev_tokens,
-                  lib.synth_dev_normal_f32_transposed):
+                  lib.synth_dev_normal_f32_transposed, lib.synth_dev_e4m3_rows):
             f.restype = ctypes.c_int
         _dev_lib = lib
     return _dev_lib
@@ -203,3 +216,11 @@ def dev_normal_f32_transposed(ptr: int, rows: int, cols: int, seed: int, tensor:
     sc = ctypes.c_float(scale_for_std(std))
     if _get_dev_lib().synth_dev_normal_f32_transposed(ptr, seed, tensor, rows, cols, sc, stream) != 0:
         raise RuntimeError("synth device fill failed")
+
+
+def dev_e4m3_rows(codes_ptr: int, scale_ptr: int, rows: int, cols: int, seed: int, tensor: int, std: float,
+                  stream: int) -> None:
+    """Device twin of e4m3_rows: codes [rows][cols] (uint8) and scales [rows] (fp32)."""
+    sc = ctypes.c_float(scale_for_std(std))
+    if _get_dev_lib().synth_dev_e4m3_rows(codes_ptr, scale_ptr, seed, tensor, rows, cols, sc, stream) != 0:
+        raise RuntimeError("synth device fp8 fill failed")

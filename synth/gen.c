@@ -20,6 +20,11 @@
  *                    when a bf16 tensor is asked for.
  *   token          = (hi32(h) * V) >> 32   (exactly uniform when V is 2^b).
  *   uniform in (0,1) = ((h >> 11) + 0.5) * 2^-53.
+ *   fp8 weights    = the bf16 normal tensor quantised per output row r:
+ *                    s_r = fp32(max_c |w[r][c]| / 448)  (1 if the row is all zero),
+ *                    code[r][c] = E4M3 code of fp32(w[r][c] / s_r), rounded to
+ *                    nearest even, |x| >= 464 saturating to 448 (OCP FP8 E4M3:
+ *                    exponent bias 7, 3 mantissa bits, no infinities).
  */
 #include <math.h>
 #include <stdint.h>
@@ -74,6 +79,47 @@ void synth_normal_bf16_as_f64(uint64_t seed, uint64_t tensor, uint64_t start, ui
     float f;
     memcpy(&f, &u, 4);
     out[j] = (double)f;
+  }
+}
+
+/* OCP E4M3 code of x, round to nearest even. */
+static inline uint8_t synth_e4m3_rne(float x) {
+  uint32_t u;
+  memcpy(&u, &x, 4);
+  const uint8_t sign = (uint8_t)((u >> 24) & 0x80u);
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a >= 0x43E80000u) return sign | 0x7Eu; /* |x| >= 464 */
+  if (a < 0x3C800000u) {                     /* |x| < 2^-6: subnormal grid, step 2^-9 */
+    float f;
+    memcpy(&f, &a, 4);
+    return sign | (uint8_t)nearbyintf(f * 512.0f); /* 8 -> code 0x08, the smallest normal */
+  }
+  const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u); /* keep 3 mantissa bits, ties to even */
+  return sign | (uint8_t)((((r >> 23) - 120u) << 3) | ((r >> 20) & 7u));
+}
+
+/* Row-wise fp8 quantisation of the bf16 normal tensor [rows][cols] (element
+ * r*cols + c of the tensor's stream). */
+void synth_e4m3_rows(uint64_t seed, uint64_t tensor, int64_t rows, int64_t cols, float scale, uint8_t* codes,
+                     float* row_scale) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    float mx = 0.0f;
+    for (int64_t c = 0; c < cols; ++c) {
+      const uint32_t u = (uint32_t)synth_bf16_rne(synth_normal_value(synth_hash(seed, tensor, (uint64_t)(r * cols + c)), scale)) << 16;
+      float w;
+      memcpy(&w, &u, 4);
+      w = fabsf(w);
+      if (w > mx) mx = w;
+    }
+    const float s = mx > 0.0f ? mx / 448.0f : 1.0f;
+    row_scale[r] = s;
+    for (int64_t c = 0; c < cols; ++c) {
+      const uint32_t u = (uint32_t)synth_bf16_rne(synth_normal_value(synth_hash(seed, tensor, (uint64_t)(r * cols + c)), scale)) << 16;
+      float w;
+      memcpy(&w, &u, 4);
+      codes[r * cols + c] = synth_e4m3_rne(w / s);
+    }
   }
 }
 

@@ -48,6 +48,41 @@ __global__ void k_normal_f32_t(float* out, uint64_t seed, uint64_t tensor, uint6
   }
 }
 
+__device__ __forceinline__ float synth_bf16_value(uint64_t seed, uint64_t tensor, uint64_t i, float scale) {
+  uint32_t u = __float_as_uint(synth_normal_value(synth_hash(seed, tensor, i), scale));
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return __uint_as_float(u & 0xFFFF0000u);
+}
+
+// OCP E4M3 code of x, round to nearest even (|x| >= 464 saturates to 448).
+__device__ __forceinline__ uint8_t synth_e4m3_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint8_t sign = (uint8_t)((u >> 24) & 0x80u);
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a >= 0x43E80000u) return sign | 0x7Eu;
+  if (a < 0x3C800000u) return sign | (uint8_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+  return sign | (uint8_t)((((r >> 23) - 120u) << 3) | ((r >> 20) & 7u));
+}
+
+// One workgroup per row: row maximum of |w|, then the codes.
+__global__ __launch_bounds__(256) void k_e4m3_rows(uint8_t* codes, float* row_scale, uint64_t seed, uint64_t tensor,
+                                                   uint64_t cols, float scale) {
+  __shared__ float red[4];
+  const uint64_t r = blockIdx.x;
+  float mx = 0.0f;
+  for (uint64_t c = threadIdx.x; c < cols; c += 256)
+    mx = fmaxf(mx, fabsf(synth_bf16_value(seed, tensor, r * cols + c, scale)));
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = mx > 0.0f ? __fdiv_rn(mx, 448.0f) : 1.0f;
+  if (threadIdx.x == 0) row_scale[r] = s;
+  for (uint64_t c = threadIdx.x; c < cols; c += 256)
+    codes[r * cols + c] = synth_e4m3_rne(__fdiv_rn(synth_bf16_value(seed, tensor, r * cols + c, scale), s));
+}
+
 dim3 grid_for(uint64_t count) {
   uint64_t b = (count + 255) / 256;
   if (b > 65536) b = 65536;
@@ -84,6 +119,14 @@ int synth_dev_tokens(void* out, uint64_t seed, uint64_t tensor, uint64_t start, 
                      void* stream) {
   hipLaunchKernelGGL(k_tokens, grid_for(count), dim3(256), 0, (hipStream_t)stream, (int32_t*)out, seed, tensor, start,
                      count, vocab);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+int synth_dev_e4m3_rows(void* codes, void* row_scale, uint64_t seed, uint64_t tensor, uint64_t rows, uint64_t cols,
+                        float scale, void* stream) {
+  if (rows == 0 || rows > 0x7FFFFFFFull) return -1;
+  hipLaunchKernelGGL(k_e4m3_rows, dim3((unsigned)rows), dim3(256), 0, (hipStream_t)stream, (uint8_t*)codes,
+                     (float*)row_scale, seed, tensor, cols, scale);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

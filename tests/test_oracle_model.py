@@ -10,7 +10,7 @@ import synth
 from synth.configs import FULL_30, FULL_LAYER, TINY, WORKLOADS
 from oracle import model as om
 from oracle import step as ost
-from oracle.numerics import e4m3_round, gelu_tanh, rmsnorm, rope, round_bf16
+from oracle.numerics import e4m3_decode, e4m3_round, gelu_tanh, rmsnorm, rope, round_bf16
 
 
 def test_round_bf16_matches_torch():
@@ -28,6 +28,52 @@ def test_e4m3_matches_torch():
     x = np.clip(x, -448, 448)
     want = torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float64).numpy()
     assert np.array_equal(e4m3_round(x.astype(np.float64)), want)
+
+
+def test_e4m3_decode_matches_torch_and_spec():
+    """Every E4M3 code against torch's float8_e4m3fn (a library decode) and
+    the values the OCP FP8 specification fixes: max normal 448 (S.1111.110),
+    min normal 2^-6, min subnormal 2^-9, one = 0.0111.000, and the NaN codes."""
+    codes = np.arange(256, dtype=np.uint8)
+    got = e4m3_decode(codes)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan) and set(np.nonzero(nan)[0]) == {0x7F, 0xFF}
+    assert np.array_equal(got[~nan], want[~nan])
+    spec = {0x7E: 448.0, 0xFE: -448.0, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9, 0x38: 1.0, 0x00: 0.0, 0x07: 7 * 2.0 ** -9,
+            0x77: 240.0}
+    for c, v in spec.items():
+        assert got[c] == v, hex(c)
+
+
+def test_synth_fp8_rows_quantiser():
+    """The fp8 weight recipe (per-row scale = max|w|/448, RNE to E4M3 of w/s)
+    against torch's float->float8_e4m3fn cast of the same fp32 ratios, and the
+    rounding bound of the decoded values: |q s - w| <= half a step (2^-4 |w|
+    for normals, 2^-10 s below 2^-6 s), the row maximum exact at +-448 s."""
+    rows, cols = 48, 704
+    tid = synth.layer_tid(0, "ex_g")
+    codes, sc = synth.e4m3_rows(0, tid, rows, cols, 0.02)
+    w = synth.normal(0, tid, (rows, cols), 0.02, "bf16_f64")
+    w32 = w.astype(np.float32)
+    s_want = (np.abs(w32).max(axis=1) / np.float32(448.0)).astype(np.float32)
+    assert np.array_equal(sc, s_want)
+    ratio = (w32 / sc[:, None]).astype(np.float32)
+    want = torch.from_numpy(ratio).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, want)
+    deq = e4m3_decode(codes) * sc.astype(np.float64)[:, None]
+    a = np.abs(w)
+    small = a < 2.0 ** -6 * sc[:, None]
+    bound = np.where(small, 2.0 ** -10 * sc[:, None], 2.0 ** -4 * a)
+    assert np.all(np.abs(deq - w) <= bound * (1 + 1e-12))
+    imax = np.argmax(a, axis=1)
+    assert np.array_equal(np.abs(e4m3_decode(codes[np.arange(rows), imax])), np.full(rows, 448.0))
+    # oracle weights of an fp8 model are exactly these decoded values
+    fp8_shape = replace(TINY, dtype="bf16", expert_dtype="fp8", lm_dtype="fp8", d_expert=cols // 4,
+                        n_experts=1)
+    W = om.Weights(fp8_shape)
+    c2, s2 = synth.e4m3_rows(0, synth.layer_tid(0, "ex_d"), fp8_shape.d_model, fp8_shape.d_expert, 0.02)
+    assert np.array_equal(W.get("ex_d", 0)[0], e4m3_decode(c2) * s2.astype(np.float64)[:, None])
 
 
 def test_gelu_and_rmsnorm():
