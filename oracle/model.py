@@ -55,8 +55,9 @@ class Weights:
         self._cache = {} if cache else None
 
     def _dtype_of(self, name: str) -> str:
+        # expert weights: the routed experts and the shared expert alike
         s = self.shape
-        if name in ("ex_g", "ex_u", "ex_d"):
+        if name in ("ex_g", "ex_u", "ex_d", "sh_g", "sh_u", "sh_d"):
             return s.expert_dtype
         if name == "lm_head":
             return s.lm_dtype

@@ -24,7 +24,7 @@ class ModelShape:
     vocab: int
     d_selfcond: int
     dtype: str = "bf16"          # dense weights and activation storage: "f32" | "bf16"
-    expert_dtype: str = "bf16"   # "f32" | "bf16" | "fp8"
+    expert_dtype: str = "bf16"   # routed and shared experts: "f32" | "bf16" | "fp8"
     lm_dtype: str = "bf16"       # "f32" | "bf16" | "fp8"
     rope_base: float = 10000.0
     norm_eps: float = 1e-6
@@ -114,7 +114,9 @@ WORKLOADS = {
     # long context on the one-layer model: 32768 prefix, 8 committed canvases.
     "longctx": Workload("longctx", FULL_LAYER, batch=1, canvas=256, prefix=32768, n_steps=48,
                         adaptive=True, n_blocks=8, lm_scale=1.0),
-    # fp8 experts + LM head, 4 independent canvases with 8192-token prefixes, 12 steps.
+    # fp8 experts + LM head, 4 independent canvases over 8192-row prefixes (random N(0,1)
+    # cache as in the one-layer workload), 12 steps, sampler seeds 0..3.
     "fp8batch4": Workload("fp8batch4", FULL_LAYER_FP8, batch=4, canvas=256, prefix=8192,
-                          n_steps=12, adaptive=False, lm_scale=1.0, sampler_seeds=(0, 1, 2, 3)),
+                          prefix_mode="random_kv", n_steps=12, adaptive=False, lm_scale=1.0,
+                          sampler_seeds=(0, 1, 2, 3)),
 }

@@ -74,6 +74,9 @@ def test_synth_fp8_rows_quantiser():
     W = om.Weights(fp8_shape)
     c2, s2 = synth.e4m3_rows(0, synth.layer_tid(0, "ex_d"), fp8_shape.d_model, fp8_shape.d_expert, 0.02)
     assert np.array_equal(W.get("ex_d", 0)[0], e4m3_decode(c2) * s2.astype(np.float64)[:, None])
+    # the shared expert is an expert too: stored in fp8 as well
+    c3, s3 = synth.e4m3_rows(0, synth.layer_tid(0, "sh_d"), fp8_shape.d_model, fp8_shape.d_shared, 0.02)
+    assert np.array_equal(W.get("sh_d", 0), e4m3_decode(c3) * s3.astype(np.float64)[:, None])
 
 
 def test_gelu_and_rmsnorm():
