@@ -31,6 +31,7 @@ DG_ERR_WORKSPACE = -4
 DG_ERR_HIP = -5
 DG_DTYPE_F32 = 0
 DG_DTYPE_BF16 = 1
+DG_DTYPE_FP8_E4M3 = 2
 DG_FLAG_NONFINITE = 1
 DG_ENTROPY_BOUND = 0.1
 DG_STOP_THRESHOLD = 0.005
@@ -46,16 +47,19 @@ class ModelConfig(ctypes.Structure):
     _fields_ = [("n_layers", c_int32), ("d_model", c_int32), ("n_q_heads", c_int32), ("n_kv_heads", c_int32),
                 ("d_head", c_int32), ("n_experts", c_int32), ("top_k", c_int32), ("d_expert", c_int32),
                 ("d_shared", c_int32), ("vocab", c_int32), ("d_selfcond", c_int32), ("dtype", c_int32),
-                ("rope_base", c_float), ("norm_eps", c_float)]
+                ("rope_base", c_float), ("norm_eps", c_float), ("expert_dtype", c_int32), ("lm_dtype", c_int32)]
 
 
 class LayerWeights(ctypes.Structure):
-    _fields_ = [(n, c_void_p) for n in ("wqkv", "wo", "wr", "sh_g", "sh_u", "sh_d", "ex_g", "ex_u", "ex_d")]
+    _fields_ = [(n, c_void_p) for n in ("wqkv", "wo", "wr", "sh_g", "sh_u", "sh_d", "ex_g", "ex_u", "ex_d",
+                                        "ex_g_scale", "ex_u_scale", "ex_d_scale", "sh_g_scale", "sh_u_scale",
+                                        "sh_d_scale")]
 
 
 class Weights(ctypes.Structure):
     _fields_ = [("embed", c_void_p), ("embed_t", c_void_p), ("lm_head", c_void_p), ("sc_up", c_void_p),
-                ("sc_down", c_void_p), ("layers", POINTER(LayerWeights)), ("lm_scale", c_float)]
+                ("sc_down", c_void_p), ("layers", POINTER(LayerWeights)), ("lm_scale", c_float),
+                ("lm_head_scale", c_void_p)]
 
 
 class KVCache(ctypes.Structure):
@@ -96,6 +100,7 @@ _temperature = _sig("dg_temperature", c_float, c_int32, c_int32)
 _ws_bytes = _sig("dg_workspace_bytes", c_size_t, _P(ModelConfig), c_int32, c_int32)
 _pack = _sig("dg_pack_weight_bf16", c_int32, c_void_p, c_void_p, c_int64, c_int64, c_void_p)
 _pack_t = _sig("dg_pack_weight_bf16_transposed", c_int32, c_void_p, c_void_p, c_int64, c_int64, c_void_p)
+_pack8 = _sig("dg_pack_weight_fp8", c_int32, c_void_p, c_void_p, c_int64, c_int64, c_void_p)
 _init_canvas = _sig("dg_init_canvas", c_int32, _P(ModelConfig), _P(Canvas), c_int32, c_void_p)
 _encode = _sig("dg_encode_append", c_int32, _P(ModelConfig), _P(Weights), _P(KVCache), c_void_p, c_int32, c_int32,
                c_void_p, c_size_t, c_void_p)
@@ -119,6 +124,7 @@ _t_encode = _sig("dg_test_encode_append", c_int32, _P(ModelConfig), _P(Weights),
                  c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p)
 
 EXPORTED = ("dg_temperature", "dg_workspace_bytes", "dg_pack_weight_bf16", "dg_pack_weight_bf16_transposed",
+            "dg_pack_weight_fp8",
             "dg_init_canvas", "dg_encode_append", "dg_denoise_step", "dg_commit_block", "dg_status_string",
             "dg_test_sample_from_logits", "dg_test_route_from_logits", "dg_test_forward_logits",
             "dg_denoise_step_traced", "dg_encode_append_traced", "dg_test_encode_append")
@@ -147,6 +153,10 @@ def dg_pack_weight_bf16(dst, src, rows: int, cols: int, stream) -> None:
 
 def dg_pack_weight_bf16_transposed(dst, src, rows: int, cols: int, stream) -> None:
     _check(_pack_t(dst, src, rows, cols, stream), "dg_pack_weight_bf16_transposed")
+
+
+def dg_pack_weight_fp8(dst, src, rows: int, cols: int, stream) -> None:
+    _check(_pack8(dst, src, rows, cols, stream), "dg_pack_weight_fp8")
 
 
 def dg_init_canvas(cfg, canvas, block: int, stream) -> None:

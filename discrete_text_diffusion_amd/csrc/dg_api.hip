@@ -21,6 +21,7 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 struct Shape {
   int L, d, nq, nkv, dh, E, k, de, ds, V, dsc, dt;
+  bool ex8, lm8;  // fp8 expert / LM-head weights
   float rope_base, eps;
   int qdim, kvdim, qkv, n_sh, nvt;
   size_t act;  // bytes per activation element
@@ -31,6 +32,8 @@ Shape shape_of(const dg_model_config* c) {
   s.L = c->n_layers; s.d = c->d_model; s.nq = c->n_q_heads; s.nkv = c->n_kv_heads; s.dh = c->d_head;
   s.E = c->n_experts; s.k = c->top_k; s.de = c->d_expert; s.ds = c->d_shared; s.V = c->vocab;
   s.dsc = c->d_selfcond; s.dt = c->dtype;
+  s.ex8 = c->expert_dtype == DG_DTYPE_FP8_E4M3;
+  s.lm8 = c->lm_dtype == DG_DTYPE_FP8_E4M3;
   s.rope_base = c->rope_base; s.eps = c->norm_eps;
   s.qdim = s.nq * s.dh; s.kvdim = s.nkv * s.dh; s.qkv = s.qdim + 2 * s.kvdim;
   s.n_sh = s.de > 0 ? s.ds / s.de : 0;
@@ -46,6 +49,10 @@ int check_config(const dg_model_config* c) {
       c->vocab < 256 || c->d_selfcond < 1)
     return DG_ERR_INVALID_ARG;
   if (c->dtype != DG_DTYPE_F32 && c->dtype != DG_DTYPE_BF16) return DG_ERR_UNSUPPORTED;
+  // fp8 weights (experts, LM head) only in bf16 models
+  for (int wd : {c->expert_dtype, c->lm_dtype})
+    if (wd != c->dtype && !(wd == DG_DTYPE_FP8_E4M3 && c->dtype == DG_DTYPE_BF16)) return DG_ERR_UNSUPPORTED;
+  if (c->expert_dtype == DG_DTYPE_FP8_E4M3 && c->d_model % 128) return DG_ERR_UNSUPPORTED;
   if (c->n_q_heads % c->n_kv_heads || c->d_shared % c->d_expert || c->vocab % 256 || c->d_head % 2 ||
       c->top_k > 16 || c->n_experts > 255 || c->d_head > 256)
     return DG_ERR_UNSUPPORTED;
@@ -327,6 +334,11 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
       a.M = 0;
       a.epi = EPI_GEGLU; a.out_act = c.at<void>(c.p.h); a.ldo = s.de;
       a.n_split = 1; a.k_split = s.d;
+      if (s.ex8) {
+        a.w_fp8 = 1;
+        a.ws0 = lw.ex_g_scale; a.ws1 = lw.ex_u_scale; a.ws_group_stride = s.de;
+        a.ws0_alt = lw.sh_g_scale; a.ws1_alt = lw.sh_u_scale; a.ws_alt_stride = s.de;  // slice c: features c*de..
+      }
       if (bf) {
         a.n_fb = (s.de + 63) / 64;
         a.tile_fastest = 0;
@@ -348,6 +360,11 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
       a.tiles = c.at<GemmTile>(c.p.tiles); a.n_tiles_dev = c.at<int32_t>(c.p.n_tiles); a.max_tiles = max_tiles;
       a.epi = EPI_STORE_F32; a.out_f32 = c.at<float>(c.p.Y); a.ldo = s.d; a.split_stride = 0;
       a.n_split = 1; a.k_split = s.de;
+      if (s.ex8) {
+        a.w_fp8 = 1;
+        a.ws0 = lw.ex_d_scale; a.ws_group_stride = s.d;
+        a.ws0_alt = lw.sh_d_scale; a.ws_alt_stride = 0;  // K slices of one matrix: same output features
+      }
       if (bf) {
         a.n_fb = (s.d + 127) / 128;
         a.tile_fastest = 0;
@@ -373,9 +390,15 @@ int check_ws(const Plan& p, void* ws, size_t bytes) {
 
 int check_weights(const dg_model_config* cfg, const dg_weights* w) {
   if (!w || !w->embed || !w->lm_head || !w->layers) return DG_ERR_INVALID_ARG;
+  auto aligned = [](const float* p) { return p && reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+  if (cfg->lm_dtype == DG_DTYPE_FP8_E4M3 && !aligned(w->lm_head_scale)) return DG_ERR_INVALID_ARG;
   for (int l = 0; l < cfg->n_layers; ++l) {
     const dg_layer_weights& L = w->layers[l];
     if (!L.wqkv || !L.wo || !L.wr || !L.sh_g || !L.sh_u || !L.sh_d || !L.ex_g || !L.ex_u || !L.ex_d)
+      return DG_ERR_INVALID_ARG;
+    if (cfg->expert_dtype == DG_DTYPE_FP8_E4M3 &&
+        !(aligned(L.ex_g_scale) && aligned(L.ex_u_scale) && aligned(L.ex_d_scale) && aligned(L.sh_g_scale) &&
+          aligned(L.sh_u_scale) && aligned(L.sh_d_scale)))
       return DG_ERR_INVALID_ARG;
   }
   return DG_OK;
@@ -499,12 +522,17 @@ int lm_head(const Ctx& c, const dg_canvas* cv, const dg_step_params* p, float* l
   a.w0 = c.w->lm_head;
   a.alpha = c.w->lm_scale;
   a.M = T; a.N = s.V; a.K = s.d; a.n_main = 1; a.kt_main = s.d / 32;
+  if (s.lm8) {
+    a.w_fp8 = 1;
+    a.ws0 = c.w->lm_head_scale;
+  }
   if (bf && s.d % 64 == 0) {
     a.n_fb = s.nvt;
     a.n_split = 1;
     a.k_split = s.d;
     return launch_rowgemm(a, &lm, c.st);
   }
+  if (s.lm8) return DG_ERR_UNSUPPORTED;
   if (bf) {
     const int bm = 64;  // 64-row tiles keep several waves per SIMD streaming; other row tiles hit L2
     a.max_tiles = (T + bm - 1) / bm;
@@ -564,6 +592,12 @@ int dg_pack_weight_bf16_transposed(void* d_dst, const void* d_src, int64_t rows,
   if (!d_dst || !d_src || rows <= 0 || cols <= 0 || rows % 16 || cols % 32) return DG_ERR_INVALID_ARG;
   return launch_pack_bf16((bf16_t*)d_dst, (const bf16_t*)d_src, rows, cols, 1, (hipStream_t)stream) == 0 ? DG_OK
                                                                                                           : DG_ERR_HIP;
+}
+
+int dg_pack_weight_fp8(void* d_dst, const void* d_src, int64_t rows, int64_t cols, void* stream) {
+  if (!d_dst || !d_src || rows <= 0 || cols <= 0 || rows % 16 || cols % 32) return DG_ERR_INVALID_ARG;
+  return launch_pack_fp8((uint8_t*)d_dst, (const uint8_t*)d_src, rows, cols, (hipStream_t)stream) == 0 ? DG_OK
+                                                                                                      : DG_ERR_HIP;
 }
 
 int dg_init_canvas(const dg_model_config* cfg, dg_canvas* cv, int32_t block, void* stream) {

@@ -59,6 +59,16 @@ struct GemmArgs {
   const void* w1_alt;
   int64_t w_alt_stride;
   int32_t n_main;
+  // fp8 weights: E4M3 codes in 16 x 32 tiles of 512 B (8 codes per lane, A-operand
+  // lane order), each output feature n scaled by an fp32 factor: main group g
+  // reads ws0/ws1[g * ws_group_stride + n], alt group c ws0_alt/ws1_alt[c * ws_alt_stride + n]
+  int32_t w_fp8;
+  const float* ws0;
+  const float* ws1;
+  int64_t ws_group_stride;
+  const float* ws0_alt;
+  const float* ws1_alt;
+  int64_t ws_alt_stride;
   int32_t kt_main;     // 32-wide k tiles per 16-row tile of a main-group matrix
   int32_t kt_alt;      // same for alt groups
   int32_t kt_off_alt;  // alt group c starts at k tile c * kt_off_alt
@@ -110,6 +120,7 @@ int launch_split_epilogue(const GemmArgs& a, const float* part, int n_split, int
                           hipStream_t s);
 int launch_gemm_simple(const GemmArgs& a, hipStream_t s);
 int launch_pack_bf16(bf16_t* dst, const bf16_t* src, int64_t rows, int64_t cols, int transposed, hipStream_t s);
+int launch_pack_fp8(uint8_t* dst, const uint8_t* src, int64_t rows, int64_t cols, hipStream_t s);
 int launch_lm_partials_from_logits(const float* logits, int rows, const LmArgs& lm, hipStream_t s);
 // k_route.hip
 int launch_topk(const float* part, int n_split, int64_t split_stride, int T, int E, int k, const int32_t* forced,

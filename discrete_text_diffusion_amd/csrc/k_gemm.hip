@@ -163,32 +163,47 @@ __device__ __forceinline__ uint4 load_act8(const GemmArgs& a, int arow, int k) {
 }
 
 struct GroupW {
-  const bf16_t* w0;
-  const bf16_t* w1;
+  const char* w0;  // first byte of the group's (packed) matrix
+  const char* w1;
+  const float* s0;  // fp8: per-feature scales of the group (null otherwise)
+  const float* s1;
   int kt, kt_off;
 };
 
-__device__ __forceinline__ GroupW group_weights(const GemmArgs& a, int g) {
+// Weight and scale bases of group g (an expert, or a shared-expert slice).
+// esize: bytes per weight element (2 bf16, 1 fp8 code).
+__device__ __forceinline__ GroupW group_weights(const GemmArgs& a, int g, int esize) {
   GroupW r;
   if (g < a.n_main) {
-    r.w0 = reinterpret_cast<const bf16_t*>(a.w0) + (int64_t)g * a.w_group_stride;
-    r.w1 = a.w1 ? reinterpret_cast<const bf16_t*>(a.w1) + (int64_t)g * a.w_group_stride : nullptr;
+    r.w0 = reinterpret_cast<const char*>(a.w0) + (int64_t)g * a.w_group_stride * esize;
+    r.w1 = a.w1 ? reinterpret_cast<const char*>(a.w1) + (int64_t)g * a.w_group_stride * esize : nullptr;
+    r.s0 = a.ws0 ? a.ws0 + (int64_t)g * a.ws_group_stride : nullptr;
+    r.s1 = a.ws1 ? a.ws1 + (int64_t)g * a.ws_group_stride : nullptr;
     r.kt = a.kt_main;
     r.kt_off = 0;
   } else {
     const int c = g - a.n_main;
-    r.w0 = reinterpret_cast<const bf16_t*>(a.w0_alt) + (int64_t)c * a.w_alt_stride;
-    r.w1 = a.w1_alt ? reinterpret_cast<const bf16_t*>(a.w1_alt) + (int64_t)c * a.w_alt_stride : nullptr;
+    r.w0 = reinterpret_cast<const char*>(a.w0_alt) + (int64_t)c * a.w_alt_stride * esize;
+    r.w1 = a.w1_alt ? reinterpret_cast<const char*>(a.w1_alt) + (int64_t)c * a.w_alt_stride * esize : nullptr;
+    r.s0 = a.ws0_alt ? a.ws0_alt + (int64_t)c * a.ws_alt_stride : nullptr;
+    r.s1 = a.ws1_alt ? a.ws1_alt + (int64_t)c * a.ws_alt_stride : nullptr;
     r.kt = a.kt_alt;
     r.kt_off = c * a.kt_off_alt;
   }
   return r;
 }
 
+// Weight operand registers: one 16-byte bf16 fragment, or 8 fp8 codes
+// converted to bf16 when the MFMA consumes them.
+template <bool FP8> struct WFrag { typedef bf16x8_t type; };
+template <> struct WFrag<true> { typedef uint2 type; };
+__device__ __forceinline__ bf16x8_t wfrag_bf16(bf16x8_t w) { return w; }
+__device__ __forceinline__ bf16x8_t wfrag_bf16(uint2 w) { return fp8x8_to_bf16(w); }
+
 // Main loop shared by the generic and the LM-head kernels.
-template <int BM, int NWT, int KC, bool GEGLU, int ACT>
-__device__ __forceinline__ void wsgemm_mainloop(const GemmArgs& a, const GemmTile& td, int fb, int ks,
-                                                bf16_t* xs, f32x4_t (&acc)[NWT][BM / 16],
+template <int BM, int NWT, int KC, bool GEGLU, int ACT, bool FP8 = false>
+__device__ __forceinline__ void wsgemm_mainloop(const GemmArgs& a, const GemmTile& td, const GroupW& gw, int fb,
+                                                int ks, bf16_t* xs, f32x4_t (&acc)[NWT][BM / 16],
                                                 f32x4_t (&accu)[NWT][BM / 16]) {
   constexpr int MW = BM / 16;
   constexpr int KS = KC / 32;          // MFMA k-steps per chunk
@@ -197,8 +212,10 @@ __device__ __forceinline__ void wsgemm_mainloop(const GemmArgs& a, const GemmTil
   constexpr int NV = BM * VPR;         // vectors per chunk
   constexpr int VPT = (NV + kThreads - 1) / kThreads;
 
+  constexpr int TILE_B = FP8 ? 512 : 1024;  // bytes of one 16 x 32 weight tile
+  constexpr int LANE_B = FP8 ? 8 : 16;      // bytes of one lane's fragment
+  using W_t = typename WFrag<FP8>::type;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const GroupW gw = group_weights(a, td.group);
 
 #pragma unroll
   for (int i = 0; i < NWT; ++i)
@@ -226,20 +243,20 @@ __device__ __forceinline__ void wsgemm_mainloop(const GemmArgs& a, const GemmTil
   }
 
   // weight tile pointers of this wave
-  const bf16_t* wp0[NWT];
-  const bf16_t* wp1[NWT];
+  const char* wp0[NWT];
+  const char* wp1[NWT];
   bool wval[NWT];
 #pragma unroll
   for (int i = 0; i < NWT; ++i) {
     const int ft = (fb * 4 + wave) * NWT + i;
     wval[i] = ft * 16 < a.N;
-    const int64_t off = ((int64_t)(wval[i] ? ft : 0) * gw.kt + gw.kt_off) * 512 + lane * 8;
+    const int64_t off = ((int64_t)(wval[i] ? ft : 0) * gw.kt + gw.kt_off) * TILE_B + lane * LANE_B;
     wp0[i] = gw.w0 + off;
     wp1[i] = GEGLU ? gw.w1 + off : nullptr;
   }
 
-  bf16x8_t wa[2][KS][NWT];
-  bf16x8_t wb[2][KS][NWT];
+  W_t wa[2][KS][NWT];
+  W_t wb[2][KS][NWT];
   uint4 xv[VPT];
 
   auto load_w = [&](auto BUF, int k0) {
@@ -250,8 +267,8 @@ __device__ __forceinline__ void wsgemm_mainloop(const GemmArgs& a, const GemmTil
 #pragma unroll
       for (int i = 0; i < NWT; ++i) {
         if (wval[i]) {
-          wa[buf][s][i] = *reinterpret_cast<const bf16x8_t*>(wp0[i] + (int64_t)(kt0 + s) * 512);
-          if constexpr (GEGLU) wb[buf][s][i] = *reinterpret_cast<const bf16x8_t*>(wp1[i] + (int64_t)(kt0 + s) * 512);
+          wa[buf][s][i] = *reinterpret_cast<const W_t*>(wp0[i] + (int64_t)(kt0 + s) * TILE_B);
+          if constexpr (GEGLU) wb[buf][s][i] = *reinterpret_cast<const W_t*>(wp1[i] + (int64_t)(kt0 + s) * TILE_B);
         }
       }
   };
@@ -289,14 +306,16 @@ __device__ __forceinline__ void wsgemm_mainloop(const GemmArgs& a, const GemmTil
 #pragma unroll
       for (int i = 0; i < NWT; ++i) {
         if (!wval[i]) continue;
+        const bf16x8_t wai = wfrag_bf16(wa[cur][s][i]);
+        bf16x8_t wbi = wai;
+        if constexpr (GEGLU) wbi = wfrag_bf16(wb[cur][s][i]);
 #pragma unroll
         for (int j = 0; j < MW; ++j) {
           if constexpr (ACT == ACT_BF16_SCALED) {
-            accu[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[cur][s][i], bx[j], accu[i][j], 0, 0, 0);
+            accu[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wai, bx[j], accu[i][j], 0, 0, 0);
           } else {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[cur][s][i], bx[j], acc[i][j], 0, 0, 0);
-            if constexpr (GEGLU)
-              accu[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[cur][s][i], bx[j], accu[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wai, bx[j], acc[i][j], 0, 0, 0);
+            if constexpr (GEGLU) accu[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wbi, bx[j], accu[i][j], 0, 0, 0);
           }
         }
       }
@@ -337,7 +356,7 @@ __device__ __forceinline__ void wsgemm_mainloop(const GemmArgs& a, const GemmTil
   }
 }
 
-template <int BM, int NWT, int KC, bool GEGLU, int ACT>
+template <int BM, int NWT, int KC, bool GEGLU, int ACT, bool FP8>
 __global__ __launch_bounds__(kThreads) void k_wsgemm(GemmArgs a) {
   constexpr int MW = BM / 16;
   constexpr int LD = KC + 8;
@@ -354,21 +373,38 @@ __global__ __launch_bounds__(kThreads) void k_wsgemm(GemmArgs a) {
   if (td.nrows <= 0) return;
 
   f32x4_t acc[NWT][MW], accu[NWT][MW];
-  wsgemm_mainloop<BM, NWT, KC, GEGLU, ACT>(a, td, fb, ks, xs, acc, accu);
+  const GroupW gw = group_weights(a, td.group, FP8 ? 1 : 2);
+  wsgemm_mainloop<BM, NWT, KC, GEGLU, ACT, FP8>(a, td, gw, fb, ks, xs, acc, accu);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < NWT; ++i) {
     const int ft = (fb * 4 + wave) * NWT + i;
     const int n = ft * 16 + (lane >> 4) * 4;
+    // fp8: per-feature scales of the four features this lane holds
+    f32x4_t sg = f32x4_t{1.f, 1.f, 1.f, 1.f}, su = sg;
+    if constexpr (FP8) {
+      if (ft * 16 < a.N) {
+        const float4 v0 = *reinterpret_cast<const float4*>(gw.s0 + n);
+        sg = f32x4_t{v0.x, v0.y, v0.z, v0.w};
+        if constexpr (GEGLU) {
+          const float4 v1 = *reinterpret_cast<const float4*>(gw.s1 + n);
+          su = f32x4_t{v1.x, v1.y, v1.z, v1.w};
+        }
+      }
+    }
 #pragma unroll
     for (int j = 0; j < MW; ++j) {
       const int r = j * 16 + (lane & 15);
       if (ft * 16 < a.N && r < td.nrows) {
         const int orow = td.row0 + r;
-        const f32x4_t g = acc[i][j];
+        f32x4_t g = acc[i][j];
         f32x4_t u = g;
         if constexpr (GEGLU) u = accu[i][j];
+        if constexpr (FP8) {
+          g *= sg;
+          u *= su;
+        }
         epi_pair<bf16_t>(a, ks, orow, n, g[0], g[1], u[0], u[1]);
         epi_pair<bf16_t>(a, ks, orow, n + 2, g[2], g[3], u[2], u[3]);
       }
@@ -561,7 +597,7 @@ __global__ __launch_bounds__(kThreads) void k_lmhead(GemmArgs a, LmArgs lm) {
   const GemmTile td{0, tile * BM, min(BM, a.M - tile * BM), 0};
 
   f32x4_t acc[4][MW], accu[4][MW];
-  wsgemm_mainloop<BM, 4, LM_KC, false, ACT_BF16>(a, td, fb, 0, xs, acc, accu);
+  wsgemm_mainloop<BM, 4, LM_KC, false, ACT_BF16>(a, td, group_weights(a, 0, 2), fb, 0, xs, acc, accu);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // halves of 64 rows through a 64 x 256 fp32 tile in LDS
@@ -634,13 +670,14 @@ constexpr int RG_X_BYTES = RG_ROWS * RG_ROW_BYTES;   // activations of one chunk
 constexpr int RG_XDMA = RG_ROWS / 16 / 8;            // activation instructions per wave per chunk
 constexpr int RG_ZROWS = 128;                        // LM head: logit rows staged at a time
 
-template <bool LMHEAD, bool SCALED>
+template <bool LMHEAD, bool SCALED, bool FP8>
 struct RgCfg {
   static constexpr int NWT = SCALED ? 2 : 4;
   static constexpr int BN = 4 * NWT * 16;                  // features per workgroup
-  static constexpr int WDMA = BN / 16 / 8;                 // weight tiles per wave per chunk
+  static constexpr int WTILE = FP8 ? 512 : 1024;           // bytes of a 16 x 32 weight tile
+  static constexpr int WDMA = BN / 16 * WTILE / 1024 / 8;  // 1 KiB weight loads per wave per chunk
   static constexpr int LOADS = RG_XDMA + WDMA;             // loads per wave per chunk
-  static constexpr int STAGE = RG_X_BYTES + BN * 64;       // activations + weight tiles
+  static constexpr int STAGE = RG_X_BYTES + BN / 16 * WTILE;  // activations + weight tiles
   static constexpr int RING = RG_SLOTS * STAGE;
   static constexpr int BODY = LMHEAD && RG_ZROWS * LM_ZLD * 4 > RING ? RG_ZROWS * LM_ZLD * 4 : RING;
   static constexpr int EXTRA = LMHEAD ? RG_ROWS * 4 : SCALED ? 2 * RG_ROWS * 4 : 0;  // uniforms / factor ring
@@ -651,9 +688,9 @@ __device__ __forceinline__ int rg_swz(int row) { return (row >> 1) & 3; }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-template <bool LMHEAD, bool SCALED>
+template <bool LMHEAD, bool SCALED, bool FP8>
 __global__ __launch_bounds__(RG_THREADS, 1) void k_rowgemm(GemmArgs a, LmArgs lm) {
-  using C = RgCfg<LMHEAD, SCALED>;
+  using C = RgCfg<LMHEAD, SCALED, FP8>;
   constexpr int MW = 8;
   constexpr int NWT = C::NWT;
   // one LDS object (stages / logit tile, then the per-row uniforms or factor
@@ -693,16 +730,21 @@ __global__ __launch_bounds__(RG_THREADS, 1) void k_rowgemm(GemmArgs a, LmArgs lm
   bool wval[NWT];
 #pragma unroll
   for (int i = 0; i < NWT; ++i) wval[i] = (fb * (C::BN / 16) + cg * NWT + i) * 16 < a.N;
-  // weight tiles moved by this wave: block tiles WDMA wave + e (tiles past N reload tile 0)
-  // (fixed-size array: a template-dependent size captured by the lambda below
-  // makes hipcc drop the host-side launch stubs of this kernel)
-  const bf16_t* wsrc[2];
-  static_assert(C::WDMA <= 2, "weight tiles per wave per chunk");
+  // 1 KiB weight loads of this wave: load u = WDMA wave + e moves block tile u
+  // (bf16), or tiles 2u and 2u + 1 (fp8, 32 lanes each); tiles past N reload
+  // tile 0.  (Fixed-size array: a template-dependent size captured by the
+  // lambda below makes hipcc drop the host-side launch stubs of this kernel.)
+  const char* wsrc[2];
+  static_assert(C::WDMA <= 2, "weight loads per wave per chunk");
+  // (a member of C named inside the lambda also drops the launch stubs)
+  const int64_t wstep = C::WTILE;
 #pragma unroll
   for (int e = 0; e < C::WDMA; ++e) {
-    const int ft = fb * (C::BN / 16) + wave * C::WDMA + e;
-    wsrc[e] = reinterpret_cast<const bf16_t*>(a.w0) + ((int64_t)(ft * 16 < a.N ? ft : 0) * a.kt_main + (kb >> 5)) * 512 +
-              lane * 8;
+    const int u = wave * C::WDMA + e;
+    const int ft = fb * (C::BN / 16) + (FP8 ? 2 * u + (lane >> 5) : u);
+    const int lofs = FP8 ? (lane & 31) * 16 : lane * 16;
+    wsrc[e] = reinterpret_cast<const char*>(a.w0) +
+              ((int64_t)(ft * 16 < a.N ? ft : 0) * a.kt_main + (kb >> 5)) * C::WTILE + lofs;
   }
   // activation instruction d of this wave fills rows (wave*RG_XDMA + d)*16 + lane/4,
   // physical column group lane%4 <- logical group (lane%4) ^ swz(row)
@@ -724,7 +766,7 @@ __global__ __launch_bounds__(RG_THREADS, 1) void k_rowgemm(GemmArgs a, LmArgs lm
                                        0);
 #pragma unroll
     for (int e = 0; e < C::WDMA; ++e)
-      __builtin_amdgcn_global_load_lds(wsrc[e] + (int64_t)cc * 512,
+      __builtin_amdgcn_global_load_lds(wsrc[e] + (int64_t)cc * wstep,
                                        (lds_void_t*)(st + RG_X_BYTES + (wave * C::WDMA + e) * 1024), 16, 0, 0);
     if constexpr (SCALED) {
       // first chunk of a K tile: wave 0 fetches the tile's 256 row factors
@@ -760,8 +802,12 @@ __global__ __launch_bounds__(RG_THREADS, 1) void k_rowgemm(GemmArgs a, LmArgs lm
     const unsigned char* st = smem + (c % RG_SLOTS) * C::STAGE;
     bf16x8_t wf[NWT];
 #pragma unroll
-    for (int i = 0; i < NWT; ++i)
-      wf[i] = *reinterpret_cast<const bf16x8_t*>(st + RG_X_BYTES + (cg * NWT + i) * 1024 + lane * 16);
+    for (int i = 0; i < NWT; ++i) {
+      if constexpr (FP8)
+        wf[i] = fp8x8_to_bf16(*reinterpret_cast<const uint2*>(st + RG_X_BYTES + (cg * NWT + i) * 512 + lane * 8));
+      else
+        wf[i] = *reinterpret_cast<const bf16x8_t*>(st + RG_X_BYTES + (cg * NWT + i) * 1024 + lane * 16);
+    }
 #pragma unroll
     for (int j = 0; j < MW; ++j) {
       const int r = rh * 128 + j * 16 + (lane & 15);
@@ -820,11 +866,16 @@ __global__ __launch_bounds__(RG_THREADS, 1) void k_rowgemm(GemmArgs a, LmArgs lm
 #pragma unroll
         for (int i = 0; i < NWT; ++i) {
           const int col = (cg * NWT + i) * 16 + (lane >> 4) * 4;
+          // z = alpha acc (bf16 weights) or alpha scale[n] acc (fp8 weights)
+          f32x4_t sc = f32x4_t{a.alpha, a.alpha, a.alpha, a.alpha};
+          if constexpr (FP8) {
+            const float4 w = *reinterpret_cast<const float4*>(a.ws0 + (int64_t)fb * C::BN + col);
+            sc = f32x4_t{a.alpha * w.x, a.alpha * w.y, a.alpha * w.z, a.alpha * w.w};
+          }
 #pragma unroll
           for (int j = 0; j < MW; ++j) {
-            const f32x4_t v = acc[i][j];
-            *reinterpret_cast<float4*>(zt + (j * 16 + (lane & 15)) * LM_ZLD + col) =
-                make_float4(a.alpha * v[0], a.alpha * v[1], a.alpha * v[2], a.alpha * v[3]);
+            const f32x4_t v = acc[i][j] * sc;
+            *reinterpret_cast<float4*>(zt + (j * 16 + (lane & 15)) * LM_ZLD + col) = make_float4(v[0], v[1], v[2], v[3]);
           }
         }
       }
@@ -953,6 +1004,21 @@ __global__ __launch_bounds__(kThreads) void k_pack_bf16(bf16_t* dst, const bf16_
   *reinterpret_cast<uint4*>(dst + t * 512 + lane * 8) = v;
 }
 
+// Logical E4M3 codes [rows][cols] -> fp8 weight layout: 16 x 32 tiles of 512 B,
+// tile (nt, kt) at byte (nt * cols / 32 + kt) * 512, lane l's 8 codes (row
+// nt*16 + l%16, k = kt*32 + 8(l/16) ...) at byte 8 l of the tile.
+__global__ __launch_bounds__(kThreads) void k_pack_fp8(uint8_t* dst, const uint8_t* src, int64_t rows, int64_t cols) {
+  const int64_t kt_n = cols / 32;
+  const int64_t tiles = (rows / 16) * kt_n;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= tiles) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t nt = t / kt_n, kt = t - nt * kt_n;
+  const int64_t r = nt * 16 + (lane & 15);
+  const int64_t c = kt * 32 + (lane >> 4) * 8;
+  *reinterpret_cast<uint2*>(dst + t * 512 + lane * 8) = *reinterpret_cast<const uint2*>(src + r * cols + c);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -963,14 +1029,35 @@ static void launch_t(const GemmArgs& a0, int act, hipStream_t s) {
   GemmArgs a = a0;
   a.nblocks = round8(a.n_split * a.max_tiles * a.n_fb);
   dim3 grid(a.nblocks);
-  if (act == ACT_BF16) hipLaunchKernelGGL((k_wsgemm<BM, NWT, KC, GEGLU, ACT_BF16>), grid, dim3(kThreads), 0, s, a);
-  else if (act == ACT_F32) hipLaunchKernelGGL((k_wsgemm<BM, NWT, KC, GEGLU, ACT_F32>), grid, dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL((k_wsgemm<BM, NWT, KC, GEGLU, ACT_BF16_SCALED>), grid, dim3(kThreads), 0, s, a);
+  if (act == ACT_BF16) hipLaunchKernelGGL((k_wsgemm<BM, NWT, KC, GEGLU, ACT_BF16, false>), grid, dim3(kThreads), 0, s, a);
+  else if (act == ACT_F32) hipLaunchKernelGGL((k_wsgemm<BM, NWT, KC, GEGLU, ACT_F32, false>), grid, dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL((k_wsgemm<BM, NWT, KC, GEGLU, ACT_BF16_SCALED, false>), grid, dim3(kThreads), 0, s, a);
+}
+
+template <int BM, int NWT, int KC, bool GEGLU>
+static void launch_fp8(const GemmArgs& a0, hipStream_t s) {
+  GemmArgs a = a0;
+  a.nblocks = round8(a.n_split * a.max_tiles * a.n_fb);
+  hipLaunchKernelGGL((k_wsgemm<BM, NWT, KC, GEGLU, ACT_BF16, true>), dim3(a.nblocks), dim3(kThreads), 0, s, a);
 }
 
 int launch_wsgemm(const GemmArgs& a, int bm, int nwt, int kc, bool geglu, hipStream_t s) {
   if (a.K % kc != 0 || a.k_split % kc != 0 || a.N % 16 != 0) return -1;
   if (a.act_kind == ACT_BF16_SCALED && (a.k_split % 256 != 0 || a.K % 256 != 0 || geglu)) return -1;
+  if (a.w_fp8) {
+    // fp8 weights: bf16 rows, per-feature scales for every group present
+    if (a.act_kind != ACT_BF16 || !a.ws0 || (geglu && !a.ws1)) return -1;
+    if (a.w0_alt && (!a.ws0_alt || (geglu && !a.ws1_alt))) return -1;
+    // float4 scale reads: 16-byte aligned bases and group strides
+    if (a.ws_group_stride % 4 || a.ws_alt_stride % 4 || reinterpret_cast<uintptr_t>(a.ws0) % 16 ||
+        reinterpret_cast<uintptr_t>(a.ws1) % 16 || reinterpret_cast<uintptr_t>(a.ws0_alt) % 16 ||
+        reinterpret_cast<uintptr_t>(a.ws1_alt) % 16)
+      return -1;
+    if (bm == 32 && nwt == 1 && kc == 128 && geglu) launch_fp8<32, 1, 128, true>(a, s);
+    else if (bm == 32 && nwt == 2 && kc == 64 && !geglu) launch_fp8<32, 2, 64, false>(a, s);
+    else return -2;
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+  }
 #define DG_CASE(BM_, NWT_, KC_, GG_)                                   \
   if (bm == BM_ && nwt == NWT_ && kc == KC_ && geglu == GG_) {         \
     launch_t<BM_, NWT_, KC_, GG_>(a, a.act_kind, s);                   \
@@ -1013,6 +1100,13 @@ int launch_pack_bf16(bf16_t* dst, const bf16_t* src, int64_t rows, int64_t cols,
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
+int launch_pack_fp8(uint8_t* dst, const uint8_t* src, int64_t rows, int64_t cols, hipStream_t s) {
+  if (rows % 16 || cols % 32) return -1;
+  const int64_t tiles = (rows / 16) * (cols / 32);
+  hipLaunchKernelGGL(k_pack_fp8, dim3((unsigned)DG_CEIL_DIV(tiles, 4)), dim3(kThreads), 0, s, dst, src, rows, cols);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
 int launch_lm_partials_from_logits(const float* logits, int rows, const LmArgs& lm, hipStream_t s) {
   const int64_t waves = (int64_t)((rows + 3) / 4) * (lm.vocab >> 8);
   hipLaunchKernelGGL(k_partials_from_logits, dim3((unsigned)DG_CEIL_DIV(waves, 4)), dim3(kThreads), 0, s,
@@ -1023,7 +1117,9 @@ int launch_lm_partials_from_logits(const float* logits, int rows, const LmArgs& 
 int launch_rowgemm(const GemmArgs& a0, const LmArgs* lm, hipStream_t s) {
   GemmArgs a = a0;
   const bool scaled = a.act_kind == ACT_BF16_SCALED;
-  const int bn = scaled ? RgCfg<false, true>::BN : RgCfg<false, false>::BN;
+  const int bn = scaled ? RgCfg<false, true, false>::BN : RgCfg<false, false, false>::BN;
+  // fp8 weights: LM head only, with 16-byte aligned per-feature scales
+  if (a.w_fp8 && (!lm || !a.ws0 || reinterpret_cast<uintptr_t>(a.ws0) % 16)) return -1;
   if (a.tiles || a.row_map || a.w1 || (a.act_kind != ACT_BF16 && !scaled) || a.M < 1 || a.N % 16 ||
       a.K % RG_KC || a.k_split % RG_KC || a.act_ld % 8)
     return -1;
@@ -1037,9 +1133,10 @@ int launch_rowgemm(const GemmArgs& a0, const LmArgs* lm, hipStream_t s) {
   if (lm) l = *lm;
   else memset(&l, 0, sizeof(l));
   const dim3 grid(a.nblocks), block(RG_THREADS);
-  if (lm) hipLaunchKernelGGL((k_rowgemm<true, false>), grid, block, 0, s, a, l);
-  else if (scaled) hipLaunchKernelGGL((k_rowgemm<false, true>), grid, block, 0, s, a, l);
-  else hipLaunchKernelGGL((k_rowgemm<false, false>), grid, block, 0, s, a, l);
+  if (lm && a.w_fp8) hipLaunchKernelGGL((k_rowgemm<true, false, true>), grid, block, 0, s, a, l);
+  else if (lm) hipLaunchKernelGGL((k_rowgemm<true, false, false>), grid, block, 0, s, a, l);
+  else if (scaled) hipLaunchKernelGGL((k_rowgemm<false, true, false>), grid, block, 0, s, a, l);
+  else hipLaunchKernelGGL((k_rowgemm<false, false, false>), grid, block, 0, s, a, l);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

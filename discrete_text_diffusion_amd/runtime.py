@@ -15,7 +15,8 @@ import synth
 from synth.configs import ModelShape
 
 from . import (Canvas, KVCache, LayerWeights, ModelConfig, StepParams, Weights, DG_DTYPE_BF16, DG_DTYPE_F32,
-               dg_pack_weight_bf16, dg_pack_weight_bf16_transposed, dg_workspace_bytes)
+               DG_DTYPE_FP8_E4M3, dg_pack_weight_bf16, dg_pack_weight_bf16_transposed, dg_pack_weight_fp8,
+               dg_workspace_bytes)
 
 
 def stream_handle(stream: torch.cuda.Stream | None = None) -> int:
@@ -23,13 +24,14 @@ def stream_handle(stream: torch.cuda.Stream | None = None) -> int:
     return s.cuda_stream
 
 
+_DTYPE = {"f32": DG_DTYPE_F32, "bf16": DG_DTYPE_BF16, "fp8": DG_DTYPE_FP8_E4M3}
+
+
 def model_config(shape: ModelShape) -> ModelConfig:
-    if shape.expert_dtype != shape.dtype or shape.lm_dtype != shape.dtype:
-        raise NotImplementedError("mixed weight dtypes are not supported by this library build")
     return ModelConfig(shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.d_head,
                        shape.n_experts, shape.top_k, shape.d_expert, shape.d_shared, shape.vocab,
-                       shape.d_selfcond, DG_DTYPE_BF16 if shape.dtype == "bf16" else DG_DTYPE_F32,
-                       shape.rope_base, shape.norm_eps)
+                       shape.d_selfcond, _DTYPE[shape.dtype], shape.rope_base, shape.norm_eps,
+                       _DTYPE[shape.expert_dtype], _DTYPE[shape.lm_dtype])
 
 
 def _tdtype(shape: ModelShape):
@@ -53,7 +55,22 @@ class DeviceModel:
             biggest = max(shape.vocab * d, shape.n_experts * shape.d_expert * d, shape.qkv_rows * d)
             tmp = torch.empty(biggest, dtype=torch.bfloat16, device=self.device)
 
-        def fill(name, tid, rows, cols, groups=1, pack=True, keep_plain=False):
+        def fill8(name, tid, rows, cols, groups=1):
+            # fp8: per-output-row scales and E4M3 codes, packed to the fp8 layout
+            n = groups * rows * cols
+            codes = tmp.view(torch.uint8)[:n]
+            sc = torch.empty(groups * rows, dtype=torch.float32, device=self.device)
+            synth.dev_e4m3_rows(codes.data_ptr(), sc.data_ptr(), groups * rows, cols, shape.weight_seed, tid,
+                                shape.weight_std, st)
+            t = torch.empty(n, dtype=torch.uint8, device=self.device)
+            dg_pack_weight_fp8(t.data_ptr(), codes.data_ptr(), groups * rows, cols, st)
+            self.tensors[name] = t
+            self.tensors[name + "_scale"] = sc
+            return t
+
+        def fill(name, tid, rows, cols, groups=1, pack=True, keep_plain=False, fp8=False):
+            if fp8:
+                return fill8(name, tid, rows, cols, groups)
             n = groups * rows * cols
             if not self.bf:
                 t = torch.empty(n, dtype=torch.float32, device=self.device)
@@ -91,7 +108,7 @@ class DeviceModel:
                 synth.dev_normal_f32_transposed(et.data_ptr(), shape.vocab, d, shape.weight_seed,
                                                 synth.TID["embed"], shape.weight_std, st)
             self.tensors["embed_t"] = et
-        fill("lm_head", synth.TID["lm_head"], shape.vocab, d)
+        fill("lm_head", synth.TID["lm_head"], shape.vocab, d, fp8=shape.lm_dtype == "fp8")
         fill("sc_up", synth.TID["sc_up"], shape.d_selfcond, d)
         fill("sc_down", synth.TID["sc_down"], d, shape.d_selfcond)
         self.layer_structs = (LayerWeights * shape.n_layers)()
@@ -100,21 +117,25 @@ class DeviceModel:
             lt["wqkv"] = fill(f"L{l}.wqkv", synth.layer_tid(l, "wqkv"), shape.qkv_rows, d)
             lt["wo"] = fill(f"L{l}.wo", synth.layer_tid(l, "wo"), d, shape.q_dim)
             lt["wr"] = fill(f"L{l}.wr", synth.layer_tid(l, "wr"), E, d)
-            lt["sh_g"] = fill(f"L{l}.sh_g", synth.layer_tid(l, "sh_g"), shape.d_shared, d)
-            lt["sh_u"] = fill(f"L{l}.sh_u", synth.layer_tid(l, "sh_u"), shape.d_shared, d)
-            lt["sh_d"] = fill(f"L{l}.sh_d", synth.layer_tid(l, "sh_d"), d, shape.d_shared)
-            lt["ex_g"] = fill(f"L{l}.ex_g", synth.layer_tid(l, "ex_g"), shape.d_expert, d, groups=E)
-            lt["ex_u"] = fill(f"L{l}.ex_u", synth.layer_tid(l, "ex_u"), shape.d_expert, d, groups=E)
-            lt["ex_d"] = fill(f"L{l}.ex_d", synth.layer_tid(l, "ex_d"), d, shape.d_expert, groups=E)
+            x8 = shape.expert_dtype == "fp8"
+            lt["sh_g"] = fill(f"L{l}.sh_g", synth.layer_tid(l, "sh_g"), shape.d_shared, d, fp8=x8)
+            lt["sh_u"] = fill(f"L{l}.sh_u", synth.layer_tid(l, "sh_u"), shape.d_shared, d, fp8=x8)
+            lt["sh_d"] = fill(f"L{l}.sh_d", synth.layer_tid(l, "sh_d"), d, shape.d_shared, fp8=x8)
+            lt["ex_g"] = fill(f"L{l}.ex_g", synth.layer_tid(l, "ex_g"), shape.d_expert, d, groups=E, fp8=x8)
+            lt["ex_u"] = fill(f"L{l}.ex_u", synth.layer_tid(l, "ex_u"), shape.d_expert, d, groups=E, fp8=x8)
+            lt["ex_d"] = fill(f"L{l}.ex_d", synth.layer_tid(l, "ex_d"), d, shape.d_expert, groups=E, fp8=x8)
             ls = self.layer_structs[l]
             for k, v in lt.items():
                 setattr(ls, k, v.data_ptr())
+                if x8 and k in ("sh_g", "sh_u", "sh_d", "ex_g", "ex_u", "ex_d"):
+                    setattr(ls, k + "_scale", self.tensors[f"L{l}.{k}_scale"].data_ptr())
         del tmp
         tn = self.tensors
         self.weights = Weights(tn["embed"].data_ptr(),
                                tn["embed_t"].data_ptr() if tn.get("embed_t") is not None else None,
                                tn["lm_head"].data_ptr(), tn["sc_up"].data_ptr(), tn["sc_down"].data_ptr(),
-                               ctypes.cast(self.layer_structs, ctypes.POINTER(LayerWeights)), float(lm_scale))
+                               ctypes.cast(self.layer_structs, ctypes.POINTER(LayerWeights)), float(lm_scale),
+                               tn["lm_head_scale"].data_ptr() if shape.lm_dtype == "fp8" else None)
         torch.cuda.synchronize()
 
     def set_lm_scale(self, s: float):

@@ -48,6 +48,7 @@ extern "C" {
 
 #define DG_DTYPE_F32 0
 #define DG_DTYPE_BF16 1
+#define DG_DTYPE_FP8_E4M3 2 /* weights only: OCP E4M3 codes with per-output-feature fp32 scales */
 
 /* canvas.flags bits (device side) */
 #define DG_FLAG_NONFINITE 1u /* some entropy of the step was NaN or infinite */
@@ -59,23 +60,34 @@ extern "C" {
  * d_shared % d_expert == 0, vocab % 256 == 0; bf16 models also need
  * d_head == 256, n_q/n_kv in {1, 2, 4}, d_model, d_expert, d_shared,
  * d_selfcond and n_q_heads*d_head multiples of 64, n_experts % 16 == 0.
- * Otherwise DG_ERR_UNSUPPORTED. */
+ * expert_dtype (routed and shared expert matrices) and lm_dtype (LM head)
+ * equal dtype, or are DG_DTYPE_FP8_E4M3 in a bf16 model: each stored weight
+ * is then an OCP E4M3 code whose value, times the fp32 scale of its output
+ * feature, is the weight (dequantised exactly to bf16 inside the kernels,
+ * bf16 MFMA, the scale applied to the fp32 sum); fp8 experts need
+ * d_model % 128 == 0.  Otherwise DG_ERR_UNSUPPORTED. */
 typedef struct dg_model_config {
   int32_t n_layers, d_model, n_q_heads, n_kv_heads, d_head;
   int32_t n_experts, top_k, d_expert, d_shared, vocab, d_selfcond;
   int32_t dtype;
   float rope_base; /* RoPE base (RoFormer pairing (2j, 2j+1)) */
   float norm_eps;  /* RMSNorm epsilon; gain 1 */
+  int32_t expert_dtype, lm_dtype;
 } dg_model_config;
 
 /* Weights of one layer, device pointers, each in the weight layout of its
- * logical [out][in] matrix (bf16) or plain row-major (fp32):
+ * logical [out][in] matrix (bf16, or fp8 codes packed by dg_pack_weight_fp8)
+ * or plain row-major (fp32):
  *   wqkv [(n_q + 2 n_kv) d_head][d_model]  rows: q heads, then k heads, then v heads
  *   wo   [d_model][n_q d_head]
  *   wr   [n_experts][d_model]              router
  *   sh_g, sh_u [d_shared][d_model]; sh_d [d_model][d_shared]   shared expert (GeGLU)
  *   ex_g, ex_u [n_experts][d_expert][d_model]; ex_d [n_experts][d_model][d_expert]
- *     (each expert's matrix packed separately, experts back to back) */
+ *     (each expert's matrix packed separately, experts back to back)
+ * fp8 experts: per-output-feature fp32 scales ex_g_scale, ex_u_scale
+ * [n_experts][d_expert], ex_d_scale [n_experts][d_model], sh_g_scale,
+ * sh_u_scale [d_shared], sh_d_scale [d_model] (16-byte aligned); NULL
+ * otherwise. */
 typedef struct dg_layer_weights {
   const void* wqkv;
   const void* wo;
@@ -86,6 +98,12 @@ typedef struct dg_layer_weights {
   const void* ex_g;
   const void* ex_u;
   const void* ex_d;
+  const float* ex_g_scale;
+  const float* ex_u_scale;
+  const float* ex_d_scale;
+  const float* sh_g_scale;
+  const float* sh_u_scale;
+  const float* sh_d_scale;
 } dg_layer_weights;
 
 typedef struct dg_weights {
@@ -97,6 +115,7 @@ typedef struct dg_weights {
   const void* sc_down; /* [d_model][d_selfcond] */
   const dg_layer_weights* layers; /* HOST array of n_layers */
   float lm_scale;      /* logits z = lm_scale * (RMSNorm(x) W_lm^T) */
+  const float* lm_head_scale; /* fp8 LM head: [vocab] fp32 per-id scales (16-byte aligned); else NULL */
 } dg_weights;
 
 /* KV cache, rows [0, length) valid:
@@ -185,6 +204,12 @@ int dg_pack_weight_bf16(void* d_dst, const void* d_src, int64_t rows, int64_t co
  * given: d_src is row-major [cols][rows] (e.g. the embedding [vocab][d_model]
  * packed as E^T [d_model][vocab] for the self-conditioning contraction). */
 int dg_pack_weight_bf16_transposed(void* d_dst, const void* d_src, int64_t rows, int64_t cols, void* stream);
+
+/* Pack logical row-major E4M3 codes [rows][cols] (device, one byte each)
+ * into the fp8 weight layout: 16-row x 32-column tiles of 512 B, tile
+ * (r/16, c/32) at byte ((r/16)*(cols/32) + c/32)*512, code (r, c) inside it
+ * at (((c%32)/8)*16 + r%16)*8 + c%8.  rows % 16 == 0, cols % 32 == 0. */
+int dg_pack_weight_fp8(void* d_dst, const void* d_src, int64_t rows, int64_t cols, void* stream);
 
 /* Fill canvas->tokens with uniform noise for `block` (Philox stream 0).
  * (euno.news, "what DiffusionGemma does": a canvas starts as random tokens;

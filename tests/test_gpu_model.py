@@ -7,13 +7,23 @@ import synth
 from oracle import model as om
 from oracle import sampler as smp
 from oracle import step as ost
+from dataclasses import replace
+
 from synth.configs import MINI_BF16, TINY, WORKLOADS
+
+# the small bf16 shape with fp8 expert and LM-head weights
+MINI_FP8 = replace(MINI_BF16, expert_dtype="fp8", lm_dtype="fp8")
 
 from .gpu_util import allclose_report, compare_decisions, say
 
 pytestmark = pytest.mark.gpu
 
 ATOL, RTOL = 2e-2, 1e-2  # logits bar (bf16); fp32 models are held to the same bar and print their error
+ATOL_FP8 = 3e-2          # logits bar with fp8 expert / LM-head weights
+
+
+def atol_for(shape):
+    return ATOL_FP8 if "fp8" in (shape.expert_dtype, shape.lm_dtype) else ATOL
 
 
 @pytest.fixture(scope="module")
@@ -32,6 +42,7 @@ class Problem:
         torch, dg, rt = env
         self.env = env
         self.shape, self.C, self.B, self.prefix = shape, C, B, prefix
+        self.atol = atol_for(shape)
         self.lm_scale = lm_scale
         self.seeds = seeds or [17 + b for b in range(B)]
         self.cap = prefix + C + cap_extra
@@ -59,7 +70,7 @@ class Problem:
         for name, ocache in (("k", self.ocache.k), ("v", self.ocache.v)):
             got = self.cache.view(name).float().cpu().numpy()
             for l in range(self.shape.n_layers):
-                allclose_report(f"cache {name} L{l}", got[l][:, :, :rows], ocache[l][:, :, :rows], ATOL, RTOL)
+                allclose_report(f"cache {name} L{l}", got[l][:, :, :rows], ocache[l][:, :, :rows], self.atol, RTOL)
 
 
 @pytest.fixture(scope="module")
@@ -73,6 +84,13 @@ def tiny(env):
 @pytest.fixture(scope="module")
 def mini(env):
     pb = Problem(env, MINI_BF16, 6.0, 40, 48, B=2, cap_extra=48)
+    pb.encode_prefix()
+    return pb
+
+
+@pytest.fixture(scope="module")
+def mini8(env):
+    pb = Problem(env, MINI_FP8, 6.0, 40, 48, B=2, cap_extra=48)
     pb.encode_prefix()
     return pb
 
@@ -156,7 +174,7 @@ def _route_margins(shape, trace):
     return np.stack(out)
 
 
-def entropy_tolerance(z_oracle, tau):
+def entropy_tolerance(z_oracle, tau, atol=ATOL):
     """Per-row entropy bar: the pages' 1e-3 nats, or the first-order entropy
     change the logit bar allows, whichever is larger.  With a = z/tau,
     dH = -sum_v p_v (a_v - E_p[a]) da_v, so |dH| <= E_p[|a - E_p a| (2e-2 + 1e-2|z|)] / tau.
@@ -165,7 +183,7 @@ def entropy_tolerance(z_oracle, tau):
     p, _, _ = smp.row_statistics(z_oracle, tau)
     a = z_oracle / tau
     abar = (p * a).sum(-1, keepdims=True)
-    prop = (p * np.abs(a - abar) * (ATOL + RTOL * np.abs(z_oracle))).sum(-1) / tau
+    prop = (p * np.abs(a - abar) * (atol + RTOL * np.abs(z_oracle))).sum(-1) / tau
     return np.maximum(1e-3, prop)
 
 
@@ -173,13 +191,13 @@ def _forced_ids(trace):
     return np.stack(trace["expert_ids"])  # [layers][T][k]
 
 
-@pytest.mark.parametrize("which", ["tiny", "mini"])
+@pytest.mark.parametrize("which", ["tiny", "mini", "mini8"])
 def test_encode_cache_matches_oracle(which, request):
     pb = request.getfixturevalue(which)
     pb.compare_cache(pb.prefix)
 
 
-@pytest.mark.parametrize("which", ["tiny", "mini"])
+@pytest.mark.parametrize("which", ["tiny", "mini", "mini8"])
 def test_forward_logits_match_oracle(which, request):
     pb = request.getfixturevalue(which)
     torch, dg, rt = pb.env
@@ -205,9 +223,9 @@ def test_forward_logits_match_oracle(which, request):
     _, Hg, _ = smp.row_statistics(z.reshape(-1, pb.shape.vocab), smp.temperature(0, 48))
     _, Ho, _ = smp.row_statistics(zo.reshape(-1, pb.shape.vocab), smp.temperature(0, 48))
     _err_summary(f"entropy {which} (oracle routes)", Hg, Ho)
-    allclose_report(f"logits {which} (oracle routes)", z, zo, ATOL, RTOL)
+    allclose_report(f"logits {which} (oracle routes)", z, zo, pb.atol, RTOL)
     allclose_report(f"entropy of logits {which} (oracle routes)", Hg, Ho,
-                    entropy_tolerance(zo.reshape(-1, pb.shape.vocab), smp.temperature(0, 48)), 0.0)
+                    entropy_tolerance(zo.reshape(-1, pb.shape.vocab), smp.temperature(0, 48), pb.atol), 0.0)
     # unforced: the first layer sees the same inputs; any route that differs
     # there must be an oracle near-tie
     zu, ru = _forward_logits(pb, 0, 48, want_router=True)
@@ -218,7 +236,7 @@ def test_forward_logits_match_oracle(which, request):
     say(f"unforced: layer-0 route flips {flips.size} (oracle margins {margins[0][flips]})")
     assert np.all(margins[0][flips] < ROUTE_EPS[pb.shape.dtype])
     du = np.abs(zu - zo).max(axis=-1).reshape(-1)
-    say(f"unforced: rows with max|dz| > {ATOL}: {int((du > ATOL).sum())} of {du.size}; max {du.max():.3e}")
+    say(f"unforced: rows with max|dz| > {pb.atol}: {int((du > pb.atol).sum())} of {du.size}; max {du.max():.3e}")
     # self-conditioning from an external distribution
     rng = np.random.default_rng(1)
     P = rng.dirichlet(np.full(pb.shape.vocab, 0.05), size=pb.B * pb.C).reshape(pb.B, pb.C, -1)
@@ -226,11 +244,11 @@ def test_forward_logits_match_oracle(which, request):
     tr2 = {}
     zo2 = ost.denoise_logits(pb.shape, pb.W, pb.ocache, tok, P.astype(np.float64), pb.lm_scale, trace=tr2)
     z2 = _forward_logits(pb, 1, 48, P, force_ids=_forced_ids(tr2))
-    allclose_report(f"logits+selfcond {which} (oracle routes)", z2, zo2, ATOL, RTOL)
+    allclose_report(f"logits+selfcond {which} (oracle routes)", z2, zo2, pb.atol, RTOL)
     assert np.abs(zo2 - zo).max() > 1e-3  # the self-conditioning term is not negligible
 
 
-@pytest.mark.parametrize("which", ["tiny", "mini"])
+@pytest.mark.parametrize("which", ["tiny", "mini", "mini8"])
 def test_denoise_loop_and_commit_match_oracle(which, request):
     """48 adaptive steps on the GPU.  Every step is checked against the
     sampler's definition (check_sampler_invariants).  The oracle runs the same
@@ -279,9 +297,9 @@ def test_denoise_loop_and_commit_match_oracle(which, request):
             ties = 0
             for b, o in enumerate(outs):
                 herr = np.abs(H[b] - o["H"])
-                tol = entropy_tolerance(z[b], o["tau"])
+                tol = entropy_tolerance(z[b], o["tau"], pb.atol)
                 assert np.all(herr <= tol), f"step {t}: entropy error {herr.max()} (bar {tol.min()})"
-                ties += compare_decisions(f"t{t} argmax", am[b], o["argmax"], o["margin_argmax"], 2 * ATOL, max_ties=2)
+                ties += compare_decisions(f"t{t} argmax", am[b], o["argmax"], o["margin_argmax"], 2 * pb.atol, max_ties=2)
                 ties += compare_decisions(f"t{t} accepted", acc[b], o["accepted"], o["margin_accept"], 2e-3,
                                           max_ties=2)
                 ties += compare_decisions(f"t{t} next tokens", gnext[b], o["next_tokens"],

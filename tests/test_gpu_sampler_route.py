@@ -42,6 +42,14 @@ def test_device_generator_matches_host(env):
     tt = torch.empty(r * c, dtype=torch.float32, device="cuda")
     synth.dev_normal_f32_transposed(tt.data_ptr(), r, c, 0, 1, 0.02, st)
     assert np.array_equal(tt.cpu().numpy().reshape(c, r), synth.normal(0, 1, (r, c), 0.02, "f32").T)
+    # fp8 weight recipe: per-row scales and E4M3 codes
+    r, c = 4096, 704
+    codes = torch.empty(r * c, dtype=torch.uint8, device="cuda")
+    sc = torch.empty(r, dtype=torch.float32, device="cuda")
+    synth.dev_e4m3_rows(codes.data_ptr(), sc.data_ptr(), r, c, 0, synth.layer_tid(0, "ex_d"), 0.02, st)
+    hc, hs = synth.e4m3_rows(0, synth.layer_tid(0, "ex_d"), r, c, 0.02)
+    assert np.array_equal(sc.cpu().numpy(), hs)
+    assert np.array_equal(codes.cpu().numpy().reshape(r, c), hc)
 
 
 def test_pack_layout_matches_header_definition(env):
@@ -62,6 +70,16 @@ def test_pack_layout_matches_header_definition(env):
     d_srct = torch.from_numpy(np.ascontiguousarray(src.T).view(np.int16).reshape(-1)).cuda()
     dg.dg_pack_weight_bf16_transposed(d_dst.data_ptr(), d_srct.data_ptr(), rows, cols, rt.stream_handle())
     assert np.array_equal(d_dst.cpu().numpy().view(np.uint16), want)
+    # fp8 layout: 16 x 32 tiles of 512 bytes
+    src8 = rng.integers(0, 256, size=(rows, cols), dtype=np.uint8)
+    want8 = np.empty(rows * cols, dtype=np.uint8)
+    for r in range(rows):
+        for c in range(cols):
+            want8[((r // 16) * (cols // 32) + c // 32) * 512 + (((c % 32) // 8) * 16 + r % 16) * 8 + c % 8] = src8[r, c]
+    d8 = torch.from_numpy(src8.reshape(-1)).cuda()
+    o8 = torch.empty_like(d8)
+    dg.dg_pack_weight_fp8(o8.data_ptr(), d8.data_ptr(), rows, cols, rt.stream_handle())
+    assert np.array_equal(o8.cpu().numpy(), want8)
 
 
 def _canvas(env, shape, B, C, seeds, selfcond=False):

@@ -48,6 +48,15 @@ def test_workspace_and_config_checks(dg):
     bad = model_config(MINI_BF16)
     bad.d_head = 128  # bf16 path needs d_head 256
     assert dg.dg_workspace_bytes(bad, 1, 256) == 0
+    # fp8 expert / LM-head weights: bf16 models only; fp8 experts need d_model % 128
+    from dataclasses import replace
+    from synth.configs import FULL_LAYER_FP8
+    assert dg.dg_workspace_bytes(model_config(FULL_LAYER_FP8), 4, 256) > 0
+    assert dg.dg_workspace_bytes(model_config(replace(TINY, expert_dtype="fp8")), 1, 32) == 0
+    odd = model_config(replace(MINI_BF16, expert_dtype="fp8"))
+    odd.d_model = 320
+    assert dg.dg_workspace_bytes(odd, 1, 32) == 0
+    assert dg.dg_workspace_bytes(model_config(replace(MINI_BF16, lm_dtype="fp8")), 1, 32) > 0
 
 
 def test_argument_errors_are_reported_before_launch(dg):
