@@ -9,8 +9,10 @@ of the canvas).  value = canvas tokens / second over the timed steps.
 Also reported: the denoising-step latency, canvas tok/s at 12 and 48 steps
 with and without the commit, a per-phase GPU time breakdown (HIP events),
 the roofline of the dominant kernel (the routed + shared expert gate/up GEMM,
-timed with HIP events on its launch stream over the timed region), and the
-CPU oracle timed on a bounded sample of the same workload.
+timed with HIP events on its launch stream over the timed region), the LM
+head's MFMA roofline timed the same way, the accepted tokens per step of a
+12-step canvas, and the CPU oracle timed on a bounded sample of the same
+workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--n-steps N]
 """
@@ -194,6 +196,7 @@ def main():
     print(f"[bench] prefill {wl.prefix} tokens: {prefill_ms:.1f} ms", file=sys.stderr, flush=True)
 
     MASK_UP = 1 << 6
+    MASK_LM = 1 << 9
 
     def canvas_pass(n_steps, trace=None, commit=True):
         dg.dg_init_canvas(cfg, canvas.struct, 0, st)
@@ -208,8 +211,8 @@ def main():
     for _ in range(args.warmup):
         canvas_pass(args.n_steps)
     torch.cuda.synchronize()
-    pool = EventPool(hip, 2 * shape.n_layers * args.n_steps * args.steps + 8)
-    tr = pool.trace(dg, MASK_UP)
+    pool = EventPool(hip, 2 * (shape.n_layers + 1) * args.n_steps * args.steps + 8)
+    tr = pool.trace(dg, MASK_UP | MASK_LM)
     torch.cuda.synchronize()
     s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s0.record()
@@ -219,8 +222,11 @@ def main():
     torch.cuda.synchronize()
     total_ms = s0.elapsed_time(s1)
     ms_per_canvas = total_ms / args.steps
-    up = [ms for ph, ms in pool.durations(tr) if ph == 6]
+    durs = pool.durations(tr)
+    up = [ms for ph, ms in durs if ph == 6]
     up_ms = sum(up) / len(up)
+    lmh = [ms for ph, ms in durs if ph == 9]
+    lm_ms = sum(lmh) / len(lmh)
 
     # denoising-step latency and commit separately; 48-step canvas
     d0, d1, d2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
@@ -259,8 +265,18 @@ def main():
         breakdown = {k: round(v, 4) for k, v in breakdown.items()}
 
     n_acc = int(canvas.n_accepted.sum().item())
+    # accepted tokens per step of one 12-step canvas (untimed)
+    acc_steps = []
+    dg.dg_init_canvas(cfg, canvas.struct, 0, st)
+    for t in range(args.n_steps):
+        dg.dg_denoise_step(cfg, model.weights, cache.struct, canvas.struct, rt.step_params(t, args.n_steps, 0, False),
+                           ws.ptr, ws.size, st)
+        acc_steps.append(int(canvas.n_accepted.sum().item()))
     up_bytes = moe_up_bytes(shape, T)
     achieved = up_bytes / (up_ms * 1e-3) / 1e9
+    lm_flops = 2.0 * T * shape.vocab * shape.d_model
+    lm_tflops = lm_flops / (lm_ms * 1e-3) / 1e12
+    lm_bytes = shape.vocab * shape.d_model * (1 if shape.lm_dtype == "fp8" else 2)
     value = T / (ms_per_canvas * 1e-3)
     out = {
         "metric": "canvas tok/s at batch 1 (256-tok canvas, 12 & 48 steps) + step ms; % roofline",
@@ -289,9 +305,11 @@ def main():
         "canvas_tok_s_48_incl_commit": round(T / (ms48 * 1e-3), 2),
         "canvas_tok_s_48_excl_commit": round(T / ((ms48 - commit_ms) * 1e-3), 2),
         "accepted_last_step": n_acc,
+        "accepted_per_step": acc_steps,
+        "accepted_mean": round(sum(acc_steps) / len(acc_steps), 2),
         "phase_ms_one_step": breakdown,
         "roofline": {
-            "kernel": "routed+shared expert gate/up GEMM (k_wsgemm<32,1,64,GeGLU>)",
+            "kernel": "routed+shared expert gate/up GEMM (k_wsgemm<32,1,128,GeGLU>)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
@@ -301,6 +319,19 @@ def main():
             "algorithmic_bytes_per_launch": up_bytes,
             "avg_launch_ms": round(up_ms, 5),
             "launches_timed": len(up),
+        },
+        "roofline_lmhead": {
+            "kernel": "fused LM head + sampler statistics (k_rowgemm<lmhead>)",
+            "bound": "mfma",
+            "achieved": round(lm_tflops, 1),
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(lm_tflops / BF16_PEAK_TFLOPS, 4),
+            "algorithmic_flops_per_launch": lm_flops,
+            "weight_bytes_per_launch": lm_bytes,
+            "weight_gbs": round(lm_bytes / (lm_ms * 1e-3) / 1e9, 1),
+            "avg_launch_ms": round(lm_ms, 5),
+            "launches_timed": len(lmh),
         },
     }
     if not args.no_cpu_baseline:

@@ -99,7 +99,7 @@ Plan make_plan(const Shape& s, int batch, int max_canvas) {
   p.att_o = take((size_t)p.att_rows * s.nq * s.dh * 4);
   p.att_ml = take((size_t)p.att_rows * s.nq * 8);
   p.o_part = take(8 * T * s.d * 4);
-  p.r_part = take(8 * T * s.E * 4);
+  p.r_part = take(16 * T * s.E * 4);  // router K-split partials (up to 16)
   p.ids = take(T * s.k * 4);
   p.wts = take(T * s.k * 4);
   p.row_token = take(rows_moe * 4);
@@ -170,6 +170,9 @@ constexpr int kTargetBlocks = 1024;
 // non-store epilogues use at most kRowPartRows rows x N of workspace.
 constexpr int kRowTargetBlocks = 256;
 constexpr int kRowMaxSplit = 16;
+// Non-store epilogues: K splits limited so the fp32 partials stay within this
+// many bytes (writing and re-reading them costs more than the extra CUs gain).
+constexpr int64_t kRowPartBytes = 32ll << 20;
 
 int pick_split(int blocks_per_split, int K, int kc, int max_split) {
   int sp = std::max(1, std::min(max_split, (kTargetBlocks + blocks_per_split - 1) / std::max(1, blocks_per_split)));
@@ -201,7 +204,8 @@ int dense_gemm(const Ctx& c, GemmArgs a, int M, int N, int K, int max_split, int
     a.n_fb = (N + 255) / 256;
     const bool store = a.epi == EPI_STORE_F32;
     // non-store epilogues: the partials must fit the split-epilogue buffer
-    const int64_t part_cap = (int64_t)kRowPartRows * std::max(c.s.qkv, c.s.dsc) / ((int64_t)M * N);
+    const int64_t part_cap = std::min<int64_t>((int64_t)kRowPartRows * std::max(c.s.qkv, c.s.dsc),
+                                               kRowPartBytes / 4) / ((int64_t)M * N);
     const int cap = store ? max_split : (int)std::min<int64_t>(kRowMaxSplit, part_cap);
     const int sp = row_split(M, N, K, std::max(1, cap));
     a.k_split = ((K / 64 + sp - 1) / sp) * 64;
@@ -310,7 +314,7 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
       a.act = xn; a.act_ld = s.d; a.act_kind = bf ? ACT_BF16 : ACT_F32;
       a.w0 = lw.wr;
       a.epi = EPI_STORE_F32; a.out_f32 = c.at<float>(c.p.r_part); a.ldo = s.E; a.split_stride = (int64_t)T * s.E;
-      DG_TRY(dense_gemm(c, a, T, s.E, s.d, 8, &r_split));
+      DG_TRY(dense_gemm(c, a, T, s.E, s.d, 16, &r_split));
       const int32_t* forced = c.force_ids ? c.force_ids + (int64_t)l * T * s.k : nullptr;
       float* r_out = c.router_out ? c.router_out + (int64_t)l * T * s.E : nullptr;
       DG_TRY(launch_topk(c.at<float>(c.p.r_part), r_split, (int64_t)T * s.E, T, s.E, s.k, forced,

@@ -116,6 +116,105 @@ __global__ __launch_bounds__(256) void k_combine_norm(float* x, const float* Y, 
   write_norm<TA>(xr, n + t * d, d, eps, red);
 }
 
+// Wide forms for d % 4 == 0 and d <= 4096: 1024 threads per row, one float4
+// of the row per thread held in registers from the residual update to the
+// norm, every load of a thread issued before the first add.
+__device__ __forceinline__ float block_sum1024(float v, float* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) t += red[w];
+  return t;
+}
+
+template <typename TA>
+__device__ __forceinline__ void write_norm4(float* xr, TA* nr, int i, bool on, float4 v, float eps, int d,
+                                            float* red) {
+  const float ss = on ? ((v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w)) : 0.f;
+  const float tot = block_sum1024(ss, red);
+  if (!on) return;
+  *reinterpret_cast<float4*>(xr + i) = v;
+  const float inv = 1.0f / sqrtf(tot / (float)d + eps);
+  if constexpr (sizeof(TA) == 2) {
+    const uint32_t lo = (uint32_t)f2bf(v.x * inv) | ((uint32_t)f2bf(v.y * inv) << 16);
+    const uint32_t hi = (uint32_t)f2bf(v.z * inv) | ((uint32_t)f2bf(v.w * inv) << 16);
+    *reinterpret_cast<uint2*>(nr + i) = make_uint2(lo, hi);
+  } else {
+    *reinterpret_cast<float4*>(nr + i) = make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
+  }
+}
+
+template <typename TA>
+__global__ __launch_bounds__(1024) void k_resid_norm4(float* x, const float* part, int n_split, int64_t split_stride,
+                                                     TA* n, int d, float eps) {
+  __shared__ float red[16];
+  const int64_t t = blockIdx.x;
+  const int i = threadIdx.x * 4;
+  const bool on = i < d;
+  float* xr = x + t * d;
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (on) {
+    constexpr int kMaxS = 16;
+    float4 p[kMaxS];
+#pragma unroll
+    for (int s = 0; s < kMaxS; ++s)
+      p[s] = s < n_split ? *reinterpret_cast<const float4*>(part + (int64_t)s * split_stride + t * d + i)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 acc = p[0];
+#pragma unroll
+    for (int s = 1; s < kMaxS; ++s) {
+      acc.x += p[s].x; acc.y += p[s].y; acc.z += p[s].z; acc.w += p[s].w;
+    }
+    v = *reinterpret_cast<const float4*>(xr + i);
+    v.x += acc.x; v.y += acc.y; v.z += acc.z; v.w += acc.w;
+  }
+  write_norm4<TA>(xr, n + t * d, i, on, v, eps, d, red);
+}
+
+template <typename TA>
+__global__ __launch_bounds__(1024) void k_combine_norm4(float* x, const float* Y, const int32_t* inv, const float* w,
+                                                       int T, int k, int n_sh, TA* n, int d, float eps) {
+  __shared__ float red[16];
+  const int64_t t = blockIdx.x;
+  const int i = threadIdx.x * 4;
+  const bool on = i < d;
+  float* xr = x + t * d;
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (on) {
+    constexpr int kMaxK = 16, kMaxSh = 8;
+    const int64_t sh0 = (int64_t)T * k;
+    float4 ys[kMaxSh], yr[kMaxK];
+    float wj[kMaxK];
+#pragma unroll
+    for (int c = 0; c < kMaxSh; ++c)
+      ys[c] = c < n_sh ? *reinterpret_cast<const float4*>(Y + (sh0 + (int64_t)c * T + t) * d + i)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      wj[j] = j < k ? w[t * k + j] : 0.f;
+      yr[j] = j < k ? *reinterpret_cast<const float4*>(Y + (int64_t)inv[t * k + j] * d + i)
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    // shared-expert slices in slice order, then the routed outputs in rank order
+    float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int c = 0; c < kMaxSh; ++c)
+      if (c < n_sh) { y.x += ys[c].x; y.y += ys[c].y; y.z += ys[c].z; y.w += ys[c].w; }
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if (j < k) {
+        y.x = fmaf(wj[j], yr[j].x, y.x); y.y = fmaf(wj[j], yr[j].y, y.y);
+        y.z = fmaf(wj[j], yr[j].z, y.z); y.w = fmaf(wj[j], yr[j].w, y.w);
+      }
+    v = *reinterpret_cast<const float4*>(xr + i);
+    v.x += y.x; v.y += y.y; v.z += y.z; v.w += y.w;
+  }
+  write_norm4<TA>(xr, n + t * d, i, on, v, eps, d, red);
+}
+
 // out[t][i] = act(sum_s part[s][t][i]) (split order).
 template <typename TA>
 __global__ __launch_bounds__(256) void k_reduce_splits(const float* part, int n_split, int64_t split_stride,
@@ -168,6 +267,15 @@ int launch_embed_norm(int dtype, const int32_t* tok, const void* emb, const floa
 int launch_resid_norm(int dtype, float* x, const float* part, int n_split, int64_t split_stride, void* n, int T, int d,
                       float eps, hipStream_t s) {
   if (n_split < 1 || n_split > 16) return -1;
+  if (d % 4 == 0 && d <= 4096 && split_stride % 4 == 0) {
+    if (dtype == 1)
+      hipLaunchKernelGGL(k_resid_norm4<bf16_t>, dim3(T), dim3(1024), 0, s, x, part, n_split, split_stride, (bf16_t*)n, d,
+                         eps);
+    else
+      hipLaunchKernelGGL(k_resid_norm4<float>, dim3(T), dim3(1024), 0, s, x, part, n_split, split_stride, (float*)n, d,
+                         eps);
+    return DG_OK_OR_HIP();
+  }
   if (dtype == 1)
     hipLaunchKernelGGL(k_resid_norm<bf16_t>, dim3(T), dim3(256), 0, s, x, part, n_split, split_stride, (bf16_t*)n, d, eps);
   else
@@ -178,6 +286,13 @@ int launch_resid_norm(int dtype, float* x, const float* part, int n_split, int64
 int launch_combine_norm(int dtype, float* x, const float* Y, const int32_t* inv, const float* w, int T, int k, int n_sh,
                         void* n, int d, float eps, hipStream_t s) {
   if (k > 16) return -1;
+  if (d % 4 == 0 && d <= 4096 && n_sh <= 8) {
+    if (dtype == 1)
+      hipLaunchKernelGGL(k_combine_norm4<bf16_t>, dim3(T), dim3(1024), 0, s, x, Y, inv, w, T, k, n_sh, (bf16_t*)n, d, eps);
+    else
+      hipLaunchKernelGGL(k_combine_norm4<float>, dim3(T), dim3(1024), 0, s, x, Y, inv, w, T, k, n_sh, (float*)n, d, eps);
+    return DG_OK_OR_HIP();
+  }
   if (dtype == 1)
     hipLaunchKernelGGL(k_combine_norm<bf16_t>, dim3(T), dim3(256), 0, s, x, Y, inv, w, T, k, n_sh, (bf16_t*)n, d, eps);
   else

@@ -11,21 +11,28 @@
 namespace {
 
 // One wave per token.  Router logits arrive as `n_split` fp32 partial sums
-// [split][T][E] added in split order.
+// [split][T][E] added in split order.  Selection by rank: the wave's E logits
+// go to LDS and every lane counts, for each logit it holds, the logits that
+// beat it (larger, or equal with a lower expert id); rank < k is selected at
+// that rank.  The weights are the softmax over the k selected logits, summed
+// in rank order.
 __global__ __launch_bounds__(256) void k_topk(const float* part, int n_split, int64_t split_stride, int T, int E,
                                               int k, const int32_t* forced, int32_t* ids, float* w,
                                               float* r_out) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (t >= T) return;
+  __shared__ float lg[4][256];
+  __shared__ float sv[4][16];
+  __shared__ int se[4][16];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  const bool live = t < T;
   constexpr int kMaxPerLane = 4;  // E <= 256
-  constexpr int kMaxSplit = 8;    // partial sums are added in split order
+  constexpr int kMaxSplit = 16;   // partial sums are added in split order
   float r[kMaxPerLane];
 #pragma unroll
   for (int q = 0; q < kMaxPerLane; ++q) {
     const int e = lane + q * 64;
     float v = -INFINITY;
-    if (e < E) {
+    if (live && e < E) {
       float ps[kMaxSplit];
 #pragma unroll
       for (int s = 0; s < kMaxSplit; ++s)
@@ -33,74 +40,51 @@ __global__ __launch_bounds__(256) void k_topk(const float* part, int n_split, in
       v = ps[0];
 #pragma unroll
       for (int s = 1; s < kMaxSplit; ++s) v += ps[s];
+      if (r_out) r_out[(int64_t)t * E + e] = v;
     }
     r[q] = v;
-    if (r_out && e < E) r_out[(int64_t)t * E + e] = v;
+    if (e < 256) lg[wave][e] = v;
   }
-  float sel_v[16];
-  int sel_e[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    sel_v[j] = -INFINITY;
-    sel_e[j] = 0;
+  // defaults keep every id in range should non-finite logits leave a rank empty
+  if (lane < 16) {
+    sv[wave][lane] = -INFINITY;
+    se[wave][lane] = 0;
   }
+  __syncthreads();
+  if (!live) return;
   if (forced) {
     // test path: the caller fixes the k experts (in rank order); weights still
     // come from this token's router logits
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (j >= k) break;
-      int e = forced[t * k + j];
+    if (lane < k) {
+      int e = forced[t * k + lane];
       if (e < 0 || e >= E) e = 0;  // keep the grouped GEMMs in bounds on bad test input
-      const int q = e >> 6;
-      float mine = r[0];
-#pragma unroll
-      for (int qq = 1; qq < kMaxPerLane; ++qq)
-        if (qq == q) mine = r[qq];
-      sel_v[j] = __shfl(mine, e & 63, 64);
-      sel_e[j] = e;
+      sv[wave][lane] = lg[wave][e];
+      se[wave][lane] = e;
     }
-  }
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    if (forced || j >= k) break;
-    float bv = -INFINITY;
-    int be = 0x7FFFFFFF;
+  } else {
 #pragma unroll
     for (int q = 0; q < kMaxPerLane; ++q) {
       const int e = lane + q * 64;
-      if (e < E && (r[q] > bv || (r[q] == bv && e < be))) { bv = r[q]; be = e; }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oe = __shfl_xor(be, o, 64);
-      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-    }
-    sel_v[j] = bv;
-    sel_e[j] = be;
-#pragma unroll
-    for (int q = 0; q < kMaxPerLane; ++q)
-      if (lane + q * 64 == be) r[q] = -INFINITY;  // taken
-  }
-  if (lane == 0) {
-    float m = sel_v[0];
-#pragma unroll
-    for (int j = 1; j < 16; ++j)
-      if (j < k) m = fmaxf(m, sel_v[j]);
-    float ex[16];
-    float den = 0.f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      ex[j] = j < k ? expf(sel_v[j] - m) : 0.f;
-      den += ex[j];
-    }
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (j < k) {
-        ids[t * k + j] = sel_e[j];
-        w[t * k + j] = ex[j] / den;
+      if (e >= E) continue;
+      const float v = r[q];
+      int rank = 0;
+      for (int o = 0; o < E; ++o) {
+        const float u = lg[wave][o];
+        rank += (u > v || (u == v && o < e)) ? 1 : 0;
       }
+      if (rank < k) {
+        sv[wave][rank] = v;
+        se[wave][rank] = e;
+      }
+    }
+  }
+  __syncthreads();
+  if (lane < k) {
+    const float m = sv[wave][0];
+    float den = 0.f;
+    for (int j = 0; j < k; ++j) den += expf(sv[wave][j] - m);
+    ids[t * k + lane] = se[wave][lane];
+    w[t * k + lane] = expf(sv[wave][lane] - m) / den;
   }
 }
 
@@ -140,17 +124,37 @@ __global__ __launch_bounds__(1024) void k_route_sort(const int32_t* ids, int T, 
     cnt[e] = run;
   }
   __syncthreads();
-  if (tid == 0) {
-    int o = 0, tf = 0;
-    for (int e = 0; e < E; ++e) {
-      off[e] = o;
-      toff[e] = tf;
-      o += cnt[e];
-      tf += (cnt[e] + bm - 1) / bm;
+  // exclusive prefix sums of the segment sizes and tile counts over the
+  // experts: first wave, four experts per lane
+  if (tid < 64) {
+    int c4[4], t4[4], cs = 0, ts = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid * 4 + q;
+      c4[q] = e < E ? cnt[e] : 0;
+      t4[q] = (c4[q] + bm - 1) / bm;
+      cs += c4[q];
+      ts += t4[q];
     }
-    off[E] = o;
-    toff[E] = tf;
-    n_tiles[0] = tf + n_sh * ((T + bm - 1) / bm);
+    int ci = cs, ti = ts;  // inclusive scans over the lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int cu = __shfl_up(ci, o, 64), tu = __shfl_up(ti, o, 64);
+      if (tid >= o) { ci += cu; ti += tu; }
+    }
+    int co = ci - cs, to = ti - ts;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid * 4 + q;
+      if (e <= E) { off[e] = co; toff[e] = to; }
+      co += c4[q];
+      to += t4[q];
+    }
+    if (tid == 63) {
+      off[E] = co;  // the totals (E = 256 has no lane for them above)
+      toff[E] = to;
+      n_tiles[0] = ti + n_sh * ((T + bm - 1) / bm);
+    }
   }
   __syncthreads();
   for (int e = tid; e <= E; e += nt) offsets[e] = off[e];
@@ -177,7 +181,7 @@ __global__ __launch_bounds__(1024) void k_route_sort(const int32_t* ids, int T, 
 
 int launch_topk(const float* part, int n_split, int64_t split_stride, int T, int E, int k, const int32_t* forced,
                 int32_t* ids, float* w, float* r_out, hipStream_t s) {
-  if (E > 256 || k > 16 || k > E || n_split < 1 || n_split > 8) return -1;
+  if (E > 256 || k > 16 || k > E || n_split < 1 || n_split > 16) return -1;
   hipLaunchKernelGGL(k_topk, dim3(DG_CEIL_DIV(T, 4)), dim3(256), 0, s, part, n_split, split_stride, T, E, k, forced, ids,
                      w, r_out);
   return hipGetLastError() == hipSuccess ? 0 : -5;

@@ -109,8 +109,10 @@ WORKLOADS = {
                        prefix_mode="random_kv", n_steps=48, adaptive=False, lm_scale=1.0,
                        selfcond_init="dirichlet", first_step=1),
     # full 30-layer model; 4096-token causal prefix; one canvas; fixed 12 / 48 and adaptive.
+    # LM-head scale 7.0: about 20 accepted tokens per step over the 12-step run
+    # (tests/golden/calibrate_lm_scale.py bisects it: 6.99 -> 19.9 per step).
     "full30": Workload("full30", FULL_30, batch=1, canvas=256, prefix=4096, n_steps=12,
-                       adaptive=False, lm_scale=1.0),
+                       adaptive=False, lm_scale=7.0),
     # long context on the one-layer model: 32768 prefix, 8 committed canvases.
     "longctx": Workload("longctx", FULL_LAYER, batch=1, canvas=256, prefix=32768, n_steps=48,
                         adaptive=True, n_blocks=8, lm_scale=1.0),
