@@ -229,3 +229,19 @@ def test_initial_canvas_stream0():
     tok = smp.initial_canvas(42, 3, 256, 262144)
     w0, _, _, _ = philox.philox4x32_10(np.arange(256), 0, 3, 0, 42, 0)
     assert (tok == (w0.astype(np.uint64) >> np.uint64(14)).astype(np.int64)).all()
+
+
+def test_full30_lm_scale_gives_about_20_accepted_per_step():
+    """The 30-layer workload's LM-head scale: with iid normal logits of
+    standard deviation s * 0.02 * sqrt(d_model) (an untied random head and a
+    unit-RMS hidden state), the oracle's acceptance rule takes about 20 tokens
+    per step on average over the 12 temperatures of the run."""
+    import os
+    import sys
+    from synth.configs import WORKLOADS
+    sys.path.insert(0, os.path.join(os.path.dirname(__file__), "golden"))
+    from calibrate_lm_scale import mean_accepted
+    wl = WORKLOADS["full30"]
+    m = mean_accepted(wl.lm_scale, d_model=wl.model.d_model, vocab=wl.model.vocab, canvas=wl.canvas,
+                      n_steps=wl.n_steps, seed=1)
+    assert 15.0 <= m <= 25.0, m
