@@ -494,13 +494,15 @@ __device__ __forceinline__ void tile_stats4(const float* z0, int64_t pitch, int 
   argmax_step(dpp_f<DPP_HALF_MIRROR>(bz), dpp_i<DPP_HALF_MIRROR>(bc));
   argmax_step(dpp_f<DPP_MIRROR>(bz), dpp_i<DPP_MIRROR>(bc));
   // a = z / tau (tau > 0, so max a = round(zmax / tau)); exp(a - m) and moments
+  // exp(d) = 2^(d log2 e) on the hardware exp2 (about 1 ulp): the epilogue is
+  // VALU-bound, and the statistics it feeds carry looser tolerances
   const float m = bz * lm.inv_tau;
   float ex[16], w[4];
   float t = 0.f;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     const float d = z[k] * lm.inv_tau - m;
-    ex[k] = expf(d);
+    ex[k] = __builtin_amdgcn_exp2f(d * 1.4426950408889634f);
     t = fmaf(ex[k], d, t);
   }
 #pragma unroll
@@ -559,9 +561,11 @@ __device__ __forceinline__ void tile_stats4(const float* z0, int64_t pitch, int 
         *reinterpret_cast<float4*>(reinterpret_cast<float*>(lm.p_side) + pidx) =
             make_float4(ex[4 * q], ex[4 * q + 1], ex[4 * q + 2], ex[4 * q + 3]);
       } else {
-        const uint32_t lo = (uint32_t)f2bf(ex[4 * q]) | ((uint32_t)f2bf(ex[4 * q + 1]) << 16);
-        const uint32_t hi = (uint32_t)f2bf(ex[4 * q + 2]) | ((uint32_t)f2bf(ex[4 * q + 3]) << 16);
-        *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(lm.p_side) + pidx) = make_uint2(lo, hi);
+        // hardware round-to-nearest-even conversion (v_cvt_pk_bf16_f32)
+        const bf16x2_t lo = {(__bf16)ex[4 * q], (__bf16)ex[4 * q + 1]};
+        const bf16x2_t hi = {(__bf16)ex[4 * q + 2], (__bf16)ex[4 * q + 3]};
+        *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(lm.p_side) + pidx) =
+            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
       }
     }
   }
@@ -688,6 +692,35 @@ __device__ __forceinline__ int rg_swz(int row) { return (row >> 1) & 3; }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// Main-loop pieces of the row-resident kernel.  A "group" is two of a wave's
+// eight 16-row tiles; its MFMAs read two B fragments.
+template <int G>
+__device__ __forceinline__ void rg_read_x(const unsigned char* st, int rh, int lane, bf16x8_t (&x)[2]) {
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    const int r = rh * 128 + (2 * G + jj) * 16 + (lane & 15);
+    x[jj] = *reinterpret_cast<const bf16x8_t*>(st + r * RG_ROW_BYTES + (((lane >> 4) ^ rg_swz(r)) << 4));
+  }
+}
+template <int NWT, bool FP8>
+__device__ __forceinline__ void rg_read_w(const unsigned char* st, int cg, int lane, bf16x8_t (&wf)[NWT]) {
+#pragma unroll
+  for (int i = 0; i < NWT; ++i) {
+    if constexpr (FP8)
+      wf[i] = fp8x8_to_bf16(*reinterpret_cast<const uint2*>(st + RG_X_BYTES + (cg * NWT + i) * 512 + lane * 8));
+    else
+      wf[i] = *reinterpret_cast<const bf16x8_t*>(st + RG_X_BYTES + (cg * NWT + i) * 1024 + lane * 16);
+  }
+}
+template <int NWT, int G>
+__device__ __forceinline__ void rg_mfma(f32x4_t (&acc)[NWT][8], const bf16x8_t (&wf)[NWT], const bf16x8_t (&x)[2]) {
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+    for (int i = 0; i < NWT; ++i)
+      acc[i][2 * G + jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[i], x[jj], acc[i][2 * G + jj], 0, 0, 0);
+}
+
 template <bool LMHEAD, bool SCALED, bool FP8>
 __global__ __launch_bounds__(RG_THREADS, 1) void k_rowgemm(GemmArgs a, LmArgs lm) {
   using C = RgCfg<LMHEAD, SCALED, FP8>;
@@ -718,7 +751,7 @@ __global__ __launch_bounds__(RG_THREADS, 1) void k_rowgemm(GemmArgs a, LmArgs lm
   if (nch <= 0) return;
 
   f32x4_t acc[NWT][MW];
-  f32x4_t accu[NWT][SCALED ? MW : 1];
+  f32x4_t accu[NWT][MW];  // scaled: raw sums of the current K tile (unused otherwise)
 #pragma unroll
   for (int i = 0; i < NWT; ++i)
 #pragma unroll
@@ -791,34 +824,43 @@ __global__ __launch_bounds__(RG_THREADS, 1) void k_rowgemm(GemmArgs a, LmArgs lm
     asm volatile("" ::: "memory");  // issue it before the chunk loads
   }
   for (int c = 0; c < RG_AHEAD; ++c) issue(c);
+  // Own loads of a chunk done, then a plain barrier: every wave's part of the
+  // stage is in LDS.  No fence: it would wait for the loads still in flight;
+  // the asm memory clobber keeps the compiler from moving LDS accesses across.
+  // Operand reads run one group ahead of the MFMAs, and the wait + barrier
+  // for chunk c + 1 come before chunk c's last group, so chunk c + 1's first
+  // reads overlap those MFMAs.  lgkmcnt(0) before that barrier: every read of
+  // chunk c has completed, so chunk c + 1 + RG_AHEAD may refill its stage.
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((RG_AHEAD - 1) * C::LOADS) : "memory");
+  issue(RG_AHEAD);
+  f32x4_t(&tgt)[NWT][MW] = SCALED ? accu : acc;
+  bf16x8_t wf[NWT], wn[NWT], xa[2], xb[2];
+  rg_read_w<NWT, FP8>(smem, cg, lane, wf);
+  rg_read_x<0>(smem, rh, lane, xa);
+  // (sched_barrier keeps the compiler from sinking each read next to its use)
   for (int c = 0; c < nch; ++c) {
-    // own loads of chunk c done, then a plain barrier: every wave's part of
-    // the stage is in LDS and every wave is done reading chunk c - 1 (its
-    // MFMAs consumed those reads), so that stage can be refilled.  No fence:
-    // it would wait for the loads still in flight.  The asm memory clobber
-    // keeps the compiler from moving LDS accesses across.
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((RG_AHEAD - 1) * C::LOADS) : "memory");
-    issue(c + RG_AHEAD);
     const unsigned char* st = smem + (c % RG_SLOTS) * C::STAGE;
-    bf16x8_t wf[NWT];
-#pragma unroll
-    for (int i = 0; i < NWT; ++i) {
-      if constexpr (FP8)
-        wf[i] = fp8x8_to_bf16(*reinterpret_cast<const uint2*>(st + RG_X_BYTES + (cg * NWT + i) * 512 + lane * 8));
-      else
-        wf[i] = *reinterpret_cast<const bf16x8_t*>(st + RG_X_BYTES + (cg * NWT + i) * 1024 + lane * 16);
+    rg_read_x<1>(st, rh, lane, xb);
+    __builtin_amdgcn_sched_barrier(0);
+    rg_mfma<NWT, 0>(tgt, wf, xa);
+    rg_read_x<2>(st, rh, lane, xa);
+    __builtin_amdgcn_sched_barrier(0);
+    rg_mfma<NWT, 1>(tgt, wf, xb);
+    rg_read_x<3>(st, rh, lane, xb);
+    __builtin_amdgcn_sched_barrier(0);
+    rg_mfma<NWT, 2>(tgt, wf, xa);
+    if (c + 1 < nch) {
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((RG_AHEAD - 1) * C::LOADS)
+                   : "memory");
+      issue(c + 1 + RG_AHEAD);
+      const unsigned char* sn = smem + ((c + 1) % RG_SLOTS) * C::STAGE;
+      rg_read_w<NWT, FP8>(sn, cg, lane, wn);
+      rg_read_x<0>(sn, rh, lane, xa);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    rg_mfma<NWT, 3>(tgt, wf, xb);
 #pragma unroll
-    for (int j = 0; j < MW; ++j) {
-      const int r = rh * 128 + j * 16 + (lane & 15);
-      const bf16x8_t bx =
-          *reinterpret_cast<const bf16x8_t*>(st + r * RG_ROW_BYTES + (((lane >> 4) ^ rg_swz(r)) << 4));
-#pragma unroll
-      for (int i = 0; i < NWT; ++i) {
-        if constexpr (SCALED) accu[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[i], bx, accu[i][j], 0, 0, 0);
-        else acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[i], bx, acc[i][j], 0, 0, 0);
-      }
-    }
+    for (int i = 0; i < NWT; ++i) wf[i] = wn[i];
     if constexpr (SCALED) {
       const int kend = kb + (c + 1) * RG_KC;
       if ((kend & 255) == 0) {
