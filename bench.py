@@ -15,6 +15,20 @@ head's MFMA roofline timed the same way, the accepted tokens per step of a
 workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--n-steps N]
+
+HBM traffic of the dominant kernel (roofline.traffic) comes from hardware
+counters taken in separate runs (each counter in its own run, the copy
+calibration in its own process):
+
+    rocprofv3 --pmc FETCH_SIZE -d F -o p -- python bench.py --pmc-step
+    rocprofv3 --pmc WRITE_SIZE -d W -o p -- python bench.py --pmc-step
+    rocprofv3 --pmc FETCH_SIZE -d CF -o p -- python bench.py --pmc-copy
+    rocprofv3 --pmc WRITE_SIZE -d CW -o p -- python bench.py --pmc-copy
+    python bench.py --pmc-summarize F W CF CW profiles/moe_up_gate_up_traffic.md
+
+The summary records the counter bytes per launch, each scaled by what the
+same counter reads for a copy of known size, and the hash of the GEMM
+source; the bench reports the traffic only while that source is unchanged.
 """
 from __future__ import annotations
 
@@ -31,6 +45,124 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+GEMM_SRC = os.path.join(ROOT, "discrete_text_diffusion_amd", "csrc", "k_gemm.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "moe_up_gate_up_traffic.md")
+MOE_UP_KERNEL = "k_wsgemm<32, 1, 128, true, 0, false>"
+COPY_BYTES = 1 << 30       # bytes read (and written) by one calibration copy
+
+
+def _sha256(path):
+    import hashlib
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def pmc_copy():
+    """One plain device copy of COPY_BYTES, three times (counter calibration)."""
+    import torch
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def pmc_step(workload: str):
+    """One denoising step of the workload (cache rows left as allocated): the
+    launches whose counters the traffic summary reads."""
+    import torch
+    from discrete_text_diffusion_amd import runtime as rt
+    import discrete_text_diffusion_amd as dg
+    from synth.configs import WORKLOADS
+    wl = WORKLOADS[workload]
+    print(f"[pmc-step] building {workload}", file=sys.stderr, flush=True)
+    model = rt.DeviceModel(wl.model, wl.lm_scale)
+    print("[pmc-step] model built", file=sys.stderr, flush=True)
+    cache = rt.DeviceCache(wl.model, wl.batch, wl.prefix + wl.canvas)
+    cache.struct.length = wl.prefix
+    cv = rt.DeviceCanvas(wl.model, wl.batch, wl.canvas, list(wl.sampler_seeds)[:wl.batch])
+    ws = rt.Workspace(model.cfg, wl.batch, wl.canvas)
+    st = rt.stream_handle()
+    dg.dg_init_canvas(model.cfg, cv.struct, 0, st)
+    dg.dg_denoise_step(model.cfg, model.weights, cache.struct, cv.struct, rt.step_params(0, 12, 0, False), ws.ptr,
+                       ws.size, st)
+    torch.cuda.synchronize()
+    print("[pmc-step] step done", file=sys.stderr, flush=True)
+
+
+def _counter_rows(d):
+    """(dispatch id, kernel name, counter name, value) of every counter record
+    under d: rocprofv3's database output (SQLite, the counters_collection
+    view) or its CSV output."""
+    import csv
+    import glob
+    import sqlite3
+    for f in glob.glob(os.path.join(d, "**", "*.db"), recursive=True):
+        con = sqlite3.connect(f)
+        for r in con.execute("select dispatch_id, kernel_name, counter_name, value from counters_collection"):
+            yield r
+        con.close()
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            yield r["Dispatch_Id"], r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])
+
+
+def _counter_kib(d, counter, name_has=None, biggest=False):
+    """Mean per-dispatch value of `counter` (KiB) over the dispatches whose
+    kernel name contains name_has (or of the dispatch with the largest value)."""
+    vals = {}
+    for disp, name, cname, value in _counter_rows(d):
+        if cname != counter or (name_has is not None and name_has not in name):
+            continue
+        key = (disp, name)
+        vals[key] = vals.get(key, 0.0) + float(value)
+    if not vals:
+        raise SystemExit(f"no {counter} values under {d}")
+    if biggest:
+        return max(vals.values()), 1, max(vals, key=vals.get)[1]
+    return sum(vals.values()) / len(vals), len(vals), None
+
+
+def pmc_summarize(df, dw, dcf, dcw, out):
+    fetch, n_f, _ = _counter_kib(df, "FETCH_SIZE", MOE_UP_KERNEL)
+    write, n_w, _ = _counter_kib(dw, "WRITE_SIZE", MOE_UP_KERNEL)
+    cfetch, _, cname = _counter_kib(dcf, "FETCH_SIZE", biggest=True)
+    cwrite, _, _ = _counter_kib(dcw, "WRITE_SIZE", biggest=True)
+    kf = cfetch * 1024.0 / COPY_BYTES   # counter bytes per byte a copy reads
+    kw = cwrite * 1024.0 / COPY_BYTES   # counter bytes per byte a copy writes
+    traffic = fetch * 1024.0 / kf + write * 1024.0 / kw
+    rec = {"kernel": MOE_UP_KERNEL, "fetch_kib": round(fetch, 1), "write_kib": round(write, 1), "launches": n_f,
+           "copy_kernel": cname, "copy_bytes": COPY_BYTES, "copy_fetch_kib": round(cfetch, 1),
+           "copy_write_kib": round(cwrite, 1), "fetch_factor": round(kf, 4), "write_factor": round(kw, 4),
+           "traffic_bytes_per_launch": int(traffic), "k_gemm_sha256": _sha256(GEMM_SRC)}
+    with open(out, "w") as fh:
+        fh.write("# HBM traffic of the routed + shared expert gate/up GEMM (full30 denoising step)\n\n")
+        fh.write("Counters per dispatch (KiB) from four separate rocprofv3 runs, from the repository root:\n\n")
+        for c, m, dd in (("FETCH_SIZE", "--pmc-step", df), ("WRITE_SIZE", "--pmc-step", dw),
+                         ("FETCH_SIZE", "--pmc-copy", dcf), ("WRITE_SIZE", "--pmc-copy", dcw)):
+            fh.write(f"    rocprofv3 --pmc {c} -d {dd} -o p -- python bench.py {m}\n")
+        fh.write(f"    python bench.py --pmc-summarize {df} {dw} {dcf} {dcw} {out}\n\n")
+        fh.write(f"* `{MOE_UP_KERNEL}`: FETCH_SIZE {fetch:.0f} KiB, WRITE_SIZE {write:.0f} KiB per launch "
+                 f"(mean of {n_f} and {n_w} launches: one step, 30 layers).\n")
+        fh.write(f"* Copy calibration ({cname}, {COPY_BYTES} B read and written): FETCH_SIZE {cfetch:.0f} KiB, "
+                 f"WRITE_SIZE {cwrite:.0f} KiB -> factors {kf:.4f} (fetch) and {kw:.4f} (write).\n")
+        fh.write(f"* HBM traffic per launch = fetch / {kf:.4f} + write / {kw:.4f} = {traffic / 1e9:.4f} GB "
+                 f"(algorithmic: the bench's algorithmic_bytes_per_launch).\n\n")
+        fh.write("```json\n" + json.dumps(rec) + "\n```\n")
+    print(json.dumps(rec))
+
+
+def stored_traffic():
+    """traffic_bytes_per_launch of the stored counter summary, or None if
+    there is none or the GEMM source has changed since it was taken."""
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+        rec = json.loads(text.split("```json")[1].split("```")[0])
+    except (OSError, IndexError, ValueError):
+        return None
+    if rec.get("k_gemm_sha256") != _sha256(GEMM_SRC):
+        return None
+    return rec.get("traffic_bytes_per_launch")
 
 
 def _hip():
@@ -151,7 +283,19 @@ def main():
     ap.add_argument("--workload", default="full30")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--pmc-step", action="store_true", help="one denoising step only (counter runs)")
+    ap.add_argument("--pmc-copy", action="store_true", help="counter calibration copy only")
+    ap.add_argument("--pmc-summarize", nargs=5, metavar=("F", "W", "CF", "CW", "OUT"))
     args = ap.parse_args()
+    if args.pmc_summarize:
+        pmc_summarize(*args.pmc_summarize)
+        return
+    if args.pmc_copy:
+        pmc_copy()
+        return
+    if args.pmc_step:
+        pmc_step(args.workload)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs the decoding step on one GPU only; "
                                    "multi-GPU sharding is described but not built"}))
@@ -315,7 +459,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": stored_traffic(),
             "algorithmic_bytes_per_launch": up_bytes,
             "avg_launch_ms": round(up_ms, 5),
             "launches_timed": len(up),

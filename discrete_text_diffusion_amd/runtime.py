@@ -81,10 +81,10 @@ class DeviceModel:
             if keep_plain:
                 self.tensors[name + "_plain"] = tmp[:n].clone()
             if pack:
+                # a bank of `groups` matrices packed one after the other is the
+                # packed form of the stacked [groups*rows][cols] matrix (rows % 16 == 0)
                 t = torch.empty(n, dtype=torch.bfloat16, device=self.device)
-                for g in range(groups):
-                    off = g * rows * cols * 2
-                    dg_pack_weight_bf16(t.data_ptr() + off, tmp.data_ptr() + off, rows, cols, st)
+                dg_pack_weight_bf16(t.data_ptr(), tmp.data_ptr(), groups * rows, cols, st)
                 self.tensors[name] = t
                 return t
             return None
