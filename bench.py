@@ -68,8 +68,8 @@ def pmc_copy():
 
 
 def pmc_step(workload: str):
-    """One denoising step of the workload (cache rows left as allocated): the
-    launches whose counters the traffic summary reads."""
+    """The bench's prefill and one denoising step (t = 0) of the workload:
+    the launches whose counters the traffic summary reads."""
     import torch
     from discrete_text_diffusion_amd import runtime as rt
     import discrete_text_diffusion_amd as dg
@@ -78,11 +78,19 @@ def pmc_step(workload: str):
     print(f"[pmc-step] building {workload}", file=sys.stderr, flush=True)
     model = rt.DeviceModel(wl.model, wl.lm_scale)
     print("[pmc-step] model built", file=sys.stderr, flush=True)
+    import synth
     cache = rt.DeviceCache(wl.model, wl.batch, wl.prefix + wl.canvas)
-    cache.struct.length = wl.prefix
     cv = rt.DeviceCanvas(wl.model, wl.batch, wl.canvas, list(wl.sampler_seeds)[:wl.batch])
     ws = rt.Workspace(model.cfg, wl.batch, wl.canvas)
     st = rt.stream_handle()
+    # the bench's prompt and prefill, so the step routes as the timed steps do
+    prompt = torch.empty(wl.batch * wl.prefix, dtype=torch.int32, device="cuda")
+    for b in range(wl.batch):
+        synth.dev_tokens(prompt.data_ptr() + 4 * b * wl.prefix, wl.prefix, wl.prompt_seed + b, synth.TID["prompt"],
+                         wl.model.vocab, st)
+    dg.dg_encode_append(model.cfg, model.weights, cache.struct, prompt.data_ptr(), wl.batch, wl.prefix, ws.ptr, ws.size,
+                        st)
+    print("[pmc-step] prefix encoded", file=sys.stderr, flush=True)
     dg.dg_init_canvas(model.cfg, cv.struct, 0, st)
     dg.dg_denoise_step(model.cfg, model.weights, cache.struct, cv.struct, rt.step_params(0, 12, 0, False), ws.ptr,
                        ws.size, st)
@@ -107,9 +115,10 @@ def _counter_rows(d):
             yield r["Dispatch_Id"], r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])
 
 
-def _counter_kib(d, counter, name_has=None, biggest=False):
+def _counter_kib(d, counter, name_has=None, biggest=False, last=None):
     """Mean per-dispatch value of `counter` (KiB) over the dispatches whose
-    kernel name contains name_has (or of the dispatch with the largest value)."""
+    kernel name contains name_has (the `last` of them in dispatch order when
+    given), or the value of the dispatch with the largest value."""
     vals = {}
     for disp, name, cname, value in _counter_rows(d):
         if cname != counter or (name_has is not None and name_has not in name):
@@ -120,12 +129,19 @@ def _counter_kib(d, counter, name_has=None, biggest=False):
         raise SystemExit(f"no {counter} values under {d}")
     if biggest:
         return max(vals.values()), 1, max(vals, key=vals.get)[1]
+    if last is not None:
+        keep = sorted(vals, key=lambda kv: int(kv[0]))[-last:]
+        vals = {kv: vals[kv] for kv in keep}
     return sum(vals.values()) / len(vals), len(vals), None
 
 
 def pmc_summarize(df, dw, dcf, dcw, out):
-    fetch, n_f, _ = _counter_kib(df, "FETCH_SIZE", MOE_UP_KERNEL)
-    write, n_w, _ = _counter_kib(dw, "WRITE_SIZE", MOE_UP_KERNEL)
+    # the denoising step's launches: the last n_layers of the kernel (the
+    # prefix encode's come first)
+    from synth.configs import WORKLOADS
+    nl = WORKLOADS["full30"].model.n_layers
+    fetch, n_f, _ = _counter_kib(df, "FETCH_SIZE", MOE_UP_KERNEL, last=nl)
+    write, n_w, _ = _counter_kib(dw, "WRITE_SIZE", MOE_UP_KERNEL, last=nl)
     cfetch, _, cname = _counter_kib(dcf, "FETCH_SIZE", biggest=True)
     cwrite, _, _ = _counter_kib(dcw, "WRITE_SIZE", biggest=True)
     kf = cfetch * 1024.0 / COPY_BYTES   # counter bytes per byte a copy reads
@@ -143,7 +159,7 @@ def pmc_summarize(df, dw, dcf, dcw, out):
             fh.write(f"    rocprofv3 --pmc {c} -d {dd} -o p -- python bench.py {m}\n")
         fh.write(f"    python bench.py --pmc-summarize {df} {dw} {dcf} {dcw} {out}\n\n")
         fh.write(f"* `{MOE_UP_KERNEL}`: FETCH_SIZE {fetch:.0f} KiB, WRITE_SIZE {write:.0f} KiB per launch "
-                 f"(mean of {n_f} and {n_w} launches: one step, 30 layers).\n")
+                 f"(mean of the {n_f} and {n_w} launches of one denoising step after the prefix encode).\n")
         fh.write(f"* Copy calibration ({cname}, {COPY_BYTES} B read and written): FETCH_SIZE {cfetch:.0f} KiB, "
                  f"WRITE_SIZE {cwrite:.0f} KiB -> factors {kf:.4f} (fetch) and {kw:.4f} (write).\n")
         fh.write(f"* HBM traffic per launch = fetch / {kf:.4f} + write / {kw:.4f} = {traffic / 1e9:.4f} GB "
@@ -210,13 +226,15 @@ class EventPool:
         return out
 
 
-def moe_up_bytes(shape, T):
+def moe_up_bytes(shape, T, experts=None):
     """Algorithmic HBM bytes of one routed + shared gate/up launch: the gate and
-    up weights of every expert that receives a token (all of them at 256 tokens
-    x top-8 of 128: P(idle) = (120/128)^256 ~ 7e-8), the shared expert's gate/up,
-    the normalised activations read once and the GeGLU output rows written."""
+    up weights of every expert that receives a token (`experts`, by default
+    all of them, as uniform routing of 256 tokens x top-8 of 128 gives:
+    P(idle) = (120/128)^256 ~ 7e-8), the shared expert's gate/up, the
+    normalised activations read once and the GeGLU output rows written."""
     d, de, ds = shape.d_model, shape.d_expert, shape.d_shared
-    experts = min(shape.n_experts, T * shape.top_k)
+    if experts is None:
+        experts = min(shape.n_experts, T * shape.top_k)
     w = experts * 2 * de * d * 2 + 2 * ds * d * 2
     act = T * d * 2
     rows = T * shape.top_k + (ds // de) * T
@@ -416,7 +434,21 @@ def main():
         dg.dg_denoise_step(cfg, model.weights, cache.struct, canvas.struct, rt.step_params(t, args.n_steps, 0, False),
                            ws.ptr, ws.size, st)
         acc_steps.append(int(canvas.n_accepted.sum().item()))
-    up_bytes = moe_up_bytes(shape, T)
+    # experts that receive tokens, from one step's routing (router logits of
+    # every layer through the test entry point, top-k on the host)
+    rl = torch.empty(shape.n_layers * T * shape.n_experts, dtype=torch.float32, device="cuda")
+    zl = torch.empty(T * shape.vocab, dtype=torch.float32, device="cuda")
+    dg.dg_init_canvas(cfg, canvas.struct, 0, st)
+    dg.dg_test_forward_logits(cfg, model.weights, cache.struct, canvas.struct, rt.step_params(0, args.n_steps, 0, False),
+                              None, rl.data_ptr(), zl.data_ptr(), ws.ptr, ws.size, st)
+    torch.cuda.synchronize()
+    r = rl.cpu().numpy().reshape(shape.n_layers, T, shape.n_experts)
+    del rl, zl
+    top = np.argsort(-r, axis=-1, kind="stable")[..., :shape.top_k]
+    touched = [int(np.unique(top[l]).size) for l in range(shape.n_layers)]
+    hottest = [int(np.bincount(top[l].reshape(-1), minlength=shape.n_experts).max()) for l in range(shape.n_layers)]
+    experts_mean = sum(touched) / len(touched)
+    up_bytes = moe_up_bytes(shape, T, experts_mean)
     achieved = up_bytes / (up_ms * 1e-3) / 1e9
     lm_flops = 2.0 * T * shape.vocab * shape.d_model
     lm_tflops = lm_flops / (lm_ms * 1e-3) / 1e12
@@ -460,7 +492,10 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": stored_traffic(),
-            "algorithmic_bytes_per_launch": up_bytes,
+            "algorithmic_bytes_per_launch": int(up_bytes),
+            "experts_touched_mean": round(experts_mean, 2),
+            "experts_touched_min": min(touched),
+            "tokens_of_hottest_expert_max": max(hottest),
             "avg_launch_ms": round(up_ms, 5),
             "launches_timed": len(up),
         },

@@ -291,40 +291,47 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void k_attn_mfma(AttnArgs a) {
 // Merge split partials in split order: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
 template <typename TA>
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
+  // one wave per (token, head) row, four of the 256 dims per lane; every
+  // lane forms the split weights itself (the same few loads, broadcast), and
+  // all loads are issued before the first use
   const int64_t T = (int64_t)a.n_seq * a.seq_len;
-  const int64_t row = blockIdx.x;  // token * n_q + head
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // token * n_q + head
   if (row >= T * a.n_q) return;
+  const int lane = threadIdx.x & 63;
   constexpr int kMaxS = 16;
-  __shared__ float wsp[kMaxS];
-  __shared__ float inv_l;
-  if (threadIdx.x == 0) {
-    float2 ml[kMaxS];
-    float M = -INFINITY;
+  float2 ml[kMaxS];
+  float4 v[kMaxS];
 #pragma unroll
-    for (int s = 0; s < kMaxS; ++s) {
-      ml[s] = s < a.n_split ? a.part_ml[(int64_t)s * T * a.n_q + row] : make_float2(-INFINITY, 0.f);
-      M = fmaxf(M, ml[s].x);
-    }
-    const float sh = M == -INFINITY ? 0.f : M;
-    float L = 0.f;
-#pragma unroll
-    for (int s = 0; s < kMaxS; ++s) {
-      wsp[s] = exp2f(ml[s].x - sh);
-      L += wsp[s] * ml[s].y;
-    }
-    inv_l = L > 0.f ? 1.f / L : 0.f;
+  for (int s = 0; s < kMaxS; ++s) {
+    const int64_t pr = (int64_t)s * T * a.n_q + row;
+    ml[s] = s < a.n_split ? a.part_ml[pr] : make_float2(-INFINITY, 0.f);
+    v[s] = s < a.n_split ? *reinterpret_cast<const float4*>(a.part_o + pr * a.d + 4 * lane)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  __syncthreads();
-  for (int dd = threadIdx.x; dd < a.d; dd += blockDim.x) {
-    float v[kMaxS];
+  float M = -INFINITY;
 #pragma unroll
-    for (int s = 0; s < kMaxS; ++s)
-      v[s] = s < a.n_split ? a.part_o[((int64_t)s * T * a.n_q + row) * a.d + dd] : 0.f;
-    float acc = 0.f;
+  for (int s = 0; s < kMaxS; ++s) M = fmaxf(M, ml[s].x);
+  const float sh = M == -INFINITY ? 0.f : M;
+  float w[kMaxS], L = 0.f;
 #pragma unroll
-    for (int s = 0; s < kMaxS; ++s) acc += wsp[s] * v[s];
-    reinterpret_cast<TA*>(a.out)[row * a.d + dd] = to_act<TA>(acc * inv_l);
+  for (int s = 0; s < kMaxS; ++s) {
+    w[s] = exp2f(ml[s].x - sh);
+    L += w[s] * ml[s].y;
   }
+  const float inv_l = L > 0.f ? 1.f / L : 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int s = 0; s < kMaxS; ++s) {
+    acc.x += w[s] * v[s].x;
+    acc.y += w[s] * v[s].y;
+    acc.z += w[s] * v[s].z;
+    acc.w += w[s] * v[s].w;
+  }
+  TA* o = reinterpret_cast<TA*>(a.out) + row * a.d + 4 * lane;
+  o[0] = to_act<TA>(acc.x * inv_l);
+  o[1] = to_act<TA>(acc.y * inv_l);
+  o[2] = to_act<TA>(acc.z * inv_l);
+  o[3] = to_act<TA>(acc.w * inv_l);
 }
 
 // Plain path (fp32 models, any d_head <= 256): one wave per (token, head),
@@ -424,7 +431,8 @@ int launch_attention(int dtype, const void* q, int64_t q_ld, const void* k, cons
   hipLaunchKernelGGL(k_attn_mfma, dim3((unsigned)blocks), dim3(ATT_THREADS), 0, s, a);
   if (hipGetLastError() != hipSuccess) return -5;
   if (n_split > 1) {
-    hipLaunchKernelGGL(k_attn_merge<bf16_t>, dim3((unsigned)((int64_t)n_seq * seq_len * n_q)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_attn_merge<bf16_t>, dim3((unsigned)DG_CEIL_DIV((int64_t)n_seq * seq_len * n_q, 4)), dim3(256), 0,
+                       s, a);
     if (hipGetLastError() != hipSuccess) return -5;
   }
   return 0;

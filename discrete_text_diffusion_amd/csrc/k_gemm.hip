@@ -721,6 +721,50 @@ __device__ __forceinline__ void rg_mfma(f32x4_t (&acc)[NWT][8], const bf16x8_t (
       acc[i][2 * G + jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[i], x[jj], acc[i][2 * G + jj], 0, 0, 0);
 }
 
+// LM-head epilogue of a 256-row x 256-id block (8 waves; wave w holds rows
+// 128 (w / 4) + [0, 128) and ids 64 (w % 4) + [0, 64) in acc): the logits
+// z = alpha acc (alpha scale[n] acc for fp8 weights) go through LDS 128 rows
+// at a time, then four rows per wave for the sampler statistics.  smem: at
+// least RG_ZROWS * LM_ZLD floats, free; u2s: RG_ROWS floats.
+template <bool FP8>
+__device__ __forceinline__ void rg_lm_epilogue(const GemmArgs& a, const LmArgs& lm, const f32x4_t (&acc)[4][8],
+                                               unsigned char* smem, float* u2s, int fb, int row0, int nrows,
+                                               uint64_t seed) {
+  constexpr int NWT = 4, MW = 8, BN = 256;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rh = wave >> 2, cg = wave & 3;
+  if (tid < nrows) u2s[tid] = row_u2_seeded(row0 + tid, seed, lm);  // read after the next barrier
+  float* zt = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if (rh == half) {
+#pragma unroll
+      for (int i = 0; i < NWT; ++i) {
+        const int col = (cg * NWT + i) * 16 + (lane >> 4) * 4;
+        f32x4_t sc = f32x4_t{a.alpha, a.alpha, a.alpha, a.alpha};
+        if constexpr (FP8) {
+          const float4 w = *reinterpret_cast<const float4*>(a.ws0 + (int64_t)fb * BN + col);
+          sc = f32x4_t{a.alpha * w.x, a.alpha * w.y, a.alpha * w.z, a.alpha * w.w};
+        }
+#pragma unroll
+        for (int j = 0; j < MW; ++j) {
+          const f32x4_t v = acc[i][j] * sc;
+          *reinterpret_cast<float4*>(zt + (j * 16 + (lane & 15)) * LM_ZLD + col) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+      }
+    }
+    __syncthreads();
+    for (int rr = wave * 4; rr < RG_ZROWS; rr += 4 * (RG_THREADS / 64)) {
+      const int r = half * RG_ZROWS + rr;
+      if (r < nrows) {
+        const int nr = min(4, nrows - r);
+        tile_stats4(zt + rr * LM_ZLD, LM_ZLD, nr, row0 + r, fb, lm, u2s[r + min(lane >> 4, nr - 1)]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 template <bool LMHEAD, bool SCALED, bool FP8>
 __global__ __launch_bounds__(RG_THREADS, 1) void k_rowgemm(GemmArgs a, LmArgs lm) {
   using C = RgCfg<LMHEAD, SCALED, FP8>;
@@ -897,40 +941,7 @@ __global__ __launch_bounds__(RG_THREADS, 1) void k_rowgemm(GemmArgs a, LmArgs lm
       }
     }
   } else {
-    float* u2s = extra;
-    if (tid < nrows) u2s[tid] = row_u2_seeded(row0 + tid, seed, lm);  // read after the next barrier
-    // logits of 128 rows x 256 ids through LDS (one row half at a time), then
-    // four rows per wave for the sampler statistics
-    float* zt = reinterpret_cast<float*>(smem);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      if (rh == half) {
-#pragma unroll
-        for (int i = 0; i < NWT; ++i) {
-          const int col = (cg * NWT + i) * 16 + (lane >> 4) * 4;
-          // z = alpha acc (bf16 weights) or alpha scale[n] acc (fp8 weights)
-          f32x4_t sc = f32x4_t{a.alpha, a.alpha, a.alpha, a.alpha};
-          if constexpr (FP8) {
-            const float4 w = *reinterpret_cast<const float4*>(a.ws0 + (int64_t)fb * C::BN + col);
-            sc = f32x4_t{a.alpha * w.x, a.alpha * w.y, a.alpha * w.z, a.alpha * w.w};
-          }
-#pragma unroll
-          for (int j = 0; j < MW; ++j) {
-            const f32x4_t v = acc[i][j] * sc;
-            *reinterpret_cast<float4*>(zt + (j * 16 + (lane & 15)) * LM_ZLD + col) = make_float4(v[0], v[1], v[2], v[3]);
-          }
-        }
-      }
-      __syncthreads();
-      for (int rr = wave * 4; rr < RG_ZROWS; rr += 4 * (RG_THREADS / 64)) {
-        const int r = half * RG_ZROWS + rr;
-        if (r < nrows) {
-          const int nr = min(4, nrows - r);
-          tile_stats4(zt + rr * LM_ZLD, LM_ZLD, nr, row0 + r, fb, lm, u2s[r + min(lane >> 4, nr - 1)]);
-        }
-      }
-      __syncthreads();
-    }
+    rg_lm_epilogue<FP8>(a, lm, acc, smem, extra, fb, row0, nrows, seed);
   }
 }
 

@@ -16,10 +16,11 @@ namespace {
 // beat it (larger, or equal with a lower expert id); rank < k is selected at
 // that rank.  The weights are the softmax over the k selected logits, summed
 // in rank order.
+template <int NQ>  // logits per lane: E <= 64 NQ
 __global__ __launch_bounds__(256) void k_topk(const float* part, int n_split, int64_t split_stride, int T, int E,
                                               int k, const int32_t* forced, int32_t* ids, float* w,
                                               float* r_out) {
-  __shared__ float lg[4][256];
+  __shared__ __attribute__((aligned(16))) float lg[4][256];
   __shared__ float sv[4][16];
   __shared__ int se[4][16];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -62,19 +63,33 @@ __global__ __launch_bounds__(256) void k_topk(const float* part, int n_split, in
       se[wave][lane] = e;
     }
   } else {
+    // four logits per LDS read, every held logit compared in the same pass
+    // (lg holds -inf past E, which beats nothing)
+    int rank[NQ];
 #pragma unroll
-    for (int q = 0; q < kMaxPerLane; ++q) {
-      const int e = lane + q * 64;
-      if (e >= E) continue;
-      const float v = r[q];
-      int rank = 0;
-      for (int o = 0; o < E; ++o) {
-        const float u = lg[wave][o];
-        rank += (u > v || (u == v && o < e)) ? 1 : 0;
+    for (int q = 0; q < NQ; ++q) rank[q] = 0;
+    const float4* lg4 = reinterpret_cast<const float4*>(lg[wave]);
+    const int E4 = (E + 3) >> 2;
+#pragma unroll 8
+    for (int o4 = 0; o4 < E4; ++o4) {
+      const float4 u = lg4[o4];
+      const float uu[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+        const int o = 4 * o4 + s2;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          const int e = lane + q * 64;
+          rank[q] += (uu[s2] > r[q] || (uu[s2] == r[q] && o < e)) ? 1 : 0;
+        }
       }
-      if (rank < k) {
-        sv[wave][rank] = v;
-        se[wave][rank] = e;
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int e = lane + q * 64;
+      if (e < E && rank[q] < k) {
+        sv[wave][rank[q]] = r[q];
+        se[wave][rank[q]] = e;
       }
     }
   }
@@ -182,8 +197,10 @@ __global__ __launch_bounds__(1024) void k_route_sort(const int32_t* ids, int T, 
 int launch_topk(const float* part, int n_split, int64_t split_stride, int T, int E, int k, const int32_t* forced,
                 int32_t* ids, float* w, float* r_out, hipStream_t s) {
   if (E > 256 || k > 16 || k > E || n_split < 1 || n_split > 16) return -1;
-  hipLaunchKernelGGL(k_topk, dim3(DG_CEIL_DIV(T, 4)), dim3(256), 0, s, part, n_split, split_stride, T, E, k, forced, ids,
-                     w, r_out);
+  const dim3 g(DG_CEIL_DIV(T, 4)), b(256);
+  if (E <= 64) hipLaunchKernelGGL(k_topk<1>, g, b, 0, s, part, n_split, split_stride, T, E, k, forced, ids, w, r_out);
+  else if (E <= 128) hipLaunchKernelGGL(k_topk<2>, g, b, 0, s, part, n_split, split_stride, T, E, k, forced, ids, w, r_out);
+  else hipLaunchKernelGGL(k_topk<4>, g, b, 0, s, part, n_split, split_stride, T, E, k, forced, ids, w, r_out);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
