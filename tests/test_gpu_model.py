@@ -129,6 +129,16 @@ def _err_summary(name, got, want):
 # rounding of an activation fell on the other side of a boundary and
 # propagated).
 ROUTE_EPS = {"f32": 1e-5, "bf16": 5e-3}
+
+
+def flip_margin_bound(got, want, dtype="bf16"):
+    """Largest oracle margin (k-th minus (k+1)-th router logit) at which a
+    GPU route may differ from the oracle's: a flip needs the two logits'
+    errors to sum past the margin, so twice the largest router-logit error
+    measured with the oracle's routes forced (that error is itself held to
+    the fp32 twin), and at least the fixed near-tie threshold."""
+    e = np.abs(np.asarray(got, dtype=np.float64) - np.asarray(want, dtype=np.float64))
+    return max(ROUTE_EPS[dtype], 2.0 * float(e.max()) if e.size else 0.0)
 # Typical (median) router-logit error bound with forced routes.
 ROUTE_MEDIAN = {"f32": 1e-6, "bf16": 1e-4}
 
