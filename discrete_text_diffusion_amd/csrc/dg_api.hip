@@ -367,7 +367,6 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
         a.n_fb = (s.de + 63) / 64;
         a.tile_fastest = 1;  // the row tiles of one (expert, feature block) run together (same XCD): a hot
                              // expert's weight slice comes from HBM once and from L2 for its other tiles
-        // 128-wide K chunks keep twice the weight bytes in flight per wave
         DG_TRY(launch_wsgemm(a, kMoeBM, 1, s.d % 128 == 0 ? 128 : 64, true, c.st));
       } else {
         DG_TRY(launch_gemm_simple(a, c.st));

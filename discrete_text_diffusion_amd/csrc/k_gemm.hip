@@ -36,18 +36,35 @@ __device__ __forceinline__ int xcd_logical_block(int nblocks) {
   return (hw & 7) * per + (hw >> 3);
 }
 
-__device__ __forceinline__ void decode_block(const GemmArgs& a, int lb, int& tile, int& fb, int& ks) {
+__device__ __forceinline__ void decode_block(const GemmArgs& a, int lb, int ntiles, int& tile, int& fb, int& ks) {
   // order: split outermost, then (tile, fb) with the chosen one fastest
-  const int per_split = a.max_tiles * a.n_fb;
+  const int per_split = ntiles * a.n_fb;
   ks = lb / per_split;
   const int r = lb - ks * per_split;
   if (a.tile_fastest) {
-    tile = r % a.max_tiles;
-    fb = r / a.max_tiles;
+    tile = r % ntiles;
+    fb = r / ntiles;
   } else {
     fb = r % a.n_fb;
     tile = r / a.n_fb;
   }
+}
+
+// The workgroup's (tile, feature block, split), or false if it has none.
+// The grid covers max_tiles row tiles; a grouped GEMM's tile list holds only
+// *n_tiles_dev of them, known on the device.  The valid workgroups are dealt
+// to the 8 XCDs in equal contiguous shares (hardware block b runs on XCD
+// b % 8), so every XCD gets the same amount of work and neighbouring
+// logical blocks (data they share) stay on one XCD.
+__device__ __forceinline__ bool block_work(const GemmArgs& a, int& ntiles, int& tile, int& fb, int& ks) {
+  ntiles = a.tiles ? *a.n_tiles_dev : a.max_tiles;
+  const int valid = a.n_split * ntiles * a.n_fb;
+  const int share = (valid + 7) >> 3;
+  const int i = blockIdx.x >> 3;
+  const int lb = (blockIdx.x & 7) * share + i;
+  if (i >= share || lb >= valid) return false;
+  decode_block(a, lb, ntiles, tile, fb, ks);
+  return true;
 }
 
 template <typename TA>
@@ -200,8 +217,10 @@ template <> struct WFrag<true> { typedef uint2 type; };
 __device__ __forceinline__ bf16x8_t wfrag_bf16(bf16x8_t w) { return w; }
 __device__ __forceinline__ bf16x8_t wfrag_bf16(uint2 w) { return fp8x8_to_bf16(w); }
 
-// Main loop shared by the generic and the LM-head kernels.
-template <int BM, int NWT, int KC, bool GEGLU, int ACT, bool FP8 = false>
+// Main loop shared by the generic and the LM-head kernels.  WS: stages of
+// the weight register ring (weights are loaded WS - 1 chunks ahead of their
+// MFMAs); activations are always one chunk ahead, double buffered in LDS.
+template <int BM, int NWT, int KC, bool GEGLU, int ACT, bool FP8 = false, int WS = 2>
 __device__ __forceinline__ void wsgemm_mainloop(const GemmArgs& a, const GemmTile& td, const GroupW& gw, int fb,
                                                 int ks, bf16_t* xs, f32x4_t (&acc)[NWT][BM / 16],
                                                 f32x4_t (&accu)[NWT][BM / 16]) {
@@ -255,10 +274,16 @@ __device__ __forceinline__ void wsgemm_mainloop(const GemmArgs& a, const GemmTil
     wp1[i] = GEGLU ? gw.w1 + off : nullptr;
   }
 
-  W_t wa[2][KS][NWT];
-  W_t wb[2][KS][NWT];
+  W_t wa[WS][KS][NWT];
+  W_t wb[WS][KS][NWT];
   uint4 xv[VPT];
 
+  // Every global load is unconditional: invalid feature tiles read tile 0,
+  // rows past the tile read its first row (zeroed when staged), and the
+  // prefetches past the last chunk re-read the last chunk.  Loads issued on
+  // every path keep the compiler's wait counts exact; a load under a branch
+  // makes it wait, conservatively, for the next chunk's loads before the
+  // current chunk's MFMAs.
   auto load_w = [&](auto BUF, int k0) {
     constexpr int buf = decltype(BUF)::value;
     const int kt0 = k0 >> 5;
@@ -266,37 +291,32 @@ __device__ __forceinline__ void wsgemm_mainloop(const GemmArgs& a, const GemmTil
     for (int s = 0; s < KS; ++s)
 #pragma unroll
       for (int i = 0; i < NWT; ++i) {
-        if (wval[i]) {
-          wa[buf][s][i] = *reinterpret_cast<const W_t*>(wp0[i] + (int64_t)(kt0 + s) * TILE_B);
-          if constexpr (GEGLU) wb[buf][s][i] = *reinterpret_cast<const W_t*>(wp1[i] + (int64_t)(kt0 + s) * TILE_B);
-        }
+        wa[buf][s][i] = *reinterpret_cast<const W_t*>(wp0[i] + (int64_t)(kt0 + s) * TILE_B);
+        if constexpr (GEGLU) wb[buf][s][i] = *reinterpret_cast<const W_t*>(wp1[i] + (int64_t)(kt0 + s) * TILE_B);
       }
   };
   auto load_x = [&](int k0) {
 #pragma unroll
     for (int q = 0; q < VPT; ++q) {
       const int v = tid + q * kThreads;
-      if (aval[q]) xv[q] = load_act8<ACT>(a, arow[q], k0 + (v % VPR) * 8);
-      else xv[q] = make_uint4(0, 0, 0, 0);
+      xv[q] = load_act8<ACT>(a, arow[q], k0 + (v % VPR) * 8);
     }
   };
   auto store_x = [&](int buf) {
 #pragma unroll
     for (int q = 0; q < VPT; ++q) {
       const int v = tid + q * kThreads;
-      if (v < NV) *reinterpret_cast<uint4*>(xs + buf * BM * LD + (v / VPR) * LD + (v % VPR) * 8) = xv[q];
+      const uint4 x = aval[q] ? xv[q] : make_uint4(0, 0, 0, 0);
+      if (v < NV) *reinterpret_cast<uint4*>(xs + buf * BM * LD + (v / VPR) * LD + (v % VPR) * 8) = x;
     }
   };
-  // one K-chunk: prefetch the next chunk (weights to registers, activations
-  // to registers then LDS), MFMAs on the current one
+  // one K-chunk: prefetch (activations of chunk c + 1 to registers then LDS,
+  // weights of chunk c + WS - 1 to registers), MFMAs on chunk c
   auto chunk = [&](auto CUR, int c) {
-    constexpr int cur = decltype(CUR)::value;
-    const bool more = c + 1 < nchunks;
-    if (more) {
-      load_x(kb + (c + 1) * KC);
-      load_w(std::integral_constant<int, cur ^ 1>{}, kb + (c + 1) * KC);
-    }
-    const bf16_t* xb = xs + cur * BM * LD;
+    constexpr int cur = decltype(CUR)::value;  // weight stage of chunk c
+    load_x(kb + min(c + 1, nchunks - 1) * KC);
+    load_w(std::integral_constant<int, (cur + WS - 1) % WS>{}, kb + min(c + WS - 1, nchunks - 1) * KC);
+    const bf16_t* xb = xs + (c & 1) * BM * LD;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       bf16x8_t bx[MW];
@@ -328,12 +348,10 @@ __device__ __forceinline__ void wsgemm_mainloop(const GemmArgs& a, const GemmTil
 #pragma unroll
         for (int j = 0; j < MW; ++j) {
           const int r = j * 16 + (lane & 15);
-          float sc = 0.f;
-          if (r < td.nrows) {
-            const int orow = td.row0 + r;
-            const int ar = a.row_map ? a.row_map[orow] : orow;
-            sc = a.act_scale[(int64_t)ar * a.scale_ld + (int64_t)tile * a.scale_tile_ld];
-          }
+          const int orow = td.row0 + (r < td.nrows ? r : 0);
+          const int ar = a.row_map ? a.row_map[orow] : orow;
+          const float sc0 = a.act_scale[(int64_t)ar * a.scale_ld + (int64_t)tile * a.scale_tile_ld];
+          const float sc = r < td.nrows ? sc0 : 0.f;
 #pragma unroll
           for (int i = 0; i < NWT; ++i) {
             acc[i][j] += sc * accu[i][j];
@@ -342,40 +360,35 @@ __device__ __forceinline__ void wsgemm_mainloop(const GemmArgs& a, const GemmTil
         }
       }
     }
-    if (more) store_x(cur ^ 1);
+    store_x((c + 1) & 1);
     __syncthreads();
   };
 
   load_x(kb);
   load_w(std::integral_constant<int, 0>{}, kb);
+  if constexpr (WS > 2) load_w(std::integral_constant<int, 1>{}, kb + min(1, nchunks - 1) * KC);
+  if constexpr (WS > 3) load_w(std::integral_constant<int, 2>{}, kb + min(2, nchunks - 1) * KC);
+  static_assert(WS >= 2 && WS <= 4, "weight ring of 2 to 4 stages");
   store_x(0);
   __syncthreads();
-  for (int c = 0; c < nchunks; c += 2) {
+  for (int c = 0; c < nchunks; c += WS) {
     chunk(std::integral_constant<int, 0>{}, c);
     if (c + 1 < nchunks) chunk(std::integral_constant<int, 1>{}, c + 1);
+    if constexpr (WS > 2) {
+      if (c + 2 < nchunks) chunk(std::integral_constant<int, 2>{}, c + 2);
+    }
+    if constexpr (WS > 3) {
+      if (c + 3 < nchunks) chunk(std::integral_constant<int, 3>{}, c + 3);
+    }
   }
 }
 
-template <int BM, int NWT, int KC, bool GEGLU, int ACT, bool FP8>
-__global__ __launch_bounds__(kThreads) void k_wsgemm(GemmArgs a) {
+// Epilogue of a 4-wave streaming workgroup: wave w holds features
+// ((fb * 4 + w) * NWT + i) * 16 + 4 (lane / 16) + e of rows j * 16 + lane % 16.
+template <int BM, int NWT, bool GEGLU, bool FP8>
+__device__ __forceinline__ void ws_epilogue(const GemmArgs& a, const GemmTile& td, const GroupW& gw, int fb, int ks,
+                                            const f32x4_t (&acc)[NWT][BM / 16], const f32x4_t (&accu)[NWT][BM / 16]) {
   constexpr int MW = BM / 16;
-  constexpr int LD = KC + 8;
-  __shared__ __attribute__((aligned(16))) bf16_t xs[2 * BM * LD];
-
-  int tile, fb, ks;
-  decode_block(a, xcd_logical_block(a.nblocks), tile, fb, ks);
-  if (ks >= a.n_split || fb >= a.n_fb) return;
-  const int ntiles = a.tiles ? *a.n_tiles_dev : a.max_tiles;
-  if (tile >= ntiles) return;
-  GemmTile td;
-  if (a.tiles) td = a.tiles[tile];
-  else td = GemmTile{0, tile * BM, min(BM, a.M - tile * BM), 0};
-  if (td.nrows <= 0) return;
-
-  f32x4_t acc[NWT][MW], accu[NWT][MW];
-  const GroupW gw = group_weights(a, td.group, FP8 ? 1 : 2);
-  wsgemm_mainloop<BM, NWT, KC, GEGLU, ACT, FP8>(a, td, gw, fb, ks, xs, acc, accu);
-
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < NWT; ++i) {
@@ -410,6 +423,26 @@ __global__ __launch_bounds__(kThreads) void k_wsgemm(GemmArgs a) {
       }
     }
   }
+}
+
+template <int BM, int NWT, int KC, bool GEGLU, int ACT, bool FP8, int WS = 2>
+__global__ __launch_bounds__(kThreads) void k_wsgemm(GemmArgs a) {
+  constexpr int MW = BM / 16;
+  constexpr int LD = KC + 8;
+  __shared__ __attribute__((aligned(16))) bf16_t xs[2 * BM * LD];
+
+  int ntiles, tile, fb, ks;
+  if (!block_work(a, ntiles, tile, fb, ks)) return;
+  GemmTile td;
+  if (a.tiles) td = a.tiles[tile];
+  else td = GemmTile{0, tile * BM, min(BM, a.M - tile * BM), 0};
+  if (td.nrows <= 0) return;
+
+  f32x4_t acc[NWT][MW], accu[NWT][MW];
+  const GroupW gw = group_weights(a, td.group, FP8 ? 1 : 2);
+  wsgemm_mainloop<BM, NWT, KC, GEGLU, ACT, FP8, WS>(a, td, gw, fb, ks, xs, acc, accu);
+
+  ws_epilogue<BM, NWT, GEGLU, FP8>(a, td, gw, fb, ks, acc, accu);
 }
 
 // ---------------------------------------------------------------------------
@@ -596,7 +629,7 @@ __global__ __launch_bounds__(kThreads) void k_lmhead(GemmArgs a, LmArgs lm) {
   float* zt = reinterpret_cast<float*>(smem);
 
   int tile, fb, ks;
-  decode_block(a, xcd_logical_block(a.nblocks), tile, fb, ks);
+  decode_block(a, xcd_logical_block(a.nblocks), a.max_tiles, tile, fb, ks);
   if (fb >= a.n_fb || tile >= a.max_tiles) return;
   const GemmTile td{0, tile * BM, min(BM, a.M - tile * BM), 0};
 
@@ -1077,21 +1110,21 @@ __global__ __launch_bounds__(kThreads) void k_pack_fp8(uint8_t* dst, const uint8
 // ---------------------------------------------------------------------------
 static int round8(int n) { return (n + 7) & ~7; }
 
-template <int BM, int NWT, int KC, bool GEGLU>
+template <int BM, int NWT, int KC, bool GEGLU, int WS = 2>
 static void launch_t(const GemmArgs& a0, int act, hipStream_t s) {
   GemmArgs a = a0;
   a.nblocks = round8(a.n_split * a.max_tiles * a.n_fb);
   dim3 grid(a.nblocks);
-  if (act == ACT_BF16) hipLaunchKernelGGL((k_wsgemm<BM, NWT, KC, GEGLU, ACT_BF16, false>), grid, dim3(kThreads), 0, s, a);
-  else if (act == ACT_F32) hipLaunchKernelGGL((k_wsgemm<BM, NWT, KC, GEGLU, ACT_F32, false>), grid, dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL((k_wsgemm<BM, NWT, KC, GEGLU, ACT_BF16_SCALED, false>), grid, dim3(kThreads), 0, s, a);
+  if (act == ACT_BF16) hipLaunchKernelGGL((k_wsgemm<BM, NWT, KC, GEGLU, ACT_BF16, false, WS>), grid, dim3(kThreads), 0, s, a);
+  else if (act == ACT_F32) hipLaunchKernelGGL((k_wsgemm<BM, NWT, KC, GEGLU, ACT_F32, false, WS>), grid, dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL((k_wsgemm<BM, NWT, KC, GEGLU, ACT_BF16_SCALED, false, WS>), grid, dim3(kThreads), 0, s, a);
 }
 
-template <int BM, int NWT, int KC, bool GEGLU>
+template <int BM, int NWT, int KC, bool GEGLU, int WS = 2>
 static void launch_fp8(const GemmArgs& a0, hipStream_t s) {
   GemmArgs a = a0;
   a.nblocks = round8(a.n_split * a.max_tiles * a.n_fb);
-  hipLaunchKernelGGL((k_wsgemm<BM, NWT, KC, GEGLU, ACT_BF16, true>), dim3(a.nblocks), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((k_wsgemm<BM, NWT, KC, GEGLU, ACT_BF16, true, WS>), dim3(a.nblocks), dim3(kThreads), 0, s, a);
 }
 
 int launch_wsgemm(const GemmArgs& a, int bm, int nwt, int kc, bool geglu, hipStream_t s) {
