@@ -47,7 +47,7 @@ HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 GEMM_SRC = os.path.join(ROOT, "discrete_text_diffusion_amd", "csrc", "k_gemm.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "moe_up_gate_up_traffic.md")
-MOE_UP_KERNEL = "k_wsgemm<32, 1, 128, true, 0, false>"
+MOE_UP_KERNEL = "k_wsgemm<32, 1, 128, true, 0, false, 2>"
 COPY_BYTES = 1 << 30       # bytes read (and written) by one calibration copy
 
 
