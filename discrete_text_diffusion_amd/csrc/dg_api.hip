@@ -200,23 +200,26 @@ int dense_gemm(const Ctx& c, GemmArgs a, int M, int N, int K, int max_split, int
   a.M = M; a.N = N; a.K = K;
   a.n_main = 1;
   if (used_split) *used_split = 1;
-  // Canvas-sized products (M <= kWsMaxRows): weight-streaming kernel, 32-row x
-  // 64-feature workgroups with 128-wide K chunks and no K split for the fused
-  // epilogues.  Many small workgroups keep more loads in flight than the
-  // row-resident kernel's 256 x 256 blocks, which at these M leave half the CUs
-  // idle or pay for fp32 partials; measured on the 30-layer step, QKV + O + router
-  // went from ~110 to ~92 us per layer.
+  // Canvas-sized products (M <= kWsMaxRows): weight-streaming kernel, 64-feature
+  // workgroups with 128-wide K chunks.  Many small workgroups keep more loads in
+  // flight than the row-resident kernel's 256 x 256 blocks, which at these M
+  // leave half the CUs idle or pay for fp32 partials.  Fused epilogues (no K
+  // split) take 64-row tiles, which halve the L2 re-reads of the weights; the
+  // K-split stores take 32-row tiles, which keep more workgroups per split
+  // (measured on the 30-layer step: QKV 42 -> 38 us, O and router faster at 32).
   if (c.s.dt == DG_DTYPE_BF16 && M <= kWsMaxRows && K % 128 == 0 && a.act_kind == ACT_BF16 &&
       a.epi != EPI_GEGLU) {
+    const bool store = a.epi == EPI_STORE_F32;
+    const int bm = store ? 32 : 64;
     a.kt_main = K / 32;
     a.n_fb = (N + 63) / 64;
-    a.max_tiles = (M + 31) / 32;
+    a.max_tiles = (M + bm - 1) / bm;
     a.tile_fastest = 1;
-    const int sp = (a.epi == EPI_STORE_F32) ? pick_split(a.max_tiles * a.n_fb, K, 128, max_split) : 1;
+    const int sp = store ? pick_split(a.max_tiles * a.n_fb, K, 128, max_split) : 1;
     a.k_split = ((K / 128 + sp - 1) / sp) * 128;
     a.n_split = (K + a.k_split - 1) / a.k_split;
     if (used_split) *used_split = a.n_split;
-    return launch_wsgemm(a, 32, 1, 128, false, c.st);
+    return launch_wsgemm(a, bm, 1, 128, false, c.st);
   }
   if (c.s.dt == DG_DTYPE_BF16 && K % 64 == 0 && a.act_kind != ACT_BF16_SCALED && a.epi != EPI_GEGLU &&
       a.epi != EPI_RESID) {

@@ -202,34 +202,56 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void k_attn_mfma(AttnArgs a) {
       }
     }
     // online softmax per query column; P^T operands: k index 8 g + e' <-> key 32 kk + 8 g + e'
+    // A tile whose 64 keys are all visible to all of the wave's queries needs
+    // no per-element mask (every tile but a split's last, and in the causal
+    // encode those below the wave's diagonal).
+    const bool full = (k0 + ATT_KT <= ke) && (!a.causal || k0 + ATT_KT - 1 <= a.n_prefix + qi0);
     f16x8_t pf[ATT_QT][2], pl[ATT_QT][2];
 #pragma unroll
     for (int qt = 0; qt < ATT_QT; ++qt) {
       float sv[16];
       float mt = -INFINITY;
+      if (full) {
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
+        for (int x = 0; x < 4; ++x)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = k0 + 32 * (x >> 1) + 8 * g + 4 * (x & 1) + e;
-          bool vis = j < ke;
-          if (a.causal) vis = vis && (j <= a.n_prefix + my_q[qt]);
-          const float xv = vis ? st[qt][x][e] * a.scale_log2 : -INFINITY;
-          sv[x * 4 + e] = xv;
-          mt = fmaxf(mt, xv);
-        }
+          for (int e = 0; e < 4; ++e) {
+            const float xv = st[qt][x][e] * a.scale_log2;
+            sv[x * 4 + e] = xv;
+            mt = fmaxf(mt, xv);
+          }
+      } else {
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = k0 + 32 * (x >> 1) + 8 * g + 4 * (x & 1) + e;
+            bool vis = j < ke;
+            if (a.causal) vis = vis && (j <= a.n_prefix + my_q[qt]);
+            const float xv = vis ? st[qt][x][e] * a.scale_log2 : -INFINITY;
+            sv[x * 4 + e] = xv;
+            mt = fmaxf(mt, xv);
+          }
+      }
       mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
       mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float m_new = fmaxf(m_run[qt], mt);
-      const float shift = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(m_run[qt] - shift);
-      m_run[qt] = m_new;
+      // The reference point m_run moves only when the tile's maximum exceeds
+      // it by more than 8 (log2 units), so the weights 2^(s - m_run) stay
+      // <= 2^8 (exact in the fp16 hi/lo pair) and the O rescale is rare.  O
+      // and l always share the same reference, so O / l is unchanged.
+      // (Hardware exp2: arguments <= 8; results below 2^-126 flush to zero.)
+      float alpha = 1.f;
+      if (mt > m_run[qt] + 8.f) {  // also the first visible key (m_run = -inf)
+        alpha = __builtin_amdgcn_exp2f(m_run[qt] - mt);
+        m_run[qt] = mt;
+      }
+      const float shift = m_run[qt] == -INFINITY ? 0.f : m_run[qt];
       float ps = 0.f;
 #pragma unroll
       for (int x = 0; x < 4; ++x)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p = exp2f(sv[x * 4 + e] - shift);
+          const float p = __builtin_amdgcn_exp2f(sv[x * 4 + e] - shift);
           ps += p;
           const _Float16 hi = (_Float16)p;
           const int kk = x >> 1, ep = 4 * (x & 1) + e;
@@ -237,8 +259,6 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void k_attn_mfma(AttnArgs a) {
           pl[qt][kk][ep] = (_Float16)(p - (float)hi);
         }
       l_run[qt] = l_run[qt] * alpha + ps;
-      // alpha == 1 leaves the accumulators as they are: skip the scaling when
-      // the running maximum held for every lane
       if (__ballot(alpha != 1.f)) {
 #pragma unroll
         for (int t = 0; t < ATT_D / 16; ++t) o[qt][t] *= alpha;

@@ -1156,6 +1156,7 @@ int launch_wsgemm(const GemmArgs& a, int bm, int nwt, int kc, bool geglu, hipStr
   DG_CASE(32, 2, 64, false)
   DG_CASE(32, 1, 64, false)
   DG_CASE(32, 1, 128, false)
+  DG_CASE(64, 1, 128, false)
   DG_CASE(32, 2, 128, false)
   DG_CASE(64, 2, 64, false)
   DG_CASE(128, 2, 64, false)

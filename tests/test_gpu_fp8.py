@@ -184,8 +184,16 @@ def test_fp8_batch_matches_single_canvas(env, fp8b4):
     dg.dg_denoise_step(cfg, f["model"].weights, one.struct, cv1.struct, rt.step_params(0, wl.n_steps, 0, False),
                        ws1.ptr, ws1.size, st)
     torch.cuda.synchronize()
+    # entropy bar: the first-order entropy change the two runs' measured logit
+    # difference allows (twice, for the second-order terms), at least 1e-3
+    tau = smp.temperature(0, wl.n_steps)
+    pz, _, _ = smp.row_statistics(zb[b], tau)
+    a = zb[b] / tau
+    abar = (pz * a).sum(-1, keepdims=True)
+    hbar = np.maximum(1e-3, 2.0 * (pz * np.abs(a - abar) * d / tau).sum(-1))
+    say(f"fp8batch4: entropy bar from the logit difference: max {hbar.max():.2e}")
     allclose_report(f"fp8batch4 canvas {b} alone vs batched entropy", cv1.entropy.cpu().numpy(),
-                    cvb.entropy.view(B, C)[b].cpu().numpy(), 1e-3, 0.0)
+                    cvb.entropy.view(B, C)[b].cpu().numpy(), hbar, 0.0)
     same = float((cv1.argmax == cvb.argmax.view(B, C)[b]).float().mean().item())
     say(f"fp8batch4 canvas {b}: argmax agreement {same:.4f}")
     cvb.tokens.copy_(tok0)
