@@ -147,7 +147,10 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void k_attn_mfma(AttnArgs a) {
         const int r = 2 * n + (lane >> 5);
         const int c = (lane & 31) ^ att_fk(r);
         const int j = min(k0 + r, a.n_keys - 1);
-        __builtin_amdgcn_global_load_lds(kbase + (int64_t)j * ATT_D + c * 8, (lds_void_t*)(st + n * 1024), 16, 0, 0);
+        // uniform base + 32-bit byte offset (< 2^31: rows x 512 B): scalar-base addressing
+        const uint32_t off = (uint32_t)(j * ATT_D + c * 8) * 2u;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(kbase) + off, (lds_void_t*)(st + n * 1024), 16,
+                                         0, 0);
       }
     } else {
 #pragma unroll
@@ -156,7 +159,9 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void k_attn_mfma(AttnArgs a) {
         const int dd = 8 * (n - 32) + (lane >> 3);
         const int c = (lane & 7) ^ (dd & 7);
         const int j = min(k0 + 8 * c, ((a.n_keys - 1) & ~7));
-        __builtin_amdgcn_global_load_lds(vbase + (int64_t)dd * a.vp + j, (lds_void_t*)(st + n * 1024), 16, 0, 0);
+        const uint32_t off = (uint32_t)(dd * a.vp + j) * 2u;  // < 2^31: 256 x pitch x 2 B
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(vbase) + off, (lds_void_t*)(st + n * 1024), 16,
+                                         0, 0);
       }
     }
   };
