@@ -560,15 +560,7 @@ int lm_head(const Ctx& c, const dg_canvas* cv, const dg_step_params* p, float* l
     a.k_split = s.d;
     return launch_rowgemm(a, &lm, c.st);
   }
-  if (s.lm8) return DG_ERR_UNSUPPORTED;
-  if (bf) {
-    const int bm = 64;  // 64-row tiles keep several waves per SIMD streaming; other row tiles hit L2
-    a.max_tiles = (T + bm - 1) / bm;
-    a.n_fb = s.nvt;
-    a.tile_fastest = 1;
-    a.k_split = s.d;
-    return launch_lmhead(a, lm, bm, c.st);
-  }
+  if (s.lm8 || bf) return DG_ERR_UNSUPPORTED;  // bf16 models have d_model % 64 == 0 (check_config)
   float* z = logits_out ? logits_out : c.at<float>(c.p.logits);
   a.epi = EPI_STORE_F32; a.out_f32 = z; a.ldo = s.V;
   DG_TRY(dense_gemm(c, a, T, s.V, s.d, 1));

@@ -110,7 +110,6 @@ struct LmArgs {
 // Launchers
 // k_gemm.hip
 int launch_wsgemm(const GemmArgs& a, int bm, int nwt, int kc, bool geglu, hipStream_t s);
-int launch_lmhead(const GemmArgs& a, const LmArgs& lm, int bm, hipStream_t s);
 // Row-resident GEMM (M rows in groups of 256, 256-feature blocks; 128 with
 // scaled activations, whose K and k_split are multiples of 256): fp32
 // partials (EPI_STORE_F32), or with lm != null the LM-head statistics.

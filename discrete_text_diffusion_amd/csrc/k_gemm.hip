@@ -217,7 +217,7 @@ template <> struct WFrag<true> { typedef uint2 type; };
 __device__ __forceinline__ bf16x8_t wfrag_bf16(bf16x8_t w) { return w; }
 __device__ __forceinline__ bf16x8_t wfrag_bf16(uint2 w) { return fp8x8_to_bf16(w); }
 
-// Main loop shared by the generic and the LM-head kernels.  WS: stages of
+// Main loop of the weight-streaming kernel.  WS: stages of
 // the weight register ring (weights are loaded WS - 1 chunks ahead of their
 // MFMAs); activations are always one chunk ahead, double buffered in LDS.
 template <int BM, int NWT, int KC, bool GEGLU, int ACT, bool FP8 = false, int WS = 2>
@@ -615,55 +615,7 @@ __device__ __forceinline__ void tile_stats4(const float* z0, int64_t pitch, int 
   }
 }
 
-constexpr int LM_KC = 64;
 constexpr int LM_ZLD = 256 + 4;  // fp32 pitch of the logit tile in LDS
-constexpr int LM_Z_BYTES = 64 * LM_ZLD * 4;
-
-template <int BM>
-__global__ __launch_bounds__(kThreads) void k_lmhead(GemmArgs a, LmArgs lm) {
-  constexpr int MW = BM / 16;
-  constexpr int XS_BYTES = 2 * BM * (LM_KC + 8) * 2;
-  constexpr int LDS = XS_BYTES > LM_Z_BYTES ? XS_BYTES : LM_Z_BYTES;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[LDS];
-  bf16_t* xs = reinterpret_cast<bf16_t*>(smem);
-  float* zt = reinterpret_cast<float*>(smem);
-
-  int tile, fb, ks;
-  decode_block(a, xcd_logical_block(a.nblocks), a.max_tiles, tile, fb, ks);
-  if (fb >= a.n_fb || tile >= a.max_tiles) return;
-  const GemmTile td{0, tile * BM, min(BM, a.M - tile * BM), 0};
-
-  f32x4_t acc[4][MW], accu[4][MW];
-  wsgemm_mainloop<BM, 4, LM_KC, false, ACT_BF16>(a, td, group_weights(a, 0, 2), fb, 0, xs, acc, accu);
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // halves of 64 rows through a 64 x 256 fp32 tile in LDS
-#pragma unroll
-  for (int half = 0; half < BM / 64; ++half) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = wave * 64 + i * 16 + (lane >> 4) * 4;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int j = half * 4 + jj;
-        const int r = jj * 16 + (lane & 15);
-        const f32x4_t v = acc[i][j];
-        *reinterpret_cast<float4*>(zt + r * LM_ZLD + c) =
-            make_float4(a.alpha * v[0], a.alpha * v[1], a.alpha * v[2], a.alpha * v[3]);
-      }
-    }
-    __syncthreads();
-    for (int rr = wave * 4; rr < 64; rr += 16) {
-      const int r = half * 64 + rr;
-      if (r < td.nrows) {
-        const int nr = min(4, td.nrows - r);
-        tile_stats4(zt + rr * LM_ZLD, LM_ZLD, nr, td.row0 + r, fb, lm,
-                    row_u2(td.row0 + r + min((int)(threadIdx.x & 63) >> 4, nr - 1), lm));
-      }
-    }
-    __syncthreads();
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Row-resident GEMM for dense weights and few rows (the denoiser's canvas):
@@ -1163,16 +1115,6 @@ int launch_wsgemm(const GemmArgs& a, int bm, int nwt, int kc, bool geglu, hipStr
   DG_CASE(256, 2, 64, false)
 #undef DG_CASE
   return -2;
-}
-
-int launch_lmhead(const GemmArgs& a0, const LmArgs& lm, int bm, hipStream_t s) {
-  GemmArgs a = a0;
-  a.n_split = 1;
-  a.nblocks = round8(a.max_tiles * a.n_fb);
-  if (bm == 64) hipLaunchKernelGGL(k_lmhead<64>, dim3(a.nblocks), dim3(kThreads), 0, s, a, lm);
-  else if (bm == 128) hipLaunchKernelGGL(k_lmhead<128>, dim3(a.nblocks), dim3(kThreads), 0, s, a, lm);
-  else return -2;
-  return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
 int launch_gemm_simple(const GemmArgs& a, hipStream_t s) {
