@@ -16,36 +16,46 @@ namespace {
 // beat it (larger, or equal with a lower expert id); rank < k is selected at
 // that rank.  The weights are the softmax over the k selected logits, summed
 // in rank order.
+// One wave per workgroup (one token): the waves never wait for each other.
+// Every partial load is issued up front and unconditionally (clamped
+// indices; the values past n_split or E are discarded), so all of them are in
+// flight together.
+constexpr int kTopkWaves = 1;
 template <int NQ>  // logits per lane: E <= 64 NQ
-__global__ __launch_bounds__(256) void k_topk(const float* part, int n_split, int64_t split_stride, int T, int E,
-                                              int k, const int32_t* forced, int32_t* ids, float* w,
-                                              float* r_out) {
-  __shared__ __attribute__((aligned(16))) float lg[4][256];
-  __shared__ float sv[4][16];
-  __shared__ int se[4][16];
+__global__ __launch_bounds__(64 * kTopkWaves) void k_topk(const float* part, int n_split, int64_t split_stride,
+                                                          int T, int E, int k, const int32_t* forced, int32_t* ids,
+                                                          float* w, float* r_out) {
+  __shared__ __attribute__((aligned(16))) float lg[kTopkWaves][256];
+  __shared__ float sv[kTopkWaves][16];
+  __shared__ int se[kTopkWaves][16];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
+  const int t = blockIdx.x * kTopkWaves + wave;
   const bool live = t < T;
-  constexpr int kMaxPerLane = 4;  // E <= 256
-  constexpr int kMaxSplit = 16;   // partial sums are added in split order
-  float r[kMaxPerLane];
+  constexpr int kMaxSplit = 16;  // partial sums are added in split order
+  const int tc = live ? t : 0;
+  float ps[NQ][kMaxSplit];
 #pragma unroll
-  for (int q = 0; q < kMaxPerLane; ++q) {
-    const int e = lane + q * 64;
-    float v = -INFINITY;
-    if (live && e < E) {
-      float ps[kMaxSplit];
+  for (int q = 0; q < NQ; ++q) {
+    const int ec = min(lane + q * 64, E - 1);
 #pragma unroll
-      for (int s = 0; s < kMaxSplit; ++s)
-        ps[s] = s < n_split ? part[(int64_t)s * split_stride + (int64_t)t * E + e] : 0.f;
-      v = ps[0];
-#pragma unroll
-      for (int s = 1; s < kMaxSplit; ++s) v += ps[s];
-      if (r_out) r_out[(int64_t)t * E + e] = v;
-    }
-    r[q] = v;
-    if (e < 256) lg[wave][e] = v;
+    for (int s = 0; s < kMaxSplit; ++s)
+      ps[q][s] = part[(int64_t)min(s, n_split - 1) * split_stride + (int64_t)tc * E + ec];
   }
+  float r[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int e = lane + q * 64;
+    float v = ps[q][0];
+#pragma unroll
+    for (int s = 1; s < kMaxSplit; ++s) v += s < n_split ? ps[q][s] : 0.f;
+    v = (live && e < E) ? v : -INFINITY;
+    if (live && e < E && r_out) r_out[(int64_t)t * E + e] = v;
+    r[q] = v;
+  }
+#pragma unroll
+  for (int q = NQ; q < 4; ++q) lg[wave][lane + q * 64] = -INFINITY;  // E <= 256
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) lg[wave][lane + q * 64] = r[q];
   // defaults keep every id in range should non-finite logits leave a rank empty
   if (lane < 16) {
     sv[wave][lane] = -INFINITY;
@@ -197,7 +207,7 @@ __global__ __launch_bounds__(1024) void k_route_sort(const int32_t* ids, int T, 
 int launch_topk(const float* part, int n_split, int64_t split_stride, int T, int E, int k, const int32_t* forced,
                 int32_t* ids, float* w, float* r_out, hipStream_t s) {
   if (E > 256 || k > 16 || k > E || n_split < 1 || n_split > 16) return -1;
-  const dim3 g(DG_CEIL_DIV(T, 4)), b(256);
+  const dim3 g(DG_CEIL_DIV(T, kTopkWaves)), b(64 * kTopkWaves);
   if (E <= 64) hipLaunchKernelGGL(k_topk<1>, g, b, 0, s, part, n_split, split_stride, T, E, k, forced, ids, w, r_out);
   else if (E <= 128) hipLaunchKernelGGL(k_topk<2>, g, b, 0, s, part, n_split, split_stride, T, E, k, forced, ids, w, r_out);
   else hipLaunchKernelGGL(k_topk<4>, g, b, 0, s, part, n_split, split_stride, T, E, k, forced, ids, w, r_out);
