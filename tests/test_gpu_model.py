@@ -139,6 +139,8 @@ def flip_margin_bound(got, want, dtype="bf16"):
     the fp32 twin), and at least the fixed near-tie threshold."""
     e = np.abs(np.asarray(got, dtype=np.float64) - np.asarray(want, dtype=np.float64))
     return max(ROUTE_EPS[dtype], 2.0 * float(e.max()) if e.size else 0.0)
+
+
 # Typical (median) router-logit error bound with forced routes.
 ROUTE_MEDIAN = {"f32": 1e-6, "bf16": 1e-4}
 
@@ -343,6 +345,45 @@ def test_denoise_loop_and_commit_match_oracle(which, request):
     nxt = pb.canvas.tokens.cpu().numpy().reshape(pb.B, pb.C)
     for b in range(pb.B):
         assert np.array_equal(nxt[b], smp.initial_canvas(pb.seeds[b], 1, pb.C, pb.shape.vocab))
+
+
+@pytest.mark.parametrize("which", ["mini", "mini8"])
+def test_skewed_routing_matches_oracle(which, request):
+    """Every token of every layer routed to the same k experts (in one order):
+    those experts' segments span several row tiles, the others receive no
+    token, and the grouped GEMMs' tile list is far below its worst case.
+    Logits and entropies against the oracle run on the same routes (weights
+    from each token's own router logits on both sides)."""
+    pb = request.getfixturevalue(which)
+    torch, dg, rt = pb.env
+    shape = pb.shape
+    T, k = pb.B * pb.C, shape.top_k
+    dg.dg_init_canvas(pb.cfg, pb.canvas.struct, 0, pb.st)
+    torch.cuda.synchronize()
+    tok = pb.canvas.tokens.cpu().numpy().reshape(pb.B, pb.C)
+    sel = np.tile(np.arange(shape.n_experts - 1, shape.n_experts - 1 - k, -1), (T, 1))  # ids E-1 .. E-k
+    force = np.stack([sel] * shape.n_layers)
+    say(f"skewed routing {which}: {T} tokens x top-{k} onto experts {sel[0].tolist()}")
+    orig = om.route
+
+    def fixed(shape_, r):
+        s_ = np.take_along_axis(r, sel, axis=1)
+        e = np.exp(s_ - s_.max(axis=1, keepdims=True))
+        return sel.copy(), e / e.sum(axis=1, keepdims=True)
+
+    om.route = fixed
+    try:
+        zo = ost.denoise_logits(shape, pb.W, pb.ocache, tok, None, pb.lm_scale)
+    finally:
+        om.route = orig
+    z = _forward_logits(pb, 0, 48, force_ids=force)
+    _err_summary(f"logits {which} (skewed routes)", z, zo)
+    allclose_report(f"logits {which} (skewed routes)", z, zo, pb.atol, RTOL)
+    tau = smp.temperature(0, 48)
+    _, Hg, _ = smp.row_statistics(z.reshape(-1, shape.vocab), tau)
+    _, Ho, _ = smp.row_statistics(zo.reshape(-1, shape.vocab), tau)
+    allclose_report(f"entropy {which} (skewed routes)", Hg, Ho,
+                    entropy_tolerance(zo.reshape(-1, shape.vocab), tau, pb.atol), 0.0)
 
 
 def test_denoise_step_is_deterministic(mini):
