@@ -386,6 +386,35 @@ def test_skewed_routing_matches_oracle(which, request):
                     entropy_tolerance(zo.reshape(-1, shape.vocab), tau, pb.atol), 0.0)
 
 
+@pytest.mark.parametrize("shape,C", [(MINI_BF16, 33), (TINY, 17)])
+def test_empty_prefix_ragged_canvas(env, shape, C):
+    """Degenerate context: no prefix (cache length 0, the canvas attends only
+    to itself) and a canvas size that is a multiple of no tile.  Logits and
+    entropies on the oracle's routes, then one full step's decisions."""
+    torch, dg, rt = env
+    pb = Problem(env, shape, 6.0, 0, C, B=1, cap_extra=-C % 8)  # bf16 caches hold a multiple of 8 rows
+    assert pb.cache.struct.length == 0 and pb.ocache.length == 0
+    say(f"empty prefix, canvas {C}, {shape.dtype}")
+    dg.dg_init_canvas(pb.cfg, pb.canvas.struct, 0, pb.st)
+    torch.cuda.synchronize()
+    tok = pb.canvas.tokens.cpu().numpy().reshape(pb.B, pb.C)
+    tr = {}
+    zo = ost.denoise_logits(pb.shape, pb.W, pb.ocache, tok, None, pb.lm_scale, trace=tr)
+    z = _forward_logits(pb, 0, 48, force_ids=_forced_ids(tr))
+    _err_summary(f"logits empty prefix C={C}", z, zo)
+    allclose_report(f"logits empty prefix C={C}", z, zo, pb.atol, RTOL)
+    tau = smp.temperature(0, 48)
+    _, Hg, _ = smp.row_statistics(z.reshape(-1, shape.vocab), tau)
+    _, Ho, _ = smp.row_statistics(zo.reshape(-1, shape.vocab), tau)
+    allclose_report(f"entropy empty prefix C={C}", Hg, Ho,
+                    entropy_tolerance(zo.reshape(-1, shape.vocab), tau, pb.atol), 0.0)
+    dg.dg_denoise_step(pb.cfg, pb.model.weights, pb.cache.struct, pb.canvas.struct, rt.step_params(0, 48),
+                       pb.ws.ptr, pb.ws.size, pb.st)
+    torch.cuda.synchronize()
+    check_sampler_invariants(pb, 0, 48, None)
+    assert pb.cache.struct.length == 0
+
+
 def test_denoise_step_is_deterministic(mini):
     pb = mini
     torch, dg, rt = pb.env
