@@ -300,6 +300,11 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
       q.seq_len = seq_len; q.pos0 = L; q.rope_base = s.rope_base;
       DG_TRY(dense_gemm(c, a, T, s.qkv, s.d, 1));
     }
+    // The causal encode keeps only the K/V rows it appends: past the last
+    // layer's QKV nothing reads its output (no LM head follows; the next chunk
+    // embeds its own tokens).  The test entry points that record or force
+    // per-layer routes run the whole layer.
+    if (causal && l == s.L - 1 && !c.router_out && !c.force_ids) break;
     // attention
     {
       Phase ph(c, DG_PHASE_ATTN);
