@@ -15,6 +15,7 @@ constexpr int kMoeBM = 32;        // row tile of the grouped expert GEMMs (bf16)
 constexpr int kSimpleBM = 16;     // row tile of the fp32 GEMMs
 constexpr int kMaxRoutePairs = 8192;
 constexpr int kMaxSplit = 16;
+constexpr int kSelfSplit = 32;   // vocabulary splits of the expected-embedding product (at most)
 constexpr int kRowPartRows = 2048;  // rows of the split-epilogue partial buffer (x split)
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
@@ -112,7 +113,7 @@ Plan make_plan(const Shape& s, int batch, int max_canvas) {
   p.lm_f = take(Tdn * s.nvt * sizeof(float4));
   p.lm_i = take(Tdn * s.nvt * sizeof(int2));
   p.logits = take(s.dt == DG_DTYPE_F32 ? Tdn * s.V * 4 : 0);
-  p.e_part = take(kMaxSplit * Tdn * s.d * 4);
+  p.e_part = take(std::max(kMaxSplit, kSelfSplit) * Tdn * s.d * 4);
   p.ebar = take(Tdn * s.d * s.act);
   p.hsc = take(Tdn * s.dsc * s.act);
   p.g_part = take((size_t)kRowPartRows * std::max(s.qkv, s.dsc) * 4);  // widest split-epilogue GEMM
@@ -221,7 +222,7 @@ int dense_gemm(const Ctx& c, GemmArgs a, int M, int N, int K, int max_split, int
     if (used_split) *used_split = a.n_split;
     return launch_wsgemm(a, bm, 1, 128, false, c.st);
   }
-  if (c.s.dt == DG_DTYPE_BF16 && K % 64 == 0 && a.act_kind != ACT_BF16_SCALED && a.epi != EPI_GEGLU &&
+  if (c.s.dt == DG_DTYPE_BF16 && K % 64 == 0 && a.epi != EPI_GEGLU &&
       a.epi != EPI_RESID) {
     a.kt_main = K / 32;
     a.n_fb = (N + 255) / 256;
@@ -478,9 +479,8 @@ int embed_canvas(const Ctx& c, const dg_canvas* cv, const dg_step_params* p) {
     if (ext) {
       a.act = cv->sc_probs; a.act_kind = ACT_F32;
     } else {
-      // carried: bf16 exp(a - m_k) with the tile-major factors exp(m_k - m) / S
-      a.act = cv->p_side; a.act_kind = bf ? ACT_BF16_SCALED : ACT_F32;
-      a.act_scale = cv->p_scale; a.scale_ld = 1; a.scale_tile_ld = T;
+      // carried: the previous step's tempered probabilities (normalised in place by its sampler)
+      a.act = cv->p_side; a.act_kind = bf ? ACT_BF16 : ACT_F32;
     }
     a.act_ld = s.V;
     a.w0 = c.w->embed_t;
@@ -488,11 +488,13 @@ int embed_canvas(const Ctx& c, const dg_canvas* cv, const dg_step_params* p) {
     a.M = T; a.N = s.d; a.K = s.V; a.n_main = 1; a.kt_main = s.V / 32;
     int n_split = 1;
     if (bf && !ext) {
-      // row-resident kernel: 128-feature blocks, vocabulary split in whole 256-id tiles
-      a.n_fb = (s.d + 127) / 128;
-      const int rg = (T + 255) / 256;
-      n_split = std::max(1, std::min(kMaxSplit, kRowTargetBlocks / std::max(1, rg * a.n_fb)));
-      a.k_split = ((s.V / 256 + n_split - 1) / n_split) * 256;
+      // row-resident kernel: 256-feature blocks (P, 134 MB at 256 rows, is
+      // re-read once per feature block), the vocabulary split so that the
+      // workgroups fill the CUs in one round (one workgroup per CU)
+      a.n_fb = (s.d + 255) / 256;
+      const int base = ((T + 255) / 256) * a.n_fb;
+      n_split = std::max(1, std::min(kSelfSplit, kRowTargetBlocks / base));
+      a.k_split = ((s.V / 32 + n_split - 1) / n_split) * 32;
       n_split = (s.V + a.k_split - 1) / a.k_split;
       a.n_split = n_split;
       DG_TRY(launch_rowgemm(a, nullptr, c.st));
@@ -579,6 +581,7 @@ int sample_and_select(const Ctx& c, dg_canvas* cv, const dg_step_params* p) {
   const int T = cv->batch * cv->canvas;
   DG_TRY(launch_row_merge(c.at<float4>(c.p.lm_f), c.at<int2>(c.p.lm_i), s.nvt, T, cv->canvas, cv->seeds, p->t,
                           p->block, cv->entropy, cv->sample, cv->argmax, cv->p_scale, c.st));
+  if (cv->p_side) DG_TRY(launch_normalize_side(s.dt == DG_DTYPE_BF16, cv->p_side, cv->p_scale, T, s.V, c.st));
   return launch_select(cv->entropy, cv->sample, cv->argmax, cv->prev_argmax, cv->tokens, cv->accepted, cv->n_accepted,
                        cv->mean_entropy, cv->stop, cv->flags, cv->seeds, cv->batch, cv->canvas, p->t, p->block, s.V,
                        p->adaptive, p->entropy_bound, p->stop_threshold, c.st);

@@ -23,8 +23,6 @@ enum GemmEpi : int32_t {
 enum ActKind : int32_t {
   ACT_BF16 = 0,         // bf16 rows
   ACT_F32 = 1,          // fp32 rows, rounded to bf16 when staged (MFMA path)
-  ACT_BF16_SCALED = 2,  // bf16 rows whose 256-wide K tiles carry a factor scale[row][k / 256] (fp32),
-                        // applied to the fp32 partial sum of each tile
 };
 
 struct QkvEpi {
@@ -46,9 +44,6 @@ struct GemmArgs {
   const void* act;
   int64_t act_ld;
   int32_t act_kind;
-  const float* act_scale;  // ACT_BF16_SCALED: factor of (row, K tile t) at row * scale_ld + t * scale_tile_ld
-  int64_t scale_ld;
-  int64_t scale_tile_ld;
   const int32_t* row_map;  // output row -> activation row (null: identity)
   // weights (the MFMA A operand), packed tiles; groups < n_main use w0/w1
   // with w_group_stride, the others use w0_alt/w1_alt.
@@ -145,6 +140,8 @@ int launch_copy_i32(int32_t* dst, const int32_t* src, int n, hipStream_t s);
 // k_sampler.hip
 int launch_row_merge(const float4* part_f, const int2* part_i, int n_vt, int rows, int C, const uint64_t* seeds,
                      int step, int block, float* H, int32_t* sample, int32_t* argmax, float* p_scale, hipStream_t s);
+// p_side *= its (row, 256-id tile) factor, in place (the carried tempered distribution)
+int launch_normalize_side(int bf16, void* p, const float* scale, int rows, int vocab, hipStream_t s);
 int launch_select(const float* H, const int32_t* sample, const int32_t* argmax, int32_t* prev_argmax, int32_t* tokens,
                   uint8_t* accepted, int32_t* n_accepted, float* mean_entropy, int32_t* stop, uint32_t* flags,
                   const uint64_t* seeds, int B, int C, int step, int block, int vocab, int adaptive, float bound,

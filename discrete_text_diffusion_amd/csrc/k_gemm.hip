@@ -167,15 +167,11 @@ template <int ACT>
 __device__ __forceinline__ uint4 load_act8(const GemmArgs& a, int arow, int k) {
   if constexpr (ACT == ACT_BF16) {
     return *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.act) + (int64_t)arow * a.act_ld + k);
-  } else if constexpr (ACT == ACT_F32) {
+  } else {
     const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.act) + (int64_t)arow * a.act_ld + k);
     const float4 x = p[0], y = p[1];
     const float f[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
     return pack8_bf16(f);
-  } else {
-    // ACT_BF16_SCALED: raw bf16; the per-(row, 256-wide K tile) scale is
-    // applied to the partial sums (see wsgemm_mainloop)
-    return *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.act) + (int64_t)arow * a.act_ld + k);
   }
 }
 
@@ -241,7 +237,7 @@ __device__ __forceinline__ void wsgemm_mainloop(const GemmArgs& a, const GemmTil
 #pragma unroll
     for (int j = 0; j < MW; ++j) {
       acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      if constexpr (GEGLU || ACT == ACT_BF16_SCALED) accu[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if constexpr (GEGLU) accu[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
   const int kb = ks * a.k_split;
@@ -331,32 +327,8 @@ __device__ __forceinline__ void wsgemm_mainloop(const GemmArgs& a, const GemmTil
         if constexpr (GEGLU) wbi = wfrag_bf16(wb[cur][s][i]);
 #pragma unroll
         for (int j = 0; j < MW; ++j) {
-          if constexpr (ACT == ACT_BF16_SCALED) {
-            accu[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wai, bx[j], accu[i][j], 0, 0, 0);
-          } else {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wai, bx[j], acc[i][j], 0, 0, 0);
-            if constexpr (GEGLU) accu[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wbi, bx[j], accu[i][j], 0, 0, 0);
-          }
-        }
-      }
-    }
-    if constexpr (ACT == ACT_BF16_SCALED) {
-      // end of a 256-wide K tile: acc += scale[row][tile] * partial
-      const int kend = kb + (c + 1) * KC;
-      if ((kend & 255) == 0) {
-        const int tile = (kend >> 8) - 1;
-#pragma unroll
-        for (int j = 0; j < MW; ++j) {
-          const int r = j * 16 + (lane & 15);
-          const int orow = td.row0 + (r < td.nrows ? r : 0);
-          const int ar = a.row_map ? a.row_map[orow] : orow;
-          const float sc0 = a.act_scale[(int64_t)ar * a.scale_ld + (int64_t)tile * a.scale_tile_ld];
-          const float sc = r < td.nrows ? sc0 : 0.f;
-#pragma unroll
-          for (int i = 0; i < NWT; ++i) {
-            acc[i][j] += sc * accu[i][j];
-            accu[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          }
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wai, bx[j], acc[i][j], 0, 0, 0);
+          if constexpr (GEGLU) accu[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wbi, bx[j], accu[i][j], 0, 0, 0);
         }
       }
     }
@@ -641,14 +613,9 @@ constexpr int LM_ZLD = 256 + 4;  // fp32 pitch of the logit tile in LDS
 // which keeps the counts exact; a wave with extra loads in flight only waits
 // longer.
 //
-// Variants:
-//  * plain (NWT 4, 256 features): fp32 partials out_f32[split][row][n] = alpha acc;
-//  * LM head (NWT 4): the sampler statistics of each 256-id tile instead;
-//  * scaled activations (NWT 2, 128 features): bf16 rows whose 256-wide K
-//    tiles carry a per-row factor; the raw products of a K tile accumulate
-//    apart and are folded in as acc += factor * partial at the tile's end.
-//    The factors, stored tile-major ([K/256][rows] fp32), are DMA'd by wave 0
-//    with the first chunk of each K tile into a two-slot LDS ring.
+// Variants (256 features per workgroup):
+//  * plain: fp32 partials out_f32[split][row][n] = alpha acc;
+//  * LM head: the sampler statistics of each 256-id tile instead.
 constexpr int RG_THREADS = 512;
 constexpr int RG_ROWS = 256;
 constexpr int RG_KC = 32;
@@ -659,9 +626,9 @@ constexpr int RG_X_BYTES = RG_ROWS * RG_ROW_BYTES;   // activations of one chunk
 constexpr int RG_XDMA = RG_ROWS / 16 / 8;            // activation instructions per wave per chunk
 constexpr int RG_ZROWS = 128;                        // LM head: logit rows staged at a time
 
-template <bool LMHEAD, bool SCALED, bool FP8>
+template <bool LMHEAD, bool FP8>
 struct RgCfg {
-  static constexpr int NWT = SCALED ? 2 : 4;
+  static constexpr int NWT = 4;
   static constexpr int BN = 4 * NWT * 16;                  // features per workgroup
   static constexpr int WTILE = FP8 ? 512 : 1024;           // bytes of a 16 x 32 weight tile
   static constexpr int WDMA = BN / 16 * WTILE / 1024 / 8;  // 1 KiB weight loads per wave per chunk
@@ -669,7 +636,7 @@ struct RgCfg {
   static constexpr int STAGE = RG_X_BYTES + BN / 16 * WTILE;  // activations + weight tiles
   static constexpr int RING = RG_SLOTS * STAGE;
   static constexpr int BODY = LMHEAD && RG_ZROWS * LM_ZLD * 4 > RING ? RG_ZROWS * LM_ZLD * 4 : RING;
-  static constexpr int EXTRA = LMHEAD ? RG_ROWS * 4 : SCALED ? 2 * RG_ROWS * 4 : 0;  // uniforms / factor ring
+  static constexpr int EXTRA = LMHEAD ? RG_ROWS * 4 : 0;  // per-row uniforms
   static constexpr int LDS = BODY + EXTRA;
 };
 
@@ -750,9 +717,9 @@ __device__ __forceinline__ void rg_lm_epilogue(const GemmArgs& a, const LmArgs& 
   }
 }
 
-template <bool LMHEAD, bool SCALED, bool FP8>
+template <bool LMHEAD, bool FP8>
 __global__ __launch_bounds__(RG_THREADS, 1) void k_rowgemm(GemmArgs a, LmArgs lm) {
-  using C = RgCfg<LMHEAD, SCALED, FP8>;
+  using C = RgCfg<LMHEAD, FP8>;
   constexpr int MW = 8;
   constexpr int NWT = C::NWT;
   // one LDS object (stages / logit tile, then the per-row uniforms or factor
@@ -780,14 +747,10 @@ __global__ __launch_bounds__(RG_THREADS, 1) void k_rowgemm(GemmArgs a, LmArgs lm
   if (nch <= 0) return;
 
   f32x4_t acc[NWT][MW];
-  f32x4_t accu[NWT][MW];  // scaled: raw sums of the current K tile (unused otherwise)
 #pragma unroll
   for (int i = 0; i < NWT; ++i)
 #pragma unroll
-    for (int j = 0; j < MW; ++j) {
-      acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      if constexpr (SCALED) accu[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int j = 0; j < MW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   bool wval[NWT];
 #pragma unroll
@@ -830,19 +793,6 @@ __global__ __launch_bounds__(RG_THREADS, 1) void k_rowgemm(GemmArgs a, LmArgs lm
     for (int e = 0; e < C::WDMA; ++e)
       __builtin_amdgcn_global_load_lds(wsrc[e] + (int64_t)cc * wstep,
                                        (lds_void_t*)(st + RG_X_BYTES + (wave * C::WDMA + e) * 1024), 16, 0, 0);
-    if constexpr (SCALED) {
-      // first chunk of a K tile: wave 0 fetches the tile's 256 row factors
-      const int k0 = kb + cc * RG_KC;
-      if (wave == 0 && c == cc && (k0 & 255) == 0) {
-        const int kt = k0 >> 8;
-        float* slot = extra + (kt & 1) * RG_ROWS;
-#pragma unroll
-        for (int i = 0; i < RG_ROWS / 64; ++i)
-          __builtin_amdgcn_global_load_lds(
-              a.act_scale + (int64_t)kt * a.scale_tile_ld + (int64_t)(row0 + min(64 * i + lane, nrows - 1)) * a.scale_ld,
-              (lds_void_t*)(slot + 64 * i), 4, 0, 0);
-      }
-    }
   };
 
   // LM head: each row's seed is loaded before the first chunks and used
@@ -862,7 +812,6 @@ __global__ __launch_bounds__(RG_THREADS, 1) void k_rowgemm(GemmArgs a, LmArgs lm
   // chunk c has completed, so chunk c + 1 + RG_AHEAD may refill its stage.
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((RG_AHEAD - 1) * C::LOADS) : "memory");
   issue(RG_AHEAD);
-  f32x4_t(&tgt)[NWT][MW] = SCALED ? accu : acc;
   bf16x8_t wf[NWT], wn[NWT], xa[2], xb[2];
   rg_read_w<NWT, FP8>(smem, cg, lane, wf);
   rg_read_x<0>(smem, rh, lane, xa);
@@ -871,13 +820,13 @@ __global__ __launch_bounds__(RG_THREADS, 1) void k_rowgemm(GemmArgs a, LmArgs lm
     const unsigned char* st = smem + (c % RG_SLOTS) * C::STAGE;
     rg_read_x<1>(st, rh, lane, xb);
     __builtin_amdgcn_sched_barrier(0);
-    rg_mfma<NWT, 0>(tgt, wf, xa);
+    rg_mfma<NWT, 0>(acc, wf, xa);
     rg_read_x<2>(st, rh, lane, xa);
     __builtin_amdgcn_sched_barrier(0);
-    rg_mfma<NWT, 1>(tgt, wf, xb);
+    rg_mfma<NWT, 1>(acc, wf, xb);
     rg_read_x<3>(st, rh, lane, xb);
     __builtin_amdgcn_sched_barrier(0);
-    rg_mfma<NWT, 2>(tgt, wf, xa);
+    rg_mfma<NWT, 2>(acc, wf, xa);
     if (c + 1 < nch) {
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((RG_AHEAD - 1) * C::LOADS)
                    : "memory");
@@ -887,25 +836,9 @@ __global__ __launch_bounds__(RG_THREADS, 1) void k_rowgemm(GemmArgs a, LmArgs lm
       rg_read_x<0>(sn, rh, lane, xa);
     }
     __builtin_amdgcn_sched_barrier(0);
-    rg_mfma<NWT, 3>(tgt, wf, xb);
+    rg_mfma<NWT, 3>(acc, wf, xb);
 #pragma unroll
     for (int i = 0; i < NWT; ++i) wf[i] = wn[i];
-    if constexpr (SCALED) {
-      const int kend = kb + (c + 1) * RG_KC;
-      if ((kend & 255) == 0) {
-        // end of K tile kt: its factors arrived with the tile's first chunk
-        const float* slot = extra + (((kend >> 8) - 1) & 1) * RG_ROWS;
-#pragma unroll
-        for (int j = 0; j < MW; ++j) {
-          const float sc = slot[rh * 128 + j * 16 + (lane & 15)];
-#pragma unroll
-          for (int i = 0; i < NWT; ++i) {
-            acc[i][j] += sc * accu[i][j];
-            accu[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          }
-        }
-      }
-    }
   }
   // drain the clamped prefetches before the LDS is reused or the wave ends
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
@@ -1001,11 +934,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_simple(GemmArgs a) {
     const int orow = td.row0 + r;
     const int arow = a.row_map ? a.row_map[orow] : orow;
     const float* x = reinterpret_cast<const float*>(a.act) + (int64_t)arow * a.act_ld;
-    const float* xs = a.act_scale ? a.act_scale + (int64_t)arow * a.scale_ld : nullptr;
-    const int64_t xs_t = a.scale_tile_ld;
     float g0 = 0.f, g1 = 0.f, u0 = 0.f, u1 = 0.f;
     for (int k = kb; k < ke; ++k) {
-      const float xv = xs ? x[k] * xs[(int64_t)(k >> 8) * xs_t] : x[k];
+      const float xv = x[k];
       g0 = fmaf(xv, w0[(int64_t)n * ldw + koff + k], g0);
       g1 = fmaf(xv, w0[(int64_t)(n + 1) * ldw + koff + k], g1);
       if (w1) {
@@ -1068,8 +999,7 @@ static void launch_t(const GemmArgs& a0, int act, hipStream_t s) {
   a.nblocks = round8(a.n_split * a.max_tiles * a.n_fb);
   dim3 grid(a.nblocks);
   if (act == ACT_BF16) hipLaunchKernelGGL((k_wsgemm<BM, NWT, KC, GEGLU, ACT_BF16, false, WS>), grid, dim3(kThreads), 0, s, a);
-  else if (act == ACT_F32) hipLaunchKernelGGL((k_wsgemm<BM, NWT, KC, GEGLU, ACT_F32, false, WS>), grid, dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL((k_wsgemm<BM, NWT, KC, GEGLU, ACT_BF16_SCALED, false, WS>), grid, dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL((k_wsgemm<BM, NWT, KC, GEGLU, ACT_F32, false, WS>), grid, dim3(kThreads), 0, s, a);
 }
 
 template <int BM, int NWT, int KC, bool GEGLU, int WS = 2>
@@ -1081,7 +1011,6 @@ static void launch_fp8(const GemmArgs& a0, hipStream_t s) {
 
 int launch_wsgemm(const GemmArgs& a, int bm, int nwt, int kc, bool geglu, hipStream_t s) {
   if (a.K % kc != 0 || a.k_split % kc != 0 || a.N % 16 != 0) return -1;
-  if (a.act_kind == ACT_BF16_SCALED && (a.k_split % 256 != 0 || a.K % 256 != 0 || geglu)) return -1;
   if (a.w_fp8) {
     // fp8 weights: bf16 rows, per-feature scales for every group present
     if (a.act_kind != ACT_BF16 || !a.ws0 || (geglu && !a.ws1)) return -1;
@@ -1147,16 +1076,14 @@ int launch_lm_partials_from_logits(const float* logits, int rows, const LmArgs& 
 
 int launch_rowgemm(const GemmArgs& a0, const LmArgs* lm, hipStream_t s) {
   GemmArgs a = a0;
-  const bool scaled = a.act_kind == ACT_BF16_SCALED;
-  const int bn = scaled ? RgCfg<false, true, false>::BN : RgCfg<false, false, false>::BN;
+  const int bn = RgCfg<false, false>::BN;
   // fp8 weights: LM head only, with 16-byte aligned per-feature scales
   if (a.w_fp8 && (!lm || !a.ws0 || reinterpret_cast<uintptr_t>(a.ws0) % 16)) return -1;
-  if (a.tiles || a.row_map || a.w1 || (a.act_kind != ACT_BF16 && !scaled) || a.M < 1 || a.N % 16 ||
+  if (a.tiles || a.row_map || a.w1 || a.act_kind != ACT_BF16 || a.M < 1 || a.N % 16 ||
       a.K % RG_KC || a.k_split % RG_KC || a.act_ld % 8)
     return -1;
   if (!lm && (a.epi != EPI_STORE_F32 || !a.out_f32 || a.ldo % 4)) return -1;
-  if (lm && (scaled || a.N % 256)) return -1;
-  if (scaled && (a.K % 256 || a.k_split % 256 || !a.act_scale)) return -1;
+  if (lm && a.N % 256) return -1;
   if (a.n_fb != (a.N + bn - 1) / bn || a.n_split < 1 || (int64_t)a.n_split * a.k_split < a.K) return -1;
   a.max_tiles = (a.M + RG_ROWS - 1) / RG_ROWS;
   a.nblocks = round8(a.max_tiles * a.n_fb * a.n_split);
@@ -1164,10 +1091,9 @@ int launch_rowgemm(const GemmArgs& a0, const LmArgs* lm, hipStream_t s) {
   if (lm) l = *lm;
   else memset(&l, 0, sizeof(l));
   const dim3 grid(a.nblocks), block(RG_THREADS);
-  if (lm && a.w_fp8) hipLaunchKernelGGL((k_rowgemm<true, false, true>), grid, block, 0, s, a, l);
-  else if (lm) hipLaunchKernelGGL((k_rowgemm<true, false, false>), grid, block, 0, s, a, l);
-  else if (scaled) hipLaunchKernelGGL((k_rowgemm<false, true, false>), grid, block, 0, s, a, l);
-  else hipLaunchKernelGGL((k_rowgemm<false, false, false>), grid, block, 0, s, a, l);
+  if (lm && a.w_fp8) hipLaunchKernelGGL((k_rowgemm<true, true>), grid, block, 0, s, a, l);
+  else if (lm) hipLaunchKernelGGL((k_rowgemm<true, false>), grid, block, 0, s, a, l);
+  else hipLaunchKernelGGL((k_rowgemm<false, false>), grid, block, 0, s, a, l);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

@@ -221,7 +221,7 @@ __global__ __launch_bounds__(256) void k_reduce_splits(const float* part, int n_
                                                       int64_t n_elems, TA* out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n_elems) return;
-  constexpr int kMaxS = 16;
+  constexpr int kMaxS = 32;
   float v[kMaxS];
 #pragma unroll
   for (int s = 0; s < kMaxS; ++s) v[s] = s < n_split ? part[(int64_t)s * split_stride + i] : 0.f;
@@ -302,7 +302,7 @@ int launch_combine_norm(int dtype, float* x, const float* Y, const int32_t* inv,
 
 int launch_reduce_splits(int dtype, const float* part, int n_split, int64_t split_stride, int64_t n_elems, void* out,
                          hipStream_t s) {
-  if (n_split < 1 || n_split > 16) return -1;
+  if (n_split < 1 || n_split > 32) return -1;
   const dim3 g((unsigned)DG_CEIL_DIV(n_elems, 256));
   if (dtype == 1) hipLaunchKernelGGL(k_reduce_splits<bf16_t>, g, dim3(256), 0, s, part, n_split, split_stride, n_elems, (bf16_t*)out);
   else hipLaunchKernelGGL(k_reduce_splits<float>, g, dim3(256), 0, s, part, n_split, split_stride, n_elems, (float*)out);

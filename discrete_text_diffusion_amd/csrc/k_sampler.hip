@@ -227,6 +227,39 @@ __global__ __launch_bounds__(1024) void k_select(SelArgs a) {
 
 }  // namespace
 
+// The carried self-conditioning input, in place: p[row][v] = exp(a - m_k)
+// (as the LM head wrote it) times the row's tile factor exp(m_k - m) / S
+// (tile-major [vocab/256][rows]) = the tempered probability, rounded once
+// more to the model dtype.  Eight ids per thread (one 256-id tile each).
+template <typename TA>
+__global__ __launch_bounds__(256) void k_normalize_side(TA* p, const float* scale, int rows, int vocab) {
+  const int64_t per_row = vocab >> 3;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)rows * per_row) return;
+  const int row = (int)(i / per_row);
+  const int v0 = (int)(i - (int64_t)row * per_row) * 8;
+  const float f = scale[(int64_t)(v0 >> 8) * rows + row];
+  TA* q = p + (int64_t)row * vocab + v0;
+  if constexpr (sizeof(TA) == 2) {
+    const uint4 u = *reinterpret_cast<const uint4*>(q);
+    uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float lo = bf2f((bf16_t)(w[j] & 0xFFFFu)) * f, hi = bf2f((bf16_t)(w[j] >> 16)) * f;
+      w[j] = (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+    }
+    *reinterpret_cast<uint4*>(q) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    float4* q4 = reinterpret_cast<float4*>(q);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float4 v = q4[j];
+      v.x *= f; v.y *= f; v.z *= f; v.w *= f;
+      q4[j] = v;
+    }
+  }
+}
+
 int launch_row_merge(const float4* part_f, const int2* part_i, int n_vt, int rows, int C, const uint64_t* seeds,
                      int step, int block, float* H, int32_t* sample, int32_t* argmax, float* p_scale, hipStream_t s) {
   hipLaunchKernelGGL(k_row_merge, dim3(rows), dim3(256), 0, s, part_f, part_i, n_vt, rows, C, seeds, step, block, H,
@@ -244,5 +277,13 @@ int launch_select(const float* H, const int32_t* sample, const int32_t* argmax, 
   int threads = 64;
   while (threads < C) threads <<= 1;
   hipLaunchKernelGGL(k_select, dim3(B), dim3(threads), 0, s, a);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+int launch_normalize_side(int bf16, void* p, const float* scale, int rows, int vocab, hipStream_t s) {
+  if (!p || !scale || rows < 1 || vocab % 256) return -1;
+  const dim3 g((unsigned)DG_CEIL_DIV((int64_t)rows * (vocab >> 3), 256));
+  if (bf16) hipLaunchKernelGGL(k_normalize_side<bf16_t>, g, dim3(256), 0, s, (bf16_t*)p, scale, rows, vocab);
+  else hipLaunchKernelGGL(k_normalize_side<float>, g, dim3(256), 0, s, (float*)p, scale, rows, vocab);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }

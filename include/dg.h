@@ -140,9 +140,10 @@ typedef struct dg_kv_cache {
  *   sc_probs     [B*C][vocab] fp32, optional external self-conditioning input
  *                (normalised probabilities); used whenever non-NULL
  *   p_side       [B*C][vocab] model dtype, and p_scale [vocab/256][B*C] fp32
- *                (tile-major): the step's tempered distribution as
- *                exp(a - m_k) and per-tile factor exp(m_k - m)/S, written by
- *                every step and read by the next one (t >= 1) as its
+ *                (tile-major): written by every step, p_side = the step's
+ *                tempered distribution softmax(z / tau_t) (formed as
+ *                exp(a - m_k) times the per-tile factor exp(m_k - m)/S, which
+ *                p_scale keeps), read by the next step (t >= 1) as its
  *                self-conditioning input.  NULL: no self-conditioning carried
  *                between steps.
  *   entropy [B*C] fp32, sample/argmax/prev_argmax [B*C] int32, accepted [B*C]
