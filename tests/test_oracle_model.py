@@ -189,6 +189,34 @@ def test_append_equals_reencode():
         assert np.allclose(a.v[layer], b.v[layer], rtol=0, atol=1e-12)
 
 
+def test_ar_step_equals_one_shot_causal_forward():
+    """The incremental AR step (prefix in the cache, one token appended per
+    step) against a one-shot causal forward of the whole sequence with no
+    cache: the logits of the last position and the argmax agree, and the
+    cache holds the whole sequence's K, V afterwards."""
+    s, W = _tiny_model(2)
+    tok = synth.tokens(2, 11, 30, s.vocab).reshape(2, 15)
+    lm = 8.0
+    a = om.KVCache(s, 2, 32)
+    ost.encode_append(s, W, a, tok[:, :12])
+    for i in range(12, 15):
+        nxt, z = ost.ar_step(s, W, a, tok[:, i], lm)
+        fresh = om.KVCache(s, 2, 32)
+        x = om.embed(s, W, tok[:, :i + 1])
+        for layer in range(s.n_layers):
+            x = om.layer_forward(s, W, layer, x, fresh, causal=True, append=True)
+        z1 = om.final_logits(s, W, x[:, -1], lm)
+        assert np.allclose(z, z1, rtol=0, atol=1e-10)
+        assert np.array_equal(nxt, np.argmax(z1, axis=-1))
+        assert a.length == i + 1
+        for layer in range(s.n_layers):
+            assert np.allclose(a.k[layer][:, :, :i + 1], fresh.k[layer][:, :, :i + 1], rtol=0, atol=1e-12)
+    # greedy ties go to the lower id
+    zt = np.zeros((1, s.vocab))
+    zt[0, [7, 3]] = 1.0
+    assert int(np.argmax(zt, axis=-1)[0]) == 3
+
+
 def test_route_topk_and_weights():
     s = TINY
     rng = np.random.default_rng(5)
