@@ -273,7 +273,8 @@ int dense_gemm(const Ctx& c, GemmArgs a, int M, int N, int K, int max_split, int
 // The layer stack over T = n_seq * seq_len tokens whose embeddings are in
 // x / n.  causal: encode (k, v appended to the cache at rows L..); else the
 // denoiser (canvas k, v kept in the workspace).
-int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, int L, bool causal) {
+int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, int L, bool causal,
+               bool need_output = false) {
   const Shape& s = c.s;
   const int T = n_seq * seq_len;
   const bool bf = s.dt == DG_DTYPE_BF16;
@@ -304,8 +305,9 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
     // The causal encode keeps only the K/V rows it appends: past the last
     // layer's QKV nothing reads its output (no LM head follows; the next chunk
     // embeds its own tokens).  The test entry points that record or force
-    // per-layer routes run the whole layer.
-    if (causal && l == s.L - 1 && !c.router_out && !c.force_ids) break;
+    // per-layer routes, and the AR step (its LM head reads the last layer's
+    // normalised output), run the whole layer.
+    if (causal && !need_output && l == s.L - 1 && !c.router_out && !c.force_ids) break;
     // attention
     {
       Phase ph(c, DG_PHASE_ATTN);
@@ -533,24 +535,17 @@ int embed_canvas(const Ctx& c, const dg_canvas* cv, const dg_step_params* p) {
                            c.at<void>(c.p.n), T, s.d, s.eps, c.st);
 }
 
-// LM head + sampler statistics.  logits_out: test path (fp32 z written).
-int lm_head(const Ctx& c, const dg_canvas* cv, const dg_step_params* p, float* logits_out) {
+// LM head + sampler statistics of the T rows of the final norm output.
+// lm: the statistics' destination and sampler parameters; lm.logits, if set
+// (test path), also receives the fp32 logits.
+int lm_head_rows(const Ctx& c, int T, LmArgs lm) {
   Phase ph(c, DG_PHASE_LMHEAD);
   const Shape& s = c.s;
   const bool bf = s.dt == DG_DTYPE_BF16;
-  const int T = cv->batch * cv->canvas;
-  LmArgs lm;
-  memset(&lm, 0, sizeof(lm));
+  float* logits_out = lm.logits;
   lm.part_f = c.at<float4>(c.p.lm_f);
   lm.part_i = c.at<int2>(c.p.lm_i);
-  lm.p_side = logits_out ? nullptr : cv->p_side;
   lm.p_side_f32 = !bf;
-  lm.logits = logits_out;
-  lm.inv_tau = 1.0f / dg_temperature(p->t, p->n_steps);
-  lm.seeds = cv->seeds;
-  lm.canvas = cv->canvas;
-  lm.step = p->t;
-  lm.block = p->block;
   lm.vocab = s.V;
   GemmArgs a = base_args();
   a.act = c.at<void>(c.p.n); a.act_ld = s.d; a.act_kind = bf ? ACT_BF16 : ACT_F32;
@@ -573,6 +568,60 @@ int lm_head(const Ctx& c, const dg_canvas* cv, const dg_step_params* p, float* l
   DG_TRY(dense_gemm(c, a, T, s.V, s.d, 1));
   lm.logits = nullptr;
   return launch_lm_partials_from_logits(z, T, lm, c.st);
+}
+
+// The canvas LM head: statistics at the step's temperature, the next step's
+// self-conditioning input (unless the logits are being captured).
+int lm_head(const Ctx& c, const dg_canvas* cv, const dg_step_params* p, float* logits_out) {
+  LmArgs lm;
+  memset(&lm, 0, sizeof(lm));
+  lm.p_side = logits_out ? nullptr : cv->p_side;
+  lm.logits = logits_out;
+  lm.inv_tau = 1.0f / dg_temperature(p->t, p->n_steps);
+  lm.seeds = cv->seeds;
+  lm.canvas = cv->canvas;
+  lm.step = p->t;
+  lm.block = p->block;
+  return lm_head_rows(c, cv->batch * cv->canvas, lm);
+}
+
+// One autoregressive decode step: the latest token of each of `batch`
+// sequences is encoded causally at row L of its cache (K/V appended) through
+// the whole layer stack, the LM head runs on those rows, and the next token
+// is their argmax (the sampler's row merge: greedy, ties to the lower id).
+int ar_impl(const dg_model_config* cfg, const dg_weights* w, dg_kv_cache* cache, const int32_t* d_tokens,
+            int32_t batch, int32_t* d_next, float* d_logits, void* d_ws, size_t ws_bytes, void* stream) {
+  DG_TRY(check_config(cfg));
+  DG_TRY(check_weights(cfg, w));
+  if (!d_tokens || !d_next || batch < 1) return DG_ERR_INVALID_ARG;
+  DG_TRY(check_cache(cfg, cache, batch));
+  if ((int64_t)cache->length + 1 > cache->capacity) return DG_ERR_KV_CAPACITY;
+  Ctx c;
+  c.s = shape_of(cfg);
+  c.p = make_plan(c.s, batch, 1);
+  DG_TRY(check_ws(c.p, d_ws, ws_bytes));
+  if ((int64_t)batch * c.s.k > kMaxRoutePairs || batch > route_max_tokens()) return DG_ERR_UNSUPPORTED;
+  c.ws = (char*)d_ws;
+  c.st = (hipStream_t)stream;
+  c.w = w;
+  const bool bf = c.s.dt == DG_DTYPE_BF16;
+  DG_TRY(launch_embed_norm(bf, d_tokens, w->embed, nullptr, 0, 0, c.at<float>(c.p.x), c.at<void>(c.p.n), batch,
+                           c.s.d, c.s.eps, c.st));
+  DG_TRY(run_layers(c, cache, batch, 1, cache->length, true, true));
+  // The statistics carry a sampling candidate drawn from per-row seeds; the
+  // greedy step reads none of it, so the seeds point at workspace words
+  // (the routing ids buffer, done with by now).
+  LmArgs lm;
+  memset(&lm, 0, sizeof(lm));
+  lm.logits = d_logits;
+  lm.inv_tau = 1.0f;
+  lm.seeds = c.at<uint64_t>(c.p.ids);
+  lm.canvas = 1;
+  DG_TRY(lm_head_rows(c, batch, lm));
+  DG_TRY(launch_row_merge(c.at<float4>(c.p.lm_f), c.at<int2>(c.p.lm_i), c.s.nvt, batch, 1, lm.seeds, 0, 0,
+                          c.at<float>(c.p.wts), c.at<int32_t>(c.p.inv), d_next, nullptr, c.st));
+  cache->length += 1;
+  return DG_OK;
 }
 
 int sample_and_select(const Ctx& c, dg_canvas* cv, const dg_step_params* p) {
@@ -721,6 +770,17 @@ int dg_denoise_step_traced(const dg_model_config* cfg, const dg_weights* w, cons
   DG_TRY(run_layers(c, cache, cv->batch, cv->canvas, cache->length, false));
   DG_TRY(lm_head(c, cv, p, nullptr));
   return sample_and_select(c, cv, p);
+}
+
+int dg_ar_step(const dg_model_config* cfg, const dg_weights* w, dg_kv_cache* cache, const int32_t* d_tokens,
+               int32_t batch, int32_t* d_next, void* d_ws, size_t ws_bytes, void* stream) {
+  return ar_impl(cfg, w, cache, d_tokens, batch, d_next, nullptr, d_ws, ws_bytes, stream);
+}
+
+int dg_test_ar_step(const dg_model_config* cfg, const dg_weights* w, dg_kv_cache* cache, const int32_t* d_tokens,
+                    int32_t batch, int32_t* d_next, float* d_logits, void* d_ws, size_t ws_bytes, void* stream) {
+  if (!d_logits) return DG_ERR_INVALID_ARG;
+  return ar_impl(cfg, w, cache, d_tokens, batch, d_next, d_logits, d_ws, ws_bytes, stream);
 }
 
 int dg_commit_block(const dg_model_config* cfg, const dg_weights* w, dg_kv_cache* cache, dg_canvas* cv,

@@ -245,6 +245,22 @@ int dg_commit_block(const dg_model_config* cfg, const dg_weights* w, dg_kv_cache
                     dg_canvas* canvas, const dg_step_params* p, void* d_ws, size_t ws_bytes,
                     void* stream);
 
+/* One autoregressive decode step on the same weights (DiffusionGemma
+ * Technical Report digest, Figure 11: the single-token AR step the diffusion
+ * step's latency is set against).  d_tokens [batch] (device int32, each in
+ * [0, vocab)) is the latest token of each sequence; it is encoded causally at
+ * position cache->length through every layer, its K/V rows appended, and the
+ * LM head runs on those batch rows.  d_next [batch] (device int32) receives
+ * the greedy next token, argmax of the logits, ties to the lower id.
+ * cache->length += 1 on success.  Workspace: dg_workspace_bytes(cfg, batch, 1).
+ * Errors: DG_ERR_INVALID_ARG for null tokens / outputs or batch < 1,
+ * DG_ERR_KV_CAPACITY if the cache is full (nothing written),
+ * DG_ERR_WORKSPACE if the workspace is short, DG_ERR_UNSUPPORTED above the
+ * routing limits (batch <= 1024, batch * top_k <= 8192). */
+int dg_ar_step(const dg_model_config* cfg, const dg_weights* w, dg_kv_cache* cache,
+               const int32_t* d_tokens, int32_t batch, int32_t* d_next, void* d_ws,
+               size_t ws_bytes, void* stream);
+
 const char* dg_status_string(int status);
 
 /* ---- measurement ---- */
@@ -324,6 +340,13 @@ int dg_test_forward_logits(const dg_model_config* cfg, const dg_weights* w, cons
 int dg_test_encode_append(const dg_model_config* cfg, const dg_weights* w, dg_kv_cache* cache,
                           const int32_t* d_tokens, int32_t batch, int32_t n_tokens, const int32_t* d_force_ids,
                           float* d_router_logits, void* d_ws, size_t ws_bytes, void* stream);
+
+/* dg_ar_step that also stores the fp32 logits of the decoded rows in
+ * d_logits [batch][vocab] (device, caller-owned, required: null is
+ * DG_ERR_INVALID_ARG).  Same workspace, errors and cache update. */
+int dg_test_ar_step(const dg_model_config* cfg, const dg_weights* w, dg_kv_cache* cache,
+                    const int32_t* d_tokens, int32_t batch, int32_t* d_next, float* d_logits,
+                    void* d_ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

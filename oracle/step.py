@@ -36,20 +36,21 @@ def encode_append(shape: ModelShape, W: Weights, cache: KVCache, tokens: np.ndar
     cache.length += n
 
 
-def ar_step(shape: ModelShape, W: Weights, cache: KVCache, tokens, lm_scale: float):
+def ar_step(shape: ModelShape, W: Weights, cache: KVCache, tokens, lm_scale: float,
+            trace: dict | None = None):
     """One autoregressive decode step on the same weights, the baseline the
     pages set the diffusion step against (DiffusionGemma Technical Report
     digest, Figure 11, the per-step cost of AR decoding): each sequence's
     latest token, tokens [B], is encoded causally at position L and appended
     to the cache (the encoder's path for a one-token block), and the next
     token is the argmax of its logits (greedy, ties to the lower id).
-    Returns (next [B], z [B, V])."""
+    Returns (next [B], z [B, V]); trace as in ``denoise_logits``."""
     tokens = np.asarray(tokens).reshape(-1, 1)
     if cache.length + 1 > cache.capacity:
         raise ValueError("KV capacity exceeded")
     x = embed(shape, W, tokens)
     for layer in range(shape.n_layers):
-        x = layer_forward(shape, W, layer, x, cache, causal=True, append=True)
+        x = layer_forward(shape, W, layer, x, cache, causal=True, append=True, trace=trace)
     cache.length += 1
     z = final_logits(shape, W, x[:, -1], lm_scale)
     return np.argmax(z, axis=-1), z

@@ -430,3 +430,89 @@ def test_denoise_step_is_deterministic(mini):
         outs.append([x.clone() for x in (pb.canvas.tokens, pb.canvas.entropy, pb.canvas.p_side, pb.canvas.p_scale)])
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+# Router-logit margin under which an autoregressive row's route may differ
+# from the oracle's with no forcing available: twice the largest bf16
+# router-logit error measured with forced routes (~5e-3), and the fp32 bar.
+AR_FLIP = {"f32": 1e-5, "bf16": 1e-2}
+
+
+@pytest.mark.parametrize("which", ["tiny", "mini", "mini8"])
+def test_ar_decode_matches_oracle(env, which):
+    """Greedy single-token decode on the same weights: every step's logits,
+    next token and appended K/V rows against the oracle's, teacher-forced with
+    the oracle's greedy tokens so both sides see the same inputs.  Steps
+    alternate the logits-capturing entry with the product entry (next token
+    only).  The cache is sized to the last step, so one more step is refused
+    without writing anything."""
+    torch, dg, rt = env
+    shape, lm_scale, prefix, B = {
+        "tiny": (WORKLOADS["tiny"].model, WORKLOADS["tiny"].lm_scale, 24, 1),
+        "mini": (MINI_BF16, 6.0, 40, 2),
+        "mini8": (MINI_FP8, 6.0, 40, 2),
+    }[which]
+    n_dec = 8
+    pb = Problem(env, shape, lm_scale, prefix, 1, B=B, cap_extra=n_dec - 1)
+    assert pb.cap == prefix + n_dec and pb.cap % 8 == 0
+    ws = rt.Workspace(pb.cfg, B, 1)
+    pb.encode_prefix()
+    V = shape.vocab
+    d_tok = torch.empty(B, dtype=torch.int32, device="cuda")
+    d_next = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    d_logits = torch.empty(B * V, dtype=torch.float32, device="cuda")
+    cur = np.array([synth.tokens(b, synth.TID["prompt"], 1, V, start=prefix)[0] for b in range(B)])
+    compared = []
+    for i in range(n_dec):
+        tr = {}
+        nxt_o, zo = ost.ar_step(shape, pb.W, pb.ocache, cur, pb.lm_scale, trace=tr)
+        d_tok.copy_(torch.from_numpy(cur.astype(np.int32)))
+        L0 = pb.cache.length
+        say(f"AR {which} step {i} at position {L0} (B={B})")
+        if i % 2 == 0:
+            dg.dg_test_ar_step(pb.cfg, pb.model.weights, pb.cache.struct, d_tok.data_ptr(), B, d_next.data_ptr(),
+                               d_logits.data_ptr(), ws.ptr, ws.size, pb.st)
+        else:
+            dg.dg_ar_step(pb.cfg, pb.model.weights, pb.cache.struct, d_tok.data_ptr(), B, d_next.data_ptr(),
+                          ws.ptr, ws.size, pb.st)
+        torch.cuda.synchronize()
+        assert pb.cache.length == L0 + 1 == pb.ocache.length
+        ok = np.all(_route_margins(shape, tr) >= AR_FLIP[shape.dtype], axis=0)  # [B]: no near-tie route
+        compared.append(ok)
+        if i % 2 == 0 and ok.any():
+            z = d_logits.cpu().numpy().reshape(B, V)
+            _err_summary(f"AR logits {which} step {i}", z[ok], zo[ok])
+            allclose_report(f"AR logits {which} step {i}", z[ok], zo[ok], pb.atol, RTOL)
+        nxt = d_next.cpu().numpy()
+        top = -np.sort(-zo, axis=1)
+        bar = 2.0 * (pb.atol + RTOL * np.abs(top[:, 0]))  # two logits each off by the logit bar
+        clear = ok & (top[:, 0] - top[:, 1] > bar)
+        assert np.array_equal(nxt[clear], nxt_o[clear]), (nxt, nxt_o)
+        # elsewhere the GPU's pick must be one of the oracle's near-maximal ids
+        assert np.all((nxt >= 0) & (nxt < V))
+        assert np.all(zo[np.arange(B), nxt][ok] >= top[ok, 0] - bar[ok])
+        # the appended K/V rows, for sequences with no near-tie route
+        for name, oc in (("k", pb.ocache.k), ("v", pb.ocache.v)):
+            got = pb.cache.view(name).float().cpu().numpy()
+            for b in np.nonzero(ok)[0]:
+                for l in range(shape.n_layers):
+                    allclose_report(f"AR cache {name} L{l} b{b} row {L0}", got[l][b][:, L0], oc[l][b][:, L0],
+                                    pb.atol, RTOL)
+        cur = nxt_o
+    compared = np.stack(compared)
+    say(f"AR {which}: {int(compared.sum())} of {compared.size} rows compared")
+    assert compared.mean() >= 0.5
+    pb.compare_cache(prefix)  # the prompt rows are untouched
+    # a full cache: refused before anything is written
+    k0, v0 = pb.cache.k.clone(), pb.cache.v.clone()
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_ar_step(pb.cfg, pb.model.weights, pb.cache.struct, d_tok.data_ptr(), B, d_next.data_ptr(),
+                      ws.ptr, ws.size, pb.st)
+    assert e.value.status == dg.DG_ERR_KV_CAPACITY
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_test_ar_step(pb.cfg, pb.model.weights, pb.cache.struct, d_tok.data_ptr(), B, d_next.data_ptr(),
+                           None, ws.ptr, ws.size, pb.st)
+    assert e.value.status == dg.DG_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert pb.cache.length == pb.cap
+    assert torch.equal(k0, pb.cache.k) and torch.equal(v0, pb.cache.v)
