@@ -241,6 +241,22 @@ def moe_up_bytes(shape, T, experts=None):
     return w + act + rows * de * 2
 
 
+def ar_step_bytes(shape, L):
+    """HBM bytes one single-token decode step at cache length L must read:
+    every layer's QKV, O and router weights, its top_k routed experts and the
+    shared expert (gate, up, down), the K and V rows [0, L] of its cache, and
+    the LM head.  Per-feature fp8 scales, the embedding row and the
+    activations (a few KB) are left out."""
+    d = shape.d_model
+    wb = 4 if shape.dtype == "f32" else 2
+    eb = 1 if shape.expert_dtype == "fp8" else wb
+    lb = 1 if shape.lm_dtype == "fp8" else wb
+    dense = (shape.qkv_rows * d + d * shape.q_dim + shape.n_experts * d) * wb
+    experts = (shape.top_k * shape.d_expert + shape.d_shared) * 3 * d * eb
+    kv = 2 * (L + 1) * shape.kv_dim * wb
+    return shape.n_layers * (dense + experts + kv) + shape.vocab * d * lb
+
+
 def cpu_baseline(wl, target_s: float):
     """The oracle on a bounded sample of the workload: one full-width
     denoising layer over the 256-token canvas against a 4096-row cache, the
@@ -412,6 +428,31 @@ def main():
     torch.cuda.synchronize()
     ms48 = f0.elapsed_time(f1)
 
+    # single-token greedy decode on the same weights and prefix cache: each
+    # step's next token is the following step's input (rows L.. appended,
+    # then dropped again)
+    ar_a = prompt.view(B, wl.prefix)[:, -1].contiguous()
+    ar_b = torch.empty_like(ar_a)
+    n_ar = min(64, cache.struct.capacity - L)
+
+    def ar_run(n):
+        src, dst = ar_a, ar_b
+        for _ in range(n):
+            dg.dg_ar_step(cfg, model.weights, cache.struct, src.data_ptr(), B, dst.data_ptr(), ws.ptr, ws.size, st)
+            src, dst = dst, src
+
+    ar_run(4)
+    cache.struct.length = L
+    torch.cuda.synchronize()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record()
+    ar_run(n_ar)
+    a1.record()
+    torch.cuda.synchronize()
+    cache.struct.length = L
+    ar_ms = a0.elapsed_time(a1) / n_ar
+    ar_bytes = ar_step_bytes(shape, L + n_ar // 2)
+
     breakdown = {}
     if not args.no_breakdown:
         pool2 = EventPool(hip, 2 * (shape.n_layers * 7 + 8))
@@ -480,6 +521,12 @@ def main():
         "canvas_tok_s_12_excl_commit": round(T / (12 * step_ms * 1e-3), 2),
         "canvas_tok_s_48_incl_commit": round(T / (ms48 * 1e-3), 2),
         "canvas_tok_s_48_excl_commit": round(T / ((ms48 - commit_ms) * 1e-3), 2),
+        "ar_step_ms": round(ar_ms, 4),
+        "ar_tok_s": round(B / (ar_ms * 1e-3), 1),
+        "ar_bytes_per_step": int(ar_bytes),
+        "ar_hbm_gbs": round(ar_bytes / (ar_ms * 1e-3) / 1e9, 1),
+        "ar_hbm_frac": round(ar_bytes / (ar_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "denoise_step_over_ar_step": round(step_ms / ar_ms, 3),
         "accepted_last_step": n_acc,
         "accepted_per_step": acc_steps,
         "accepted_mean": round(sum(acc_steps) / len(acc_steps), 2),
