@@ -98,6 +98,35 @@ def pmc_step(workload: str):
     print("[pmc-step] step done", file=sys.stderr, flush=True)
 
 
+def ar_profile(workload: str, n: int):
+    """n single-token greedy decode steps of the workload's model at its prefix
+    length (kernel profiles of the decode step).  The prefix cache holds N(0,1)
+    rows instead of an encoded prompt, so that after the weight set-up the only
+    kernels in the run are the decode steps'."""
+    import torch
+    from discrete_text_diffusion_amd import runtime as rt
+    import discrete_text_diffusion_amd as dg
+    from synth.configs import WORKLOADS
+    wl = WORKLOADS[workload]
+    shape, B = wl.model, wl.batch
+    print(f"[ar-profile] building {workload}", file=sys.stderr, flush=True)
+    model = rt.DeviceModel(shape, wl.lm_scale)
+    cache = rt.DeviceCache(shape, B, wl.prefix + n + (-(wl.prefix + n)) % 8)
+    cache.fill_random(wl.prefix)
+    cache.struct.length = wl.prefix
+    ws = rt.Workspace(model.cfg, B, 1)
+    st = rt.stream_handle()
+    a = torch.zeros(B, dtype=torch.int32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    print(f"[ar-profile] {n} decode steps from position {wl.prefix}", file=sys.stderr, flush=True)
+    for _ in range(n):
+        dg.dg_ar_step(model.cfg, model.weights, cache.struct, a.data_ptr(), B, b.data_ptr(), ws.ptr, ws.size, st)
+        a, b = b, a
+    torch.cuda.synchronize()
+    print("[ar-profile] done", file=sys.stderr, flush=True)
+
+
 def _counter_rows(d):
     """(dispatch id, kernel name, counter name, value) of every counter record
     under d: rocprofv3's database output (SQLite, the counters_collection
@@ -320,7 +349,11 @@ def main():
     ap.add_argument("--pmc-step", action="store_true", help="one denoising step only (counter runs)")
     ap.add_argument("--pmc-copy", action="store_true", help="counter calibration copy only")
     ap.add_argument("--pmc-summarize", nargs=5, metavar=("F", "W", "CF", "CW", "OUT"))
+    ap.add_argument("--ar-profile", type=int, metavar="N", help="N single-token decode steps only (kernel profiles)")
     args = ap.parse_args()
+    if args.ar_profile:
+        ar_profile(args.workload, args.ar_profile)
+        return
     if args.pmc_summarize:
         pmc_summarize(*args.pmc_summarize)
         return

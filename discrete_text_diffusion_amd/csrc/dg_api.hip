@@ -15,6 +15,7 @@ constexpr int kMoeBM = 32;        // row tile of the grouped expert GEMMs (bf16)
 constexpr int kSimpleBM = 16;     // row tile of the fp32 GEMMs
 constexpr int kMaxRoutePairs = 8192;
 constexpr int kMaxSplit = 16;
+constexpr int kAttMaxSplit = 32;  // key splits of one attention launch (the merge takes any count)
 constexpr int kSelfSplit = 32;   // vocabulary splits of the expected-embedding product (at most)
 constexpr int kRowPartRows = 2048;  // rows of the split-epilogue partial buffer (x split)
 
@@ -211,6 +212,26 @@ int dense_gemm(const Ctx& c, GemmArgs a, int M, int N, int K, int max_split, int
   if (c.s.dt == DG_DTYPE_BF16 && M <= kWsMaxRows && K % 128 == 0 && a.act_kind == ACT_BF16 &&
       a.epi != EPI_GEGLU) {
     const bool store = a.epi == EPI_STORE_F32;
+    // A handful of rows (the single-token decode step): a fused epilogue
+    // without a K split would run one workgroup per 64 features, too few to
+    // keep the weight stream going, so K is split through fp32 partials in the
+    // workspace and the summing epilogue kernel applies the epilogue.
+    const int64_t part_rows = (int64_t)kRowPartRows * std::max(c.s.qkv, c.s.dsc);
+    if (!store && (int64_t)((M + 63) / 64) * ((N + 63) / 64) * 4 <= kTargetBlocks &&
+        (int64_t)M * N * kRowMaxSplit <= part_rows) {
+      a.kt_main = K / 32;
+      a.n_fb = (N + 63) / 64;
+      a.max_tiles = (M + 31) / 32;
+      a.tile_fastest = 1;
+      const int sp = pick_split(a.max_tiles * a.n_fb, K, 128, kRowMaxSplit);
+      a.k_split = ((K / 128 + sp - 1) / sp) * 128;
+      a.n_split = (K + a.k_split - 1) / a.k_split;
+      GemmArgs pa = a;
+      pa.epi = EPI_STORE_F32; pa.out_f32 = c.at<float>(c.p.g_part); pa.ldo = N; pa.split_stride = (int64_t)M * N;
+      pa.alpha = 1.0f;
+      DG_TRY(launch_wsgemm(pa, 32, 1, 128, false, c.st));
+      return launch_split_epilogue(a, pa.out_f32, a.n_split, pa.split_stride, N, c.st);
+    }
     const int bm = store ? 32 : 64;
     a.kt_main = K / 32;
     a.n_fb = (N + 63) / 64;
@@ -316,9 +337,11 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
       if (bf) {
         const int G = s.nq / s.nkv;
         const int base_blocks = n_seq * s.nkv * ((seq_len + 128 / G - 1) / (128 / G));
-        split = std::max(1, (256 + base_blocks - 1) / base_blocks);         // ~1 workgroup (4 waves) per CU
-        split = std::min(split, std::max(1, (n_keys + 255) / 256));         // >= 4 key tiles per split
-        split = std::min(split, std::min(kMaxSplit, std::max(1, c.p.att_rows / T)));
+        split = std::max(1, (256 + base_blocks - 1) / base_blocks);         // ~1 workgroup per CU
+        // >= 4 key tiles per split; >= 2 when there are few query blocks
+        // (the decode step: 8 workgroups before the split)
+        split = std::min(split, std::max(1, (n_keys + 255) / 256 * (base_blocks < 32 ? 2 : 1)));
+        split = std::min(split, std::min(kAttMaxSplit, std::max(1, c.p.att_rows / T)));
       }
       DG_TRY(launch_attention(bf, c.at<void>(c.p.q), s.qdim, kc, vc, c_seq, c_head, cache->capacity, n_keys, L,
                               causal ? 1 : 0, seq_len, n_seq, s.nq, s.nkv, s.dh, split, c.at<float>(c.p.att_o),

@@ -323,35 +323,46 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // token * n_q + head
   if (row >= T * a.n_q) return;
   const int lane = threadIdx.x & 63;
-  constexpr int kMaxS = 16;
-  float2 ml[kMaxS];
-  float4 v[kMaxS];
-#pragma unroll
-  for (int s = 0; s < kMaxS; ++s) {
-    const int64_t pr = (int64_t)s * T * a.n_q + row;
-    ml[s] = s < a.n_split ? a.part_ml[pr] : make_float2(-INFINITY, 0.f);
-    v[s] = s < a.n_split ? *reinterpret_cast<const float4*>(a.part_o + pr * a.d + 4 * lane)
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+  // splits in passes of kS (all loads of a pass issued before their use);
+  // the sums run in split order whatever the pass size
+  constexpr int kS = 16;
+  const int64_t sstride = T * a.n_q;
   float M = -INFINITY;
+  for (int s0 = 0; s0 < a.n_split; s0 += kS) {
+    float mx[kS];
 #pragma unroll
-  for (int s = 0; s < kMaxS; ++s) M = fmaxf(M, ml[s].x);
+    for (int j = 0; j < kS; ++j) mx[j] = s0 + j < a.n_split ? a.part_ml[(s0 + j) * sstride + row].x : -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kS; ++j) M = fmaxf(M, mx[j]);
+  }
   const float sh = M == -INFINITY ? 0.f : M;
-  float w[kMaxS], L = 0.f;
+  float L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < a.n_split; s0 += kS) {
+    float2 ml[kS];
+    float4 v[kS];
 #pragma unroll
-  for (int s = 0; s < kMaxS; ++s) {
-    w[s] = exp2f(ml[s].x - sh);
-    L += w[s] * ml[s].y;
+    for (int j = 0; j < kS; ++j) {
+      const int64_t pr = (s0 + j) * sstride + row;
+      ml[j] = s0 + j < a.n_split ? a.part_ml[pr] : make_float2(-INFINITY, 0.f);
+      v[j] = s0 + j < a.n_split ? *reinterpret_cast<const float4*>(a.part_o + pr * a.d + 4 * lane)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float w[kS];
+#pragma unroll
+    for (int j = 0; j < kS; ++j) {
+      w[j] = exp2f(ml[j].x - sh);
+      L += w[j] * ml[j].y;
+    }
+#pragma unroll
+    for (int j = 0; j < kS; ++j) {
+      acc.x += w[j] * v[j].x;
+      acc.y += w[j] * v[j].y;
+      acc.z += w[j] * v[j].z;
+      acc.w += w[j] * v[j].w;
+    }
   }
   const float inv_l = L > 0.f ? 1.f / L : 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-  for (int s = 0; s < kMaxS; ++s) {
-    acc.x += w[s] * v[s].x;
-    acc.y += w[s] * v[s].y;
-    acc.z += w[s] * v[s].z;
-    acc.w += w[s] * v[s].w;
-  }
   TA* o = reinterpret_cast<TA*>(a.out) + row * a.d + 4 * lane;
   o[0] = to_act<TA>(acc.x * inv_l);
   o[1] = to_act<TA>(acc.y * inv_l);

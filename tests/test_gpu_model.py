@@ -438,25 +438,38 @@ def test_denoise_step_is_deterministic(mini):
 AR_FLIP = {"f32": 1e-5, "bf16": 1e-2}
 
 
-@pytest.mark.parametrize("which", ["tiny", "mini", "mini8"])
+@pytest.mark.parametrize("which", ["tiny", "mini", "mini8", "mini_long"])
 def test_ar_decode_matches_oracle(env, which):
     """Greedy single-token decode on the same weights: every step's logits,
     next token and appended K/V rows against the oracle's, teacher-forced with
     the oracle's greedy tokens so both sides see the same inputs.  Steps
     alternate the logits-capturing entry with the product entry (next token
     only).  The cache is sized to the last step, so one more step is refused
-    without writing anything."""
+    without writing anything.  mini_long decodes after a 4096-row seeded
+    N(0,1) cache (no encoder), where the attention splits the keys 32 ways."""
     torch, dg, rt = env
     shape, lm_scale, prefix, B = {
         "tiny": (WORKLOADS["tiny"].model, WORKLOADS["tiny"].lm_scale, 24, 1),
         "mini": (MINI_BF16, 6.0, 40, 2),
         "mini8": (MINI_FP8, 6.0, 40, 2),
+        "mini_long": (MINI_BF16, 6.0, 4096, 1),
     }[which]
     n_dec = 8
     pb = Problem(env, shape, lm_scale, prefix, 1, B=B, cap_extra=n_dec - 1)
     assert pb.cap == prefix + n_dec and pb.cap % 8 == 0
     ws = rt.Workspace(pb.cfg, B, 1)
-    pb.encode_prefix()
+    if which == "mini_long":
+        pb.cache.fill_random(prefix, seed=0, std=1.0)
+        pb.cache.struct.length = prefix
+        for name, tid in (("k", synth.TID["kv_k"]), ("v", synth.TID["kv_v"])):
+            vals = synth.bf16_bits_to_f32(synth.normal(0, tid, (shape.n_layers, B, shape.n_kv_heads, prefix,
+                                                                shape.d_head), 1.0))
+            for l in range(shape.n_layers):
+                getattr(pb.ocache, name)[l][:, :, :prefix] = vals[l].astype(np.float64)
+        pb.ocache.length = prefix
+        torch.cuda.synchronize()
+    else:
+        pb.encode_prefix()
     V = shape.vocab
     d_tok = torch.empty(B, dtype=torch.int32, device="cuda")
     d_next = torch.full((B,), -1, dtype=torch.int32, device="cuda")
