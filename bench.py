@@ -346,6 +346,7 @@ def main():
     ap.add_argument("--workload", default="full30")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--no-ar", action="store_true", help="skip the single-token decode timing")
     ap.add_argument("--pmc-step", action="store_true", help="one denoising step only (counter runs)")
     ap.add_argument("--pmc-copy", action="store_true", help="counter calibration copy only")
     ap.add_argument("--pmc-summarize", nargs=5, metavar=("F", "W", "CF", "CW", "OUT"))
@@ -474,17 +475,27 @@ def main():
             dg.dg_ar_step(cfg, model.weights, cache.struct, src.data_ptr(), B, dst.data_ptr(), ws.ptr, ws.size, st)
             src, dst = dst, src
 
-    ar_run(4)
-    cache.struct.length = L
-    torch.cuda.synchronize()
-    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a0.record()
-    ar_run(n_ar)
-    a1.record()
-    torch.cuda.synchronize()
-    cache.struct.length = L
-    ar_ms = a0.elapsed_time(a1) / n_ar
-    ar_bytes = ar_step_bytes(shape, L + n_ar // 2)
+    ar = {}
+    if not args.no_ar:
+        ar_run(4)
+        cache.struct.length = L
+        torch.cuda.synchronize()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        ar_run(n_ar)
+        a1.record()
+        torch.cuda.synchronize()
+        cache.struct.length = L
+        ar_ms = a0.elapsed_time(a1) / n_ar
+        ar_bytes = ar_step_bytes(shape, L + n_ar // 2)
+        ar = {
+            "ar_step_ms": round(ar_ms, 4),
+            "ar_tok_s": round(B / (ar_ms * 1e-3), 1),
+            "ar_bytes_per_step": int(ar_bytes),
+            "ar_hbm_gbs": round(ar_bytes / (ar_ms * 1e-3) / 1e9, 1),
+            "ar_hbm_frac": round(ar_bytes / (ar_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "denoise_step_over_ar_step": round(step_ms / ar_ms, 3),
+        }
 
     breakdown = {}
     if not args.no_breakdown:
@@ -554,12 +565,7 @@ def main():
         "canvas_tok_s_12_excl_commit": round(T / (12 * step_ms * 1e-3), 2),
         "canvas_tok_s_48_incl_commit": round(T / (ms48 * 1e-3), 2),
         "canvas_tok_s_48_excl_commit": round(T / ((ms48 - commit_ms) * 1e-3), 2),
-        "ar_step_ms": round(ar_ms, 4),
-        "ar_tok_s": round(B / (ar_ms * 1e-3), 1),
-        "ar_bytes_per_step": int(ar_bytes),
-        "ar_hbm_gbs": round(ar_bytes / (ar_ms * 1e-3) / 1e9, 1),
-        "ar_hbm_frac": round(ar_bytes / (ar_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "denoise_step_over_ar_step": round(step_ms / ar_ms, 3),
+        **ar,
         "accepted_last_step": n_acc,
         "accepted_per_step": acc_steps,
         "accepted_mean": round(sum(acc_steps) / len(acc_steps), 2),
