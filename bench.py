@@ -127,6 +127,64 @@ def ar_profile(workload: str, n: int):
     print("[ar-profile] done", file=sys.stderr, flush=True)
 
 
+def sweep(workload: str, batches, n_time: int):
+    """Concurrency sweep: denoising-step time at B = 1, 2, 4, ... canvases of
+    the workload (each over its own prefix rows; the cache holds seeded N(0,1)
+    rows instead of encoded prompts: the step's work depends on the cache values
+    only through the routing they lead to).  Steps
+    t = 1 .. n_time of a 12-step schedule after one untimed step, with the
+    self-conditioning input carried from step to step, then one traced step
+    for the per-phase times."""
+    import torch
+    from discrete_text_diffusion_amd import runtime as rt
+    import discrete_text_diffusion_amd as dg
+    from synth.configs import WORKLOADS
+    wl = WORKLOADS[workload]
+    shape, C = wl.model, wl.canvas
+    st = rt.stream_handle()
+    print(f"[sweep] building {workload}", file=sys.stderr, flush=True)
+    model = rt.DeviceModel(shape, wl.lm_scale)
+    cfg = model.cfg
+    hip = _hip()
+    rows = []
+    for B in batches:
+        cache = rt.DeviceCache(shape, B, wl.prefix + C)
+        cache.fill_random(wl.prefix)
+        cache.struct.length = wl.prefix
+        canvas = rt.DeviceCanvas(shape, B, C, list(range(B)))
+        ws = rt.Workspace(cfg, B, C)
+        dg.dg_init_canvas(cfg, canvas.struct, 0, st)
+        dg.dg_denoise_step(cfg, model.weights, cache.struct, canvas.struct, rt.step_params(0, 12, 0, False),
+                           ws.ptr, ws.size, st)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for t in range(1, n_time + 1):
+            dg.dg_denoise_step(cfg, model.weights, cache.struct, canvas.struct, rt.step_params(t, 12, 0, False),
+                               ws.ptr, ws.size, st)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n_time
+        acc = int(canvas.n_accepted.sum().item())
+        # per-phase times of one more step (HIP events around each phase)
+        pool = EventPool(hip, 2 * (shape.n_layers * 8 + 8))
+        tr = pool.trace(dg, (1 << len(dg.PHASES)) - 1)
+        dg.dg_denoise_step_traced(cfg, model.weights, cache.struct, canvas.struct,
+                                  rt.step_params(n_time + 1, 12, 0, False), ws.ptr, ws.size, st, tr)
+        torch.cuda.synchronize()
+        phases = {}
+        for ph, pms in pool.durations(tr):
+            phases[dg.PHASES[ph]] = phases.get(dg.PHASES[ph], 0.0) + pms
+        rows.append({"batch": B, "tokens_per_step": B * C, "step_ms": round(ms, 3),
+                     "canvas_tok_s_12_steps": round(B * C / (12 * ms * 1e-3), 1),
+                     "per_canvas_tok_s_12_steps": round(C / (12 * ms * 1e-3), 1),
+                     "accepted_last_step": acc, "phase_ms": {k: round(v, 3) for k, v in phases.items()}})
+        print(f"[sweep] B={B}: {ms:.3f} ms per step", file=sys.stderr, flush=True)
+        del cache, canvas, ws
+        torch.cuda.empty_cache()
+    print(json.dumps({"workload": workload, "prefix": wl.prefix, "canvas": C, "sweep": rows}))
+
+
 def _counter_rows(d):
     """(dispatch id, kernel name, counter name, value) of every counter record
     under d: rocprofv3's database output (SQLite, the counters_collection
@@ -351,7 +409,11 @@ def main():
     ap.add_argument("--pmc-copy", action="store_true", help="counter calibration copy only")
     ap.add_argument("--pmc-summarize", nargs=5, metavar=("F", "W", "CF", "CW", "OUT"))
     ap.add_argument("--ar-profile", type=int, metavar="N", help="N single-token decode steps only (kernel profiles)")
+    ap.add_argument("--sweep", metavar="B,B,...", help="denoising-step time at these canvas counts (own JSON line)")
     args = ap.parse_args()
+    if args.sweep:
+        sweep(args.workload, [int(b) for b in args.sweep.split(",")], 3)
+        return
     if args.ar_profile:
         ar_profile(args.workload, args.ar_profile)
         return

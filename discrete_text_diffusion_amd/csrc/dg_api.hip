@@ -13,7 +13,8 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int kMoeBM = 32;        // row tile of the grouped expert GEMMs (bf16)
 constexpr int kSimpleBM = 16;     // row tile of the fp32 GEMMs
-constexpr int kMaxRoutePairs = 8192;
+constexpr int kMaxRoutePairs = 8192;   // (token, slot) pairs of one encode pass
+constexpr int kMaxStepTokens = 16384;  // canvas tokens (batch x canvas) of one denoising step
 constexpr int kMaxSplit = 16;
 constexpr int kAttMaxSplit = 32;  // key splits of one attention launch (the merge takes any count)
 constexpr int kSelfSplit = 32;   // vocabulary splits of the expected-embedding product (at most)
@@ -81,7 +82,7 @@ struct Plan {
   int Tdn;      // denoise tokens
   int att_rows; // attention partial rows (split x tokens)
   size_t x, n, q, o, att_o, att_ml, o_part, r_part, ids, wts, row_token, inv, offsets, tiles,
-      n_tiles, h, Y, lm_f, lm_i, logits, e_part, ebar, hsc, g_part, total;
+      n_tiles, h, Y, lm_f, lm_i, logits, e_part, ebar, hsc, g_part, rcnt, total;
 };
 
 Plan make_plan(const Shape& s, int batch, int max_canvas) {
@@ -118,6 +119,7 @@ Plan make_plan(const Shape& s, int batch, int max_canvas) {
   p.ebar = take(Tdn * s.d * s.act);
   p.hsc = take(Tdn * s.dsc * s.act);
   p.g_part = take((size_t)kRowPartRows * std::max(s.qkv, s.dsc) * 4);  // widest split-epilogue GEMM
+  p.rcnt = take((size_t)std::max(1, route_chunk_words((int)T)) * 4);     // routing sort, per-chunk counts
   p.total = off;
   return p;
 }
@@ -375,7 +377,7 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
                          c.at<int32_t>(c.p.ids), c.at<float>(c.p.wts), r_out, c.st));
       DG_TRY(launch_route_sort(c.at<int32_t>(c.p.ids), T, s.k, s.E, s.n_sh, bm, c.at<int32_t>(c.p.row_token),
                                c.at<int32_t>(c.p.inv), c.at<int32_t>(c.p.offsets), c.at<GemmTile>(c.p.tiles),
-                               c.at<int32_t>(c.p.n_tiles), c.st));
+                               c.at<int32_t>(c.p.n_tiles), c.at<int32_t>(c.p.rcnt), c.st));
     }
     const int max_tiles = T * s.k / bm + s.E + s.n_sh * ((T + bm - 1) / bm);
     // experts + shared slices: gate/up with GeGLU
@@ -782,8 +784,7 @@ int dg_denoise_step_traced(const dg_model_config* cfg, const dg_weights* w, cons
   c.s = shape_of(cfg);
   c.p = make_plan(c.s, cv->batch, cv->canvas);
   DG_TRY(check_ws(c.p, d_ws, ws_bytes));
-  if ((int64_t)cv->batch * cv->canvas * c.s.k > kMaxRoutePairs || cv->batch * cv->canvas > route_max_tokens())
-    return DG_ERR_UNSUPPORTED;
+  if ((int64_t)cv->batch * cv->canvas > std::min(kMaxStepTokens, route_max_tokens())) return DG_ERR_UNSUPPORTED;
   c.ws = (char*)d_ws;
   c.st = (hipStream_t)stream;
   c.w = w;
@@ -870,7 +871,7 @@ int dg_test_route_from_logits(const dg_model_config* cfg, const float* d_logits,
   DG_TRY(check_config(cfg));
   if (!d_logits || !d_ids || !d_w || !d_row_token || !d_inv || !d_offsets || T < 1) return DG_ERR_INVALID_ARG;
   const Shape s = shape_of(cfg);
-  if ((int64_t)T * s.k > kMaxRoutePairs || T > route_max_tokens()) return DG_ERR_UNSUPPORTED;
+  if (T > std::min(kMaxStepTokens, route_max_tokens())) return DG_ERR_UNSUPPORTED;
   const Plan p = make_plan(s, 1, T);
   DG_TRY(check_ws(p, d_ws, ws_bytes));
   char* ws = (char*)d_ws;
@@ -878,7 +879,8 @@ int dg_test_route_from_logits(const dg_model_config* cfg, const float* d_logits,
   const int bm = s.dt == DG_DTYPE_BF16 ? kMoeBM : kSimpleBM;
   DG_TRY(launch_topk(d_logits, 1, 0, T, s.E, s.k, nullptr, d_ids, d_w, nullptr, st));
   DG_TRY(launch_route_sort(d_ids, T, s.k, s.E, s.n_sh, bm, d_row_token, d_inv, d_offsets,
-                           reinterpret_cast<GemmTile*>(ws + p.tiles), reinterpret_cast<int32_t*>(ws + p.n_tiles), st));
+                           reinterpret_cast<GemmTile*>(ws + p.tiles), reinterpret_cast<int32_t*>(ws + p.n_tiles),
+                           reinterpret_cast<int32_t*>(ws + p.rcnt), st));
   return DG_OK;
 }
 
@@ -898,6 +900,7 @@ int dg_test_forward_logits(const dg_model_config* cfg, const dg_weights* w, cons
   c.ws = (char*)d_ws;
   c.st = (hipStream_t)stream;
   c.w = w;
+  if ((int64_t)cv->batch * cv->canvas > std::min(kMaxStepTokens, route_max_tokens())) return DG_ERR_UNSUPPORTED;
   c.force_ids = d_force_ids;
   c.router_out = d_router_logits;
   DG_TRY(embed_canvas(c, cv, p));

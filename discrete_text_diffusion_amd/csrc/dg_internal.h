@@ -120,8 +120,10 @@ int launch_lm_partials_from_logits(const float* logits, int rows, const LmArgs& 
 int launch_topk(const float* part, int n_split, int64_t split_stride, int T, int E, int k, const int32_t* forced,
                 int32_t* ids, float* w, float* r_out, hipStream_t s);
 int route_max_tokens();
+// int32 words of per-chunk counts the sort needs for T tokens (0: one workgroup)
+int route_chunk_words(int T);
 int launch_route_sort(const int32_t* ids, int T, int k, int E, int n_sh, int bm, int32_t* row_token, int32_t* inv,
-                      int32_t* offsets, GemmTile* tiles, int32_t* n_tiles, hipStream_t s);
+                      int32_t* offsets, GemmTile* tiles, int32_t* n_tiles, int32_t* chunk_counts, hipStream_t s);
 // k_attn.hip
 int launch_attention(int dtype, const void* q, int64_t q_ld, const void* k, const void* v, int64_t s_seq,
                      int64_t s_head, int vp, int n_keys, int n_prefix, int causal, int seq_len, int n_seq, int n_q,

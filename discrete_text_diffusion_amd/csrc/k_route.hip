@@ -202,6 +202,126 @@ __global__ __launch_bounds__(1024) void k_route_sort(const int32_t* ids, int T, 
   for (int i = tid; i < n_sh * T; i += nt) row_token[npairs + i] = i % T;
 }
 
+// More tokens than one workgroup's bitmaps hold: the same stable counting
+// over chunks of kChunk tokens in three launches.  (1) per chunk, the pairs
+// of every expert; (2) one workgroup: per expert, the pairs in earlier chunks
+// (summed in chunk order), the segment offsets and the GEMM row tiles as
+// above; (3) per chunk, the bitmaps again and each pair's row = segment start
+// + the expert's pairs in earlier chunks + the earlier tokens of its chunk.
+// The rows come out exactly as the one-workgroup sort would place them.
+constexpr int kChunk = 64 * kMaxWords;
+constexpr int kMaxChunks = 64;
+
+__global__ __launch_bounds__(1024) void k_route_count(const int32_t* ids, int T, int k, int E, int32_t* ccnt) {
+  __shared__ int32_t cnt[256];
+  const int c = blockIdx.x, t0 = c * kChunk, tn = min(kChunk, T - t0);
+  const int tid = threadIdx.x, nt = blockDim.x;
+  for (int e = tid; e < E; e += nt) cnt[e] = 0;
+  __syncthreads();
+  const int32_t* cid = ids + (int64_t)t0 * k;
+  for (int q = tid; q < tn * k; q += nt) atomicAdd(&cnt[cid[q]], 1);
+  __syncthreads();
+  for (int e = tid; e < E; e += nt) ccnt[c * E + e] = cnt[e];
+}
+
+__global__ __launch_bounds__(1024) void k_route_scan(int32_t* ccnt, int nchunks, int T, int k, int E, int n_sh,
+                                                    int bm, int32_t* offsets, GemmTile* tiles, int32_t* n_tiles) {
+  __shared__ int32_t cnt[256];
+  __shared__ int32_t off[257];
+  __shared__ int32_t toff[257];
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int npairs = T * k;
+  for (int e = tid; e < E; e += nt) {
+    int run = 0;
+    for (int c = 0; c < nchunks; ++c) {
+      const int v = ccnt[c * E + e];
+      ccnt[c * E + e] = run;
+      run += v;
+    }
+    cnt[e] = run;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    int c4[4], t4[4], cs = 0, ts = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid * 4 + q;
+      c4[q] = e < E ? cnt[e] : 0;
+      t4[q] = (c4[q] + bm - 1) / bm;
+      cs += c4[q];
+      ts += t4[q];
+    }
+    int ci = cs, ti = ts;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int cu = __shfl_up(ci, o, 64), tu = __shfl_up(ti, o, 64);
+      if (tid >= o) { ci += cu; ti += tu; }
+    }
+    int co = ci - cs, to = ti - ts;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid * 4 + q;
+      if (e <= E) { off[e] = co; toff[e] = to; }
+      co += c4[q];
+      to += t4[q];
+    }
+    if (tid == 63) {
+      off[E] = co;
+      toff[E] = to;
+      n_tiles[0] = ti + n_sh * ((T + bm - 1) / bm);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e <= E; e += nt) offsets[e] = off[e];
+  for (int i = tid; i < nchunks * E; i += nt) ccnt[i] += off[i % E];  // absolute first row of (chunk, expert)
+  for (int e = tid; e < E; e += nt) {
+    const int base = off[e], n = cnt[e];
+    for (int i = 0, j = toff[e]; i * bm < n; ++i, ++j) tiles[j] = GemmTile{e, base + i * bm, min(bm, n - i * bm), 0};
+  }
+  const int per_sh = (T + bm - 1) / bm;
+  for (int i = tid; i < n_sh * per_sh; i += nt) {
+    const int c = i / per_sh, q = i - c * per_sh;
+    tiles[toff[E] + i] = GemmTile{E + c, npairs + c * T + q * bm, min(bm, T - q * bm), 0};
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_route_place(const int32_t* ids, const int32_t* cbase, int T, int k, int E,
+                                                     int n_sh, int32_t* row_token, int32_t* inv) {
+  __shared__ unsigned long long bits[256 * kMaxWords];
+  __shared__ int32_t wpre[256 * kMaxWords];
+  const int c = blockIdx.x, t0 = c * kChunk, tn = min(kChunk, T - t0);
+  const int W = (tn + 63) >> 6;
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int32_t* cid = ids + (int64_t)t0 * k;
+  for (int i = tid; i < E * W; i += nt) bits[i] = 0ull;
+  __syncthreads();
+  for (int q = tid; q < tn * k; q += nt) {
+    const int e = cid[q], t = q / k;
+    atomicOr(&bits[e * W + (t >> 6)], 1ull << (t & 63));
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += nt) {
+    int run = 0;
+    for (int w = 0; w < W; ++w) {
+      wpre[e * W + w] = run;
+      run += __popcll(bits[e * W + w]);
+    }
+  }
+  __syncthreads();
+  for (int q = tid; q < tn * k; q += nt) {
+    const int e = cid[q], t = q / k;
+    const unsigned long long below = bits[e * W + (t >> 6)] & ((1ull << (t & 63)) - 1ull);
+    const int p = cbase[c * E + e] + wpre[e * W + (t >> 6)] + __popcll(below);
+    row_token[p] = t0 + t;
+    inv[(int64_t)t0 * k + q] = p;
+  }
+  const int npairs = T * k;
+  for (int i = tid; i < n_sh * tn; i += nt) {
+    const int sh = i / tn, t = i - sh * tn;
+    row_token[npairs + sh * T + t0 + t] = t0 + t;
+  }
+}
+
 }  // namespace
 
 int launch_topk(const float* part, int n_split, int64_t split_stride, int T, int E, int k, const int32_t* forced,
@@ -214,12 +334,23 @@ int launch_topk(const float* part, int n_split, int64_t split_stride, int T, int
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
-int route_max_tokens() { return 64 * kMaxWords; }
+int route_max_tokens() { return kChunk * kMaxChunks; }
+
+int route_chunk_words(int T) { return T > kChunk ? DG_CEIL_DIV(T, kChunk) * 256 : 0; }
 
 int launch_route_sort(const int32_t* ids, int T, int k, int E, int n_sh, int bm, int32_t* row_token, int32_t* inv,
-                      int32_t* offsets, GemmTile* tiles, int32_t* n_tiles, hipStream_t s) {
-  if (E > 256 || T > 64 * kMaxWords || T < 1) return -1;
-  hipLaunchKernelGGL(k_route_sort, dim3(1), dim3(1024), 0, s, ids, T, k, E, n_sh, bm, row_token, inv, offsets,
-                     tiles, n_tiles);
+                      int32_t* offsets, GemmTile* tiles, int32_t* n_tiles, int32_t* chunk_counts, hipStream_t s) {
+  if (E > 256 || T > kChunk * kMaxChunks || T < 1 || (int64_t)T * (k + n_sh) > INT32_MAX) return -1;
+  if (T <= kChunk) {
+    hipLaunchKernelGGL(k_route_sort, dim3(1), dim3(1024), 0, s, ids, T, k, E, n_sh, bm, row_token, inv, offsets,
+                       tiles, n_tiles);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+  }
+  if (!chunk_counts) return -1;
+  const int nchunks = DG_CEIL_DIV(T, kChunk);
+  hipLaunchKernelGGL(k_route_count, dim3(nchunks), dim3(1024), 0, s, ids, T, k, E, chunk_counts);
+  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, s, chunk_counts, nchunks, T, k, E, n_sh, bm, offsets, tiles,
+                     n_tiles);
+  hipLaunchKernelGGL(k_route_place, dim3(nchunks), dim3(1024), 0, s, ids, chunk_counts, T, k, E, n_sh, row_token, inv);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }

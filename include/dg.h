@@ -232,7 +232,8 @@ int dg_encode_append(const dg_model_config* cfg, const dg_weights* w, dg_kv_cach
  * [length, length + canvas); rows below length are not written; capacity
  * below length + canvas: DG_ERR_KV_CAPACITY), final norm, fused LM head
  * (logits never stored), per-position entropy / sample / argmax, entropy-
- * bounded acceptance, re-noise, stop test.  Writes the canvas outputs. */
+ * bounded acceptance, re-noise, stop test.  Writes the canvas outputs.
+ * batch * canvas <= 16384 (else DG_ERR_UNSUPPORTED). */
 int dg_denoise_step(const dg_model_config* cfg, const dg_weights* w, const dg_kv_cache* cache,
                     dg_canvas* canvas, const dg_step_params* p, void* d_ws, size_t ws_bytes,
                     void* stream);
@@ -313,7 +314,8 @@ int dg_test_sample_from_logits(const dg_model_config* cfg, const float* d_logits
 
 /* Routing from given router logits d_logits [T][n_experts] fp32: d_ids/d_w
  * [T][top_k], d_row_token [T*top_k + (d_shared/d_expert)*T], d_inv [T*top_k],
- * d_offsets [n_experts + 1]. */
+ * d_offsets [n_experts + 1].  T <= 16384 (above 1024 the sort runs in
+ * 1024-token chunks); workspace dg_workspace_bytes(cfg, 1, T). */
 int dg_test_route_from_logits(const dg_model_config* cfg, const float* d_logits, int32_t T,
                               int32_t* d_ids, float* d_w, int32_t* d_row_token, int32_t* d_inv,
                               int32_t* d_offsets, void* d_ws, size_t ws_bytes, void* stream);

@@ -14,7 +14,7 @@ from synth.configs import MINI_BF16, TINY, WORKLOADS
 # the small bf16 shape with fp8 expert and LM-head weights
 MINI_FP8 = replace(MINI_BF16, expert_dtype="fp8", lm_dtype="fp8")
 
-from .gpu_util import allclose_report, compare_decisions, say
+from .gpu_util import allclose_report, bar_or_twin, compare_decisions, say
 
 pytestmark = pytest.mark.gpu
 
@@ -529,3 +529,60 @@ def test_ar_decode_matches_oracle(env, which):
     torch.cuda.synchronize()
     assert pb.cache.length == pb.cap
     assert torch.equal(k0, pb.cache.k) and torch.equal(v0, pb.cache.v)
+
+
+def _f32_twin_on_routes(pb, tok, expert_ids):
+    """The oracle's definition evaluated with fp32 products and sums on the
+    oracle's own routes (the fp32 twin of the full-size parity criterion)."""
+    ids = list(expert_ids)
+    orig = om.route
+
+    def fixed(shape_, r):
+        sel = ids.pop(0)
+        s_ = np.take_along_axis(r, sel, axis=1)
+        e = np.exp(s_ - s_.max(axis=1, keepdims=True))
+        return sel, e / e.sum(axis=1, keepdims=True)
+
+    om.route = fixed
+    trt = {}
+    try:
+        with om.accumulation("f32"):
+            zt = ost.denoise_logits(pb.shape, pb.W, pb.ocache, tok, None, pb.lm_scale, trace=trt)
+    finally:
+        om.route = orig
+    return zt, trt
+
+
+def test_many_canvases_match_oracle(env):
+    """24 canvases of 48 tokens: 1152 tokens in one step, so the routing sort
+    runs in 1024-token chunks and the grouped GEMMs see more than 1024 rows.
+    Logits, router logits and entropies on the oracle's routes (4.7M logits:
+    the elementwise bar, or the fp32-twin criterion where the bf16 tail
+    reaches it), then one full step's sampler invariants on every canvas."""
+    torch, dg, rt = env
+    B, C, prefix = 24, 48, 16
+    pb = Problem(env, MINI_BF16, 6.0, prefix, C, B=B)
+    pb.encode_prefix()
+    pb.compare_cache(prefix)
+    say(f"{B} canvases of {C}")
+    dg.dg_init_canvas(pb.cfg, pb.canvas.struct, 0, pb.st)
+    torch.cuda.synchronize()
+    tok = pb.canvas.tokens.cpu().numpy().reshape(B, C)
+    tr = {}
+    zo = ost.denoise_logits(pb.shape, pb.W, pb.ocache, tok, None, pb.lm_scale, trace=tr)
+    zt, trt = _f32_twin_on_routes(pb, tok, tr["expert_ids"])
+    z, rg = _forward_logits(pb, 0, 48, force_ids=_forced_ids(tr), want_router=True)
+    bar_or_twin(f"router logits {B}x{C} (oracle routes)", rg, np.stack(tr["router_logits"]),
+                np.stack(trt["router_logits"]), ROUTE_EPS["bf16"], 0.0)
+    bar_or_twin(f"logits {B}x{C} (oracle routes)", z, zo, zt, pb.atol, RTOL)
+    tau = smp.temperature(0, 48)
+    V = pb.shape.vocab
+    _, Hg, _ = smp.row_statistics(z.reshape(-1, V), tau)
+    _, Ho, _ = smp.row_statistics(zo.reshape(-1, V), tau)
+    _, Ht, _ = smp.row_statistics(zt.reshape(-1, V), tau)
+    bar_or_twin(f"entropy {B}x{C}", Hg, Ho, Ht, entropy_tolerance(zo.reshape(-1, V), tau, pb.atol), 0.0)
+    dg.dg_denoise_step(pb.cfg, pb.model.weights, pb.cache.struct, pb.canvas.struct, rt.step_params(0, 48),
+                       pb.ws.ptr, pb.ws.size, pb.st)
+    torch.cuda.synchronize()
+    check_sampler_invariants(pb, 0, 48, None)
+    assert pb.cache.struct.length == prefix

@@ -170,13 +170,21 @@ def test_stop_fires_on_confident_repeated_prediction(env):
             assert int(cv.stop.item()) == int(o["stop"]) == w2
 
 
-@pytest.mark.parametrize("shape,T", [(MINI_BF16, 48), (FULL_LAYER, 256), (TINY, 96), (FULL_LAYER, 1024)])
-def test_routing_from_oracle_logits(env, shape, T):
+@pytest.mark.parametrize("shape,T,skew", [(MINI_BF16, 48, False), (FULL_LAYER, 256, False), (TINY, 96, False),
+                                          (FULL_LAYER, 1024, False), (MINI_BF16, 1025, False),
+                                          (FULL_LAYER, 3000, False), (FULL_LAYER, 16384, False),
+                                          (FULL_LAYER, 5000, True)])
+def test_routing_from_oracle_logits(env, shape, T, skew):
+    """Above 1024 tokens the sort runs over 1024-token chunks (a one-token last
+    chunk at 1025, a ragged one at 3000, sixteen at 16384); skew sends every
+    token to the same top_k experts, 5000 rows each."""
     torch, dg, rt = env
-    say(f"routing parity E={shape.n_experts} k={shape.top_k} T={T}")
+    say(f"routing parity E={shape.n_experts} k={shape.top_k} T={T} skew={skew}")
     rng = np.random.default_rng(T)
     r = rng.standard_normal((T, shape.n_experts)).astype(np.float32)
-    r[0, 3] = r[0, 5] = 9.0  # exact tie: lower id first
+    if skew:
+        r[:, -shape.top_k:] += 20.0
+    r[0, 3] = r[0, 5] = 9.0 + (30.0 if skew else 0.0)  # exact tie: lower id first
     cfg = rt.model_config(shape)
     ws = rt.Workspace(cfg, 1, T)
     k = shape.top_k
