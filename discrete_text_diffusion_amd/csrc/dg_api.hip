@@ -180,6 +180,16 @@ constexpr int kRowMaxSplit = 16;
 // many bytes (writing and re-reading them costs more than the extra CUs gain).
 constexpr int64_t kRowPartBytes = 32ll << 20;
 
+// Row tile of the grouped expert GEMMs (bf16): 32 rows while the experts see
+// a few dozen tokens each (the weight stream bounds them); 64 and 128 once an
+// average expert's rows span several tiles, so that each weight fragment a
+// wave loads feeds more MFMAs.  fp8 experts keep 32.
+int moe_bm(const Shape& s, int T) {
+  if (s.ex8) return kMoeBM;
+  const int64_t per_expert = (int64_t)T * s.k / s.E;
+  return per_expert >= 512 ? 128 : per_expert >= 128 ? 64 : kMoeBM;
+}
+
 int pick_split(int blocks_per_split, int K, int kc, int max_split) {
   int sp = std::max(1, std::min(max_split, (kTargetBlocks + blocks_per_split - 1) / std::max(1, blocks_per_split)));
   while (sp > 1 && (K / kc) < sp) --sp;
@@ -363,7 +373,7 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
     }
     // router logits
     int r_split = 1;
-    const int bm = bf ? kMoeBM : kSimpleBM;
+    const int bm = bf ? moe_bm(s, T) : kSimpleBM;
     {
       Phase ph(c, DG_PHASE_ROUTE);
       GemmArgs a = base_args();
@@ -403,7 +413,7 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
         a.n_fb = (s.de + 63) / 64;
         a.tile_fastest = 1;  // the row tiles of one (expert, feature block) run together (same XCD): a hot
                              // expert's weight slice comes from HBM once and from L2 for its other tiles
-        DG_TRY(launch_wsgemm(a, kMoeBM, 1, s.d % 128 == 0 ? 128 : 64, true, c.st));
+        DG_TRY(launch_wsgemm(a, bm, 1, bm == 128 ? 64 : s.d % 128 == 0 ? 128 : 64, true, c.st));
       } else {
         DG_TRY(launch_gemm_simple(a, c.st));
       }
@@ -429,7 +439,7 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
         a.n_fb = (s.d + 127) / 128;
         a.tile_fastest = 1;  // the row tiles of one (expert, feature block) run together (same XCD): a hot
                              // expert's weight slice comes from HBM once and from L2 for its other tiles
-        DG_TRY(launch_wsgemm(a, kMoeBM, 2, 64, false, c.st));
+        DG_TRY(launch_wsgemm(a, bm, 2, 64, false, c.st));
       } else {
         DG_TRY(launch_gemm_simple(a, c.st));
       }

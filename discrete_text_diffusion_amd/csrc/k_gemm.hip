@@ -1034,6 +1034,8 @@ int launch_wsgemm(const GemmArgs& a, int bm, int nwt, int kc, bool geglu, hipStr
   DG_CASE(64, 1, 64, false)
   DG_CASE(32, 1, 64, true)
   DG_CASE(32, 1, 128, true)
+  DG_CASE(64, 1, 128, true)
+  DG_CASE(128, 1, 64, true)
   DG_CASE(32, 2, 64, false)
   DG_CASE(32, 1, 64, false)
   DG_CASE(32, 1, 128, false)

@@ -553,14 +553,16 @@ def _f32_twin_on_routes(pb, tok, expert_ids):
     return zt, trt
 
 
-def test_many_canvases_match_oracle(env):
-    """24 canvases of 48 tokens: 1152 tokens in one step, so the routing sort
-    runs in 1024-token chunks and the grouped GEMMs see more than 1024 rows.
+@pytest.mark.parametrize("B", [24, 48])
+def test_many_canvases_match_oracle(env, B):
+    """24 or 48 canvases of 48 tokens: 1152 or 2304 tokens in one step, so the
+    routing sort runs in 1024-token chunks and the grouped expert GEMMs take
+    64- and 128-row tiles (288 and 576 rows per expert on average).
     Logits, router logits and entropies on the oracle's routes (4.7M logits:
     the elementwise bar, or the fp32-twin criterion where the bf16 tail
     reaches it), then one full step's sampler invariants on every canvas."""
     torch, dg, rt = env
-    B, C, prefix = 24, 48, 16
+    C, prefix = 48, 16
     pb = Problem(env, MINI_BF16, 6.0, prefix, C, B=B)
     pb.encode_prefix()
     pb.compare_cache(prefix)
