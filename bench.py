@@ -134,7 +134,8 @@ def sweep(workload: str, batches, n_time: int):
     only through the routing they lead to).  Steps
     t = 1 .. n_time of a 12-step schedule after one untimed step, with the
     self-conditioning input carried from step to step, then one traced step
-    for the per-phase times."""
+    for the per-phase times; then 16 single-token greedy decode steps of the
+    same B sequences from the same prefix (after 16 untimed ones)."""
     import torch
     from discrete_text_diffusion_amd import runtime as rt
     import discrete_text_diffusion_amd as dg
@@ -175,10 +176,24 @@ def sweep(workload: str, batches, n_time: int):
         phases = {}
         for ph, pms in pool.durations(tr):
             phases[dg.PHASES[ph]] = phases.get(dg.PHASES[ph], 0.0) + pms
+        # single-token greedy decode of the same B sequences over the same cache
+        a = torch.zeros(B, dtype=torch.int32, device="cuda")
+        b = torch.empty_like(a)
+        for rep in range(2):  # warm-up pass, then the timed one
+            cache.struct.length = wl.prefix
+            e0.record()
+            for _ in range(16):
+                dg.dg_ar_step(cfg, model.weights, cache.struct, a.data_ptr(), B, b.data_ptr(), ws.ptr, ws.size, st)
+                a, b = b, a
+            e1.record()
+            torch.cuda.synchronize()
+        ar_ms = e0.elapsed_time(e1) / 16
         rows.append({"batch": B, "tokens_per_step": B * C, "step_ms": round(ms, 3),
                      "canvas_tok_s_12_steps": round(B * C / (12 * ms * 1e-3), 1),
                      "per_canvas_tok_s_12_steps": round(C / (12 * ms * 1e-3), 1),
-                     "accepted_last_step": acc, "phase_ms": {k: round(v, 3) for k, v in phases.items()}})
+                     "accepted_last_step": acc, "phase_ms": {k: round(v, 3) for k, v in phases.items()},
+                     "ar_step_ms": round(ar_ms, 3), "ar_tok_s": round(B / (ar_ms * 1e-3), 1),
+                     "ar_per_sequence_tok_s": round(1 / (ar_ms * 1e-3), 1)})
         print(f"[sweep] B={B}: {ms:.3f} ms per step", file=sys.stderr, flush=True)
         del cache, canvas, ws
         torch.cuda.empty_cache()
