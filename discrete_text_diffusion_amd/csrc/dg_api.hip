@@ -13,7 +13,8 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int kMoeBM = 32;        // row tile of the grouped expert GEMMs (bf16)
 constexpr int kSimpleBM = 16;     // row tile of the fp32 GEMMs
-constexpr int kMaxRoutePairs = 8192;   // (token, slot) pairs of one encode pass
+constexpr int kMaxRoutePairs = 32768;  // (token, slot) pairs of one encode pass
+constexpr int kPassTokens = 4096;      // tokens of one encode pass (at most)
 constexpr int kMaxStepTokens = 16384;  // canvas tokens (batch x canvas) of one denoising step
 constexpr int kMaxSplit = 16;
 constexpr int kAttMaxSplit = 32;  // key splits of one attention launch (the merge takes any count)
@@ -74,13 +75,14 @@ int check_config(const dg_model_config* c) {
 // handles up to route_max_tokens() tokens at a time).
 int max_tokens(const Shape& s, int batch, int max_canvas) {
   const int route_cap = std::min(kMaxRoutePairs / s.k, route_max_tokens());
-  return std::max(std::min(2048, route_cap), batch * max_canvas);
+  return std::max(std::min(kPassTokens, route_cap), batch * max_canvas);
 }
 
 struct Plan {
   int T;        // tokens per pass
   int Tdn;      // denoise tokens
   int att_rows; // attention partial rows (split x tokens)
+  int g_rows;   // rows (x the widest N) of the split-epilogue partial buffer
   size_t x, n, q, o, att_o, att_ml, o_part, r_part, ids, wts, row_token, inv, offsets, tiles,
       n_tiles, h, Y, lm_f, lm_i, logits, e_part, ebar, hsc, g_part, rcnt, total;
 };
@@ -118,7 +120,10 @@ Plan make_plan(const Shape& s, int batch, int max_canvas) {
   p.e_part = take(std::max(kMaxSplit, kSelfSplit) * Tdn * s.d * 4);
   p.ebar = take(Tdn * s.d * s.act);
   p.hsc = take(Tdn * s.dsc * s.act);
-  p.g_part = take((size_t)kRowPartRows * std::max(s.qkv, s.dsc) * 4);  // widest split-epilogue GEMM
+  // split-epilogue partials: every row a pass or step can hold (a non-store
+  // epilogue over the row-resident kernel stages at least M x N fp32 values)
+  p.g_rows = std::max(kRowPartRows, std::max(p.T, p.Tdn));
+  p.g_part = take((size_t)p.g_rows * std::max(s.qkv, s.dsc) * 4);
   p.rcnt = take((size_t)std::max(1, route_chunk_words((int)T)) * 4);     // routing sort, per-chunk counts
   p.total = off;
   return p;
@@ -261,8 +266,8 @@ int dense_gemm(const Ctx& c, GemmArgs a, int M, int N, int K, int max_split, int
     a.n_fb = (N + 255) / 256;
     const bool store = a.epi == EPI_STORE_F32;
     // non-store epilogues: the partials must fit the split-epilogue buffer
-    const int64_t part_cap = std::min<int64_t>((int64_t)kRowPartRows * std::max(c.s.qkv, c.s.dsc),
-                                               kRowPartBytes / 4) / ((int64_t)M * N);
+    const int64_t g_cap = (int64_t)c.p.g_rows * std::max(c.s.qkv, c.s.dsc);
+    const int64_t part_cap = std::min<int64_t>(g_cap, kRowPartBytes / 4) / ((int64_t)M * N);
     const int cap = store ? max_split : (int)std::min<int64_t>(kRowMaxSplit, part_cap);
     const int sp = row_split(M, N, K, std::max(1, cap));
     a.k_split = ((K / 64 + sp - 1) / sp) * 64;
@@ -271,6 +276,7 @@ int dense_gemm(const Ctx& c, GemmArgs a, int M, int N, int K, int max_split, int
       if (used_split) *used_split = a.n_split;
       return launch_rowgemm(a, nullptr, c.st);
     }
+    if ((int64_t)M * N * a.n_split > g_cap) return DG_ERR_UNSUPPORTED;
     GemmArgs pa = a;
     pa.epi = EPI_STORE_F32; pa.out_f32 = c.at<float>(c.p.g_part); pa.ldo = N; pa.split_stride = (int64_t)M * N;
     pa.alpha = 1.0f;

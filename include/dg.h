@@ -257,7 +257,7 @@ int dg_commit_block(const dg_model_config* cfg, const dg_weights* w, dg_kv_cache
  * Errors: DG_ERR_INVALID_ARG for null tokens / outputs or batch < 1,
  * DG_ERR_KV_CAPACITY if the cache is full (nothing written),
  * DG_ERR_WORKSPACE if the workspace is short, DG_ERR_UNSUPPORTED above the
- * routing limits (batch <= 1024, batch * top_k <= 8192). */
+ * routing limits (batch <= 16384, batch * top_k <= 32768). */
 int dg_ar_step(const dg_model_config* cfg, const dg_weights* w, dg_kv_cache* cache,
                const int32_t* d_tokens, int32_t batch, int32_t* d_next, void* d_ws,
                size_t ws_bytes, void* stream);
@@ -338,7 +338,7 @@ int dg_test_forward_logits(const dg_model_config* cfg, const dg_weights* w, cons
  * d_force_ids [n_layers][batch*n_tokens][top_k] (rank order), d_router_logits
  * [n_layers][batch*n_tokens][n_experts] fp32, rows in [batch][position]
  * order.  The whole encode must fit in one internal chunk (batch*n_tokens
- * <= 1024 and batch*n_tokens*top_k <= 8192), else DG_ERR_UNSUPPORTED. */
+ * <= 4096 and batch*n_tokens*top_k <= 32768), else DG_ERR_UNSUPPORTED. */
 int dg_test_encode_append(const dg_model_config* cfg, const dg_weights* w, dg_kv_cache* cache,
                           const int32_t* d_tokens, int32_t batch, int32_t n_tokens, const int32_t* d_force_ids,
                           float* d_router_logits, void* d_ws, size_t ws_bytes, void* stream);
