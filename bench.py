@@ -343,6 +343,56 @@ def moe_up_bytes(shape, T, experts=None):
     return w + act + rows * de * 2
 
 
+def prefill_flops(shape, n):
+    """Multiply-add flops (2 per MAC) of encoding n prompt tokens into an empty
+    cache: every layer's QKV, and for all but the last layer (whose output
+    nothing reads) causal attention (token i attends to i + 1 keys), the O
+    projection, the router, the top_k routed experts and the shared expert."""
+    d = shape.d_model
+    qkv = 2 * n * shape.qkv_rows * d
+    attn = 4 * shape.n_q_heads * shape.d_head * n * (n + 1) // 2
+    rest = 2 * n * (d * shape.q_dim + shape.n_experts * d + (shape.top_k * shape.d_expert + shape.d_shared) * 3 * d)
+    return shape.n_layers * qkv + (shape.n_layers - 1) * (attn + rest)
+
+
+def prefill_run(workload: str, lengths):
+    """Prompt encoding (dg_encode_append into an empty cache) of each length,
+    timed with events after one untimed run of the same length."""
+    import torch
+    from discrete_text_diffusion_amd import runtime as rt
+    import discrete_text_diffusion_amd as dg
+    import synth
+    from synth.configs import WORKLOADS
+    wl = WORKLOADS[workload]
+    shape = wl.model
+    st = rt.stream_handle()
+    print(f"[prefill] building {workload}", file=sys.stderr, flush=True)
+    model = rt.DeviceModel(shape, wl.lm_scale)
+    cfg = model.cfg
+    ws = rt.Workspace(cfg, 1, 1)
+    rows = []
+    for n in lengths:
+        cache = rt.DeviceCache(shape, 1, n + (-n) % 8)
+        prompt = torch.empty(n, dtype=torch.int32, device="cuda")
+        synth.dev_tokens(prompt.data_ptr(), n, wl.prompt_seed, synth.TID["prompt"], shape.vocab, st)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for rep in range(2):
+            cache.struct.length = 0
+            e0.record()
+            dg.dg_encode_append(cfg, model.weights, cache.struct, prompt.data_ptr(), 1, n, ws.ptr, ws.size, st)
+            e1.record()
+            torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        fl = prefill_flops(shape, n)
+        rows.append({"tokens": n, "ms": round(ms, 2), "tok_s": round(n / (ms * 1e-3), 1),
+                     "tflop": round(fl / 1e12, 2), "tflop_s": round(fl / (ms * 1e-3) / 1e12, 1),
+                     "mfma_frac": round(fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)})
+        print(f"[prefill] {n} tokens: {ms:.1f} ms", file=sys.stderr, flush=True)
+        del cache, prompt
+        torch.cuda.empty_cache()
+    print(json.dumps({"workload": workload, "prefill": rows}))
+
+
 def ar_step_bytes(shape, L):
     """HBM bytes one single-token decode step at cache length L must read:
     every layer's QKV, O and router weights, its top_k routed experts and the
@@ -425,7 +475,11 @@ def main():
     ap.add_argument("--pmc-summarize", nargs=5, metavar=("F", "W", "CF", "CW", "OUT"))
     ap.add_argument("--ar-profile", type=int, metavar="N", help="N single-token decode steps only (kernel profiles)")
     ap.add_argument("--sweep", metavar="B,B,...", help="denoising-step time at these canvas counts (own JSON line)")
+    ap.add_argument("--prefill", metavar="N,N,...", help="prompt encoding time at these lengths (own JSON line)")
     args = ap.parse_args()
+    if args.prefill:
+        prefill_run(args.workload, [int(n) for n in args.prefill.split(",")])
+        return
     if args.sweep:
         sweep(args.workload, [int(b) for b in args.sweep.split(",")], 3)
         return
@@ -638,6 +692,7 @@ def main():
         "steps_per_s": round(1000.0 / step_ms, 2),
         "commit_ms": round(commit_ms, 3),
         "prefill_ms": round(prefill_ms, 2),
+        "prefill_tflop_s": round(prefill_flops(shape, wl.prefix) / (prefill_ms * 1e-3) / 1e12, 1),
         "canvas_tok_s_12_incl_commit": round(T / ((12 * step_ms + commit_ms) * 1e-3), 2),
         "canvas_tok_s_12_excl_commit": round(T / (12 * step_ms * 1e-3), 2),
         "canvas_tok_s_48_incl_commit": round(T / (ms48 * 1e-3), 2),
