@@ -564,6 +564,13 @@ def test_many_canvases_match_oracle(env, B):
     torch, dg, rt = env
     C, prefix = 48, 16
     pb = Problem(env, MINI_BF16, 6.0, prefix, C, B=B)
+    # a workspace followed by 16 MiB of guard bytes: no launch may write past
+    # the size dg_workspace_bytes gives
+    guard = 16 << 20
+    buf = torch.full((pb.ws.size + 256 + guard,), 0xA5, dtype=torch.uint8, device="cuda")
+    off = (-buf.data_ptr()) % 256
+    pb.ws.buf, pb.ws.ptr = buf, buf.data_ptr() + off
+    tail = buf[off + pb.ws.size:off + pb.ws.size + guard]
     pb.encode_prefix()
     pb.compare_cache(prefix)
     say(f"{B} canvases of {C}")
@@ -588,3 +595,4 @@ def test_many_canvases_match_oracle(env, B):
     torch.cuda.synchronize()
     check_sampler_invariants(pb, 0, 48, None)
     assert pb.cache.struct.length == prefix
+    assert bool((tail == 0xA5).all()), "a launch wrote past the workspace"
