@@ -51,10 +51,28 @@ class Problem:
         self.cache = rt.DeviceCache(shape, B, self.cap)
         self.canvas = rt.DeviceCanvas(shape, B, C, self.seeds)
         self.ws = rt.Workspace(self.cfg, B, C)
+        self.guard_workspace(self.ws)
         self.st = rt.stream_handle()
         self.W = om.Weights(shape)
         self.ocache = om.KVCache(shape, B, self.cap)
         self.prompt = np.stack([synth.tokens(b, synth.TID["prompt"], prefix, shape.vocab) for b in range(B)])
+
+    GUARD = 4 << 20
+
+    def guard_workspace(self, ws):
+        """Re-seat ws on a buffer followed by GUARD bytes of 0xA5 (checked by
+        check_guards: no launch may write past dg_workspace_bytes)."""
+        torch = self.env[0]
+        buf = torch.full((ws.size + 256 + self.GUARD,), 0xA5, dtype=torch.uint8, device="cuda")
+        off = (-buf.data_ptr()) % 256
+        ws.buf, ws.ptr = buf, buf.data_ptr() + off
+        self.guards = getattr(self, "guards", []) + [buf[off + ws.size:off + ws.size + self.GUARD]]
+        return ws
+
+    def check_guards(self):
+        self.env[0].cuda.synchronize()
+        for g in self.guards:
+            assert bool((g == 0xA5).all()), "a launch wrote past the workspace"
 
     def encode_prefix(self):
         torch, dg, rt = self.env
@@ -207,6 +225,7 @@ def _forced_ids(trace):
 def test_encode_cache_matches_oracle(which, request):
     pb = request.getfixturevalue(which)
     pb.compare_cache(pb.prefix)
+    pb.check_guards()
 
 
 @pytest.mark.parametrize("which", ["tiny", "mini", "mini8"])
@@ -258,6 +277,7 @@ def test_forward_logits_match_oracle(which, request):
     z2 = _forward_logits(pb, 1, 48, P, force_ids=_forced_ids(tr2))
     allclose_report(f"logits+selfcond {which} (oracle routes)", z2, zo2, pb.atol, RTOL)
     assert np.abs(zo2 - zo).max() > 1e-3  # the self-conditioning term is not negligible
+    pb.check_guards()
 
 
 @pytest.mark.parametrize("which", ["tiny", "mini", "mini8"])
@@ -345,6 +365,7 @@ def test_denoise_loop_and_commit_match_oracle(which, request):
     nxt = pb.canvas.tokens.cpu().numpy().reshape(pb.B, pb.C)
     for b in range(pb.B):
         assert np.array_equal(nxt[b], smp.initial_canvas(pb.seeds[b], 1, pb.C, pb.shape.vocab))
+    pb.check_guards()
 
 
 @pytest.mark.parametrize("which", ["mini", "mini8"])
@@ -384,6 +405,7 @@ def test_skewed_routing_matches_oracle(which, request):
     _, Ho, _ = smp.row_statistics(zo.reshape(-1, shape.vocab), tau)
     allclose_report(f"entropy {which} (skewed routes)", Hg, Ho,
                     entropy_tolerance(zo.reshape(-1, shape.vocab), tau, pb.atol), 0.0)
+    pb.check_guards()
 
 
 @pytest.mark.parametrize("shape,C", [(MINI_BF16, 33), (TINY, 17)])
@@ -413,6 +435,7 @@ def test_empty_prefix_ragged_canvas(env, shape, C):
     torch.cuda.synchronize()
     check_sampler_invariants(pb, 0, 48, None)
     assert pb.cache.struct.length == 0
+    pb.check_guards()
 
 
 def test_denoise_step_is_deterministic(mini):
@@ -430,6 +453,7 @@ def test_denoise_step_is_deterministic(mini):
         outs.append([x.clone() for x in (pb.canvas.tokens, pb.canvas.entropy, pb.canvas.p_side, pb.canvas.p_scale)])
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+    pb.check_guards()
 
 
 # Router-logit margin under which an autoregressive row's route may differ
@@ -457,7 +481,7 @@ def test_ar_decode_matches_oracle(env, which):
     n_dec = 8
     pb = Problem(env, shape, lm_scale, prefix, 1, B=B, cap_extra=n_dec - 1)
     assert pb.cap == prefix + n_dec and pb.cap % 8 == 0
-    ws = rt.Workspace(pb.cfg, B, 1)
+    ws = pb.guard_workspace(rt.Workspace(pb.cfg, B, 1))
     if which == "mini_long":
         pb.cache.fill_random(prefix, seed=0, std=1.0)
         pb.cache.struct.length = prefix
@@ -529,6 +553,7 @@ def test_ar_decode_matches_oracle(env, which):
     torch.cuda.synchronize()
     assert pb.cache.length == pb.cap
     assert torch.equal(k0, pb.cache.k) and torch.equal(v0, pb.cache.v)
+    pb.check_guards()
 
 
 def _f32_twin_on_routes(pb, tok, expert_ids):
@@ -564,13 +589,6 @@ def test_many_canvases_match_oracle(env, B):
     torch, dg, rt = env
     C, prefix = 48, 16
     pb = Problem(env, MINI_BF16, 6.0, prefix, C, B=B)
-    # a workspace followed by 16 MiB of guard bytes: no launch may write past
-    # the size dg_workspace_bytes gives
-    guard = 16 << 20
-    buf = torch.full((pb.ws.size + 256 + guard,), 0xA5, dtype=torch.uint8, device="cuda")
-    off = (-buf.data_ptr()) % 256
-    pb.ws.buf, pb.ws.ptr = buf, buf.data_ptr() + off
-    tail = buf[off + pb.ws.size:off + pb.ws.size + guard]
     pb.encode_prefix()
     pb.compare_cache(prefix)
     say(f"{B} canvases of {C}")
@@ -595,4 +613,4 @@ def test_many_canvases_match_oracle(env, B):
     torch.cuda.synchronize()
     check_sampler_invariants(pb, 0, 48, None)
     assert pb.cache.struct.length == prefix
-    assert bool((tail == 0xA5).all()), "a launch wrote past the workspace"
+    pb.check_guards()
