@@ -2,12 +2,15 @@
 """Throughput of the block-diffusion denoising path on one MI355X.
 
 One timed step = one canvas of the 30-layer bf16 model (config "full30":
-256-token canvas, 4096-token causally encoded prefix): fresh canvas noise,
-N fixed denoising steps (default 12) and the commit (causal encode & append
-of the canvas).  value = canvas tokens / second over the timed steps.
+256-token canvas, 4096-token causally encoded prefix) in block-by-block
+generation: denoising steps 1 .. N - 1 (N = 12 by default; step 0 came with
+the previous canvas's commit), then the commit (causal encode & append of
+the canvas) fused with the next block's step 0 (fresh noise), one pass
+through the layer stack.  value = canvas tokens / second over the timed
+steps.
 
-Also reported: the denoising-step latency, canvas tok/s at 12 and 48 steps
-with and without the commit, a per-phase GPU time breakdown (HIP events),
+Also reported: the denoising-step latency, the commit alone and fused with a
+step, canvas tok/s at 12 and 48 steps with and without the commit, a per-phase GPU time breakdown (HIP events),
 the roofline of the dominant kernel (the routed + shared expert gate/up GEMM,
 timed with HIP events on its launch stream over the timed region), the LM
 head's MFMA roofline timed the same way, the accepted tokens per step of a
@@ -519,7 +522,8 @@ def main():
     t0 = time.time()
     model = rt.DeviceModel(shape, wl.lm_scale)
     cfg = model.cfg
-    cache = rt.DeviceCache(shape, B, wl.prefix + C)
+    # room for one committed block per canvas of a measurement group
+    cache = rt.DeviceCache(shape, B, wl.prefix + C * (args.warmup + args.steps + 2))
     canvas = rt.DeviceCanvas(shape, B, C, list(wl.sampler_seeds)[:B])
     ws = rt.Workspace(cfg, B, C)
     prompt = torch.empty(B * wl.prefix, dtype=torch.int32, device="cuda")
@@ -541,16 +545,29 @@ def main():
     MASK_UP = 1 << 6
     MASK_LM = 1 << 9
 
-    def canvas_pass(n_steps, trace=None, commit=True):
-        dg.dg_init_canvas(cfg, canvas.struct, 0, st)
-        for t in range(n_steps):
-            p = rt.step_params(t, n_steps, 0, adaptive=False)
-            dg.dg_denoise_step_traced(cfg, model.weights, cache.struct, canvas.struct, p, ws.ptr, ws.size, st, trace)
-        if commit:
-            dg.dg_commit_block(cfg, model.weights, cache.struct, canvas.struct,
-                               rt.step_params(n_steps - 1, n_steps, 0), ws.ptr, ws.size, st)
-            cache.struct.length = L  # the next canvas overwrites the appended rows
+    blk = [0]
 
+    def start_canvas(n_steps):
+        """The cache back to the prompt, block 0's noise and its first step."""
+        cache.struct.length = L
+        blk[0] = 0
+        dg.dg_init_canvas(cfg, canvas.struct, 0, st)
+        dg.dg_denoise_step(cfg, model.weights, cache.struct, canvas.struct, rt.step_params(0, n_steps, 0, False),
+                           ws.ptr, ws.size, st)
+
+    def canvas_pass(n_steps, trace=None):
+        """One canvas of the block-by-block generation in steady state: steps
+        1 .. n_steps - 1, then its commit fused with the next block's step 0."""
+        b = blk[0]
+        for t in range(1, n_steps):
+            p = rt.step_params(t, n_steps, b, adaptive=False)
+            dg.dg_denoise_step_traced(cfg, model.weights, cache.struct, canvas.struct, p, ws.ptr, ws.size, st, trace)
+        dg.dg_commit_and_step(cfg, model.weights, cache.struct, canvas.struct,
+                              rt.step_params(n_steps - 1, n_steps, b, False), rt.step_params(0, n_steps, b + 1, False),
+                              ws.ptr, ws.size, st)
+        blk[0] = b + 1
+
+    start_canvas(args.n_steps)
     for _ in range(args.warmup):
         canvas_pass(args.n_steps)
     torch.cuda.synchronize()
@@ -573,6 +590,7 @@ def main():
 
     # denoising-step latency and commit separately; 48-step canvas
     d0, d1, d2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    cache.struct.length = L
     dg.dg_init_canvas(cfg, canvas.struct, 0, st)
     d0.record()
     for t in range(args.n_steps):
@@ -586,12 +604,26 @@ def main():
     cache.struct.length = L
     step_ms = d0.elapsed_time(d1) / args.n_steps
     commit_ms = d1.elapsed_time(d2)
+    # the commit fused with the next block's first step, alone
+    dg.dg_init_canvas(cfg, canvas.struct, 0, st)
+    for t in range(args.n_steps):
+        dg.dg_denoise_step(cfg, model.weights, cache.struct, canvas.struct,
+                           rt.step_params(t, args.n_steps, 0, False), ws.ptr, ws.size, st)
+    d0.record()
+    dg.dg_commit_and_step(cfg, model.weights, cache.struct, canvas.struct,
+                          rt.step_params(args.n_steps - 1, args.n_steps, 0, False),
+                          rt.step_params(0, args.n_steps, 1, False), ws.ptr, ws.size, st)
+    d1.record()
+    torch.cuda.synchronize()
+    fused_ms = d0.elapsed_time(d1)
     f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start_canvas(48)
     f0.record()
     canvas_pass(48)
     f1.record()
     torch.cuda.synchronize()
     ms48 = f0.elapsed_time(f1)
+    cache.struct.length = L
 
     # single-token greedy decode on the same weights and prefix cache: each
     # step's next token is the following step's input (rows L.. appended,
@@ -686,17 +718,20 @@ def main():
         "config": {"workload": f"{args.workload}: {shape.n_layers}-layer bf16 MoE decoder, d_model {shape.d_model}, "
                                f"{shape.n_experts} experts top-{shape.top_k} + shared, vocab {shape.vocab}; "
                                f"batch {B} x {C}-token canvas, {wl.prefix}-token encoded prefix; "
-                               f"one step = {args.n_steps} denoising steps + commit",
+                               f"one step = one canvas of block-by-block generation: {args.n_steps - 1} "
+                               f"denoising steps, then its commit fused with the next block's first step",
                    "batch": B, "canvas": C, "prefix": wl.prefix, "denoise_steps": args.n_steps},
         "denoise_step_ms": round(step_ms, 3),
         "steps_per_s": round(1000.0 / step_ms, 2),
         "commit_ms": round(commit_ms, 3),
         "prefill_ms": round(prefill_ms, 2),
         "prefill_tflop_s": round(prefill_flops(shape, wl.prefix) / (prefill_ms * 1e-3) / 1e12, 1),
-        "canvas_tok_s_12_incl_commit": round(T / ((12 * step_ms + commit_ms) * 1e-3), 2),
+        "commit_and_step_ms": round(fused_ms, 3),
+        "canvas_tok_s_12_incl_commit": round(T / ((11 * step_ms + fused_ms) * 1e-3), 2),
         "canvas_tok_s_12_excl_commit": round(T / (12 * step_ms * 1e-3), 2),
+        "canvas_tok_s_12_separate_commit": round(T / ((12 * step_ms + commit_ms) * 1e-3), 2),
         "canvas_tok_s_48_incl_commit": round(T / (ms48 * 1e-3), 2),
-        "canvas_tok_s_48_excl_commit": round(T / ((ms48 - commit_ms) * 1e-3), 2),
+        "canvas_tok_s_48_excl_commit": round(T / (48 * step_ms * 1e-3), 2),
         **ar,
         "accepted_last_step": n_acc,
         "accepted_per_step": acc_steps,

@@ -108,6 +108,8 @@ _denoise = _sig("dg_denoise_step", c_int32, _P(ModelConfig), _P(Weights), _P(KVC
                 c_void_p, c_size_t, c_void_p)
 _commit = _sig("dg_commit_block", c_int32, _P(ModelConfig), _P(Weights), _P(KVCache), _P(Canvas), _P(StepParams),
                c_void_p, c_size_t, c_void_p)
+_commit_step = _sig("dg_commit_and_step", c_int32, _P(ModelConfig), _P(Weights), _P(KVCache), _P(Canvas),
+                    _P(StepParams), _P(StepParams), c_void_p, c_size_t, c_void_p)
 _ar = _sig("dg_ar_step", c_int32, _P(ModelConfig), _P(Weights), _P(KVCache), c_void_p, c_int32, c_void_p, c_void_p,
            c_size_t, c_void_p)
 _denoise_tr = _sig("dg_denoise_step_traced", c_int32, _P(ModelConfig), _P(Weights), _P(KVCache), _P(Canvas),
@@ -131,7 +133,7 @@ EXPORTED = ("dg_temperature", "dg_workspace_bytes", "dg_pack_weight_bf16", "dg_p
             "dg_pack_weight_fp8",
             "dg_init_canvas", "dg_encode_append", "dg_denoise_step", "dg_commit_block", "dg_status_string",
             "dg_test_sample_from_logits", "dg_test_route_from_logits", "dg_test_forward_logits",
-            "dg_denoise_step_traced", "dg_encode_append_traced", "dg_test_encode_append", "dg_ar_step",
+            "dg_denoise_step_traced", "dg_encode_append_traced", "dg_test_encode_append", "dg_ar_step", "dg_commit_and_step",
             "dg_test_ar_step")
 
 
@@ -181,6 +183,11 @@ def dg_denoise_step(cfg, weights, cache, canvas, params, ws, ws_bytes: int, stre
 def dg_commit_block(cfg, weights, cache, canvas, params, ws, ws_bytes: int, stream) -> None:
     _check(_commit(ctypes.byref(cfg), ctypes.byref(weights), ctypes.byref(cache), ctypes.byref(canvas),
                    ctypes.byref(params), ws, ws_bytes, stream), "dg_commit_block")
+
+
+def dg_commit_and_step(cfg, weights, cache, canvas, p_commit, p_next, ws, ws_bytes: int, stream) -> None:
+    _check(_commit_step(ctypes.byref(cfg), ctypes.byref(weights), ctypes.byref(cache), ctypes.byref(canvas),
+                        ctypes.byref(p_commit), ctypes.byref(p_next), ws, ws_bytes, stream), "dg_commit_and_step")
 
 
 def dg_ar_step(cfg, weights, cache, d_tokens, batch: int, d_next, ws, ws_bytes: int, stream) -> None:

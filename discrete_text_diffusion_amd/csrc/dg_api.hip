@@ -138,6 +138,7 @@ struct Ctx {
   dg_trace* tr = nullptr;
   const int32_t* force_ids = nullptr;  // test path: [n_layers][T][k] expert ids
   float* router_out = nullptr;         // test path: [n_layers][T][E] router logits
+  size_t head_row0 = 0;                // first row of the normalised output the LM head reads
   template <typename T> T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
 };
 
@@ -312,10 +313,17 @@ int dense_gemm(const Ctx& c, GemmArgs a, int M, int N, int K, int max_split, int
 // The layer stack over T = n_seq * seq_len tokens whose embeddings are in
 // x / n.  causal: encode (k, v appended to the cache at rows L..); else the
 // denoiser (canvas k, v kept in the workspace).
+// Two segments (`fused`): rows [0, n_seq seq_len) are a committed block
+// encoded causally at L (K/V appended at rows [L, L + seq_len)), rows
+// [n_seq seq_len, 2 n_seq seq_len) the next block's canvas, bidirectional
+// over [cache ; committed block ; canvas] (K/V at rows [L + seq_len, L + 2
+// seq_len)).  The projections, routing and experts run over both at once.
 int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, int L, bool causal,
-               bool need_output = false) {
+               bool need_output = false, bool fused = false) {
   const Shape& s = c.s;
-  const int T = n_seq * seq_len;
+  const int n_segs = fused ? 2 : 1;
+  const int Tseg = n_seq * seq_len;
+  const int T = n_segs * Tseg;
   const bool bf = s.dt == DG_DTYPE_BF16;
   const int64_t layer_elems = (int64_t)cache->batch * s.nkv * cache->capacity * s.dh;
   const int64_t c_seq = (int64_t)s.nkv * cache->capacity * s.dh, c_head = (int64_t)cache->capacity * s.dh;
@@ -325,32 +333,34 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
     char* kc = reinterpret_cast<char*>(cache->k) + (size_t)l * layer_elems * s.act;
     char* vc = reinterpret_cast<char*>(cache->v) + (size_t)l * layer_elems * s.act;
     // q, k, v with RoPE
-    {
+    for (int seg = 0; seg < n_segs; ++seg) {
       Phase ph(c, DG_PHASE_QKV);
       GemmArgs a = base_args();
-      a.act = xn; a.act_ld = s.d; a.act_kind = bf ? ACT_BF16 : ACT_F32;
+      a.act = c.at<char>(c.p.n) + (size_t)seg * Tseg * s.d * s.act; a.act_ld = s.d;
+      a.act_kind = bf ? ACT_BF16 : ACT_F32;
       a.w0 = lw.wqkv;
       a.epi = EPI_QKV;
       QkvEpi& q = a.qkv;
-      q.q = c.at<void>(c.p.q);
+      q.q = c.at<char>(c.p.q) + (size_t)seg * Tseg * s.qdim * s.act;
       q.q_dim = s.qdim; q.kv_dim = s.kvdim; q.d_head = s.dh; q.n_kv = s.nkv;
       // k, v of these tokens go to cache rows [L, L + seq_len): appended by the
       // encoder; scratch rows for the denoiser, which leaves the length as is
-      q.k = kc; q.v = vc; q.kv_b_stride = c_seq; q.kv_h_stride = c_head; q.kv_row0 = L;
+      q.k = kc; q.v = vc; q.kv_b_stride = c_seq; q.kv_h_stride = c_head; q.kv_row0 = L + seg * seq_len;
       q.v_pitch = cache->capacity;
-      q.seq_len = seq_len; q.pos0 = L; q.rope_base = s.rope_base;
-      DG_TRY(dense_gemm(c, a, T, s.qkv, s.d, 1));
+      q.seq_len = seq_len; q.pos0 = L + seg * seq_len; q.rope_base = s.rope_base;
+      DG_TRY(dense_gemm(c, a, Tseg, s.qkv, s.d, 1));
     }
     // The causal encode keeps only the K/V rows it appends: past the last
     // layer's QKV nothing reads its output (no LM head follows; the next chunk
     // embeds its own tokens).  The test entry points that record or force
     // per-layer routes, and the AR step (its LM head reads the last layer's
     // normalised output), run the whole layer.
-    if (causal && !need_output && l == s.L - 1 && !c.router_out && !c.force_ids) break;
-    // attention
-    {
+    if (causal && !fused && !need_output && l == s.L - 1 && !c.router_out && !c.force_ids) break;
+    // attention (per segment: the second sees the first's K/V rows as context)
+    for (int seg = 0; seg < n_segs; ++seg) {
       Phase ph(c, DG_PHASE_ATTN);
-      const int n_keys = L + seq_len;
+      const int L0 = L + seg * seq_len;
+      const int n_keys = L0 + seq_len;
       int split = 1;
       if (bf) {
         const int G = s.nq / s.nkv;
@@ -359,11 +369,12 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
         // >= 4 key tiles per split; >= 2 when there are few query blocks
         // (the decode step: 8 workgroups before the split)
         split = std::min(split, std::max(1, (n_keys + 255) / 256 * (base_blocks < 32 ? 2 : 1)));
-        split = std::min(split, std::min(kAttMaxSplit, std::max(1, c.p.att_rows / T)));
+        split = std::min(split, std::min(kAttMaxSplit, std::max(1, c.p.att_rows / Tseg)));
       }
-      DG_TRY(launch_attention(bf, c.at<void>(c.p.q), s.qdim, kc, vc, c_seq, c_head, cache->capacity, n_keys, L,
-                              causal ? 1 : 0, seq_len, n_seq, s.nq, s.nkv, s.dh, split, c.at<float>(c.p.att_o),
-                              c.at<float2>(c.p.att_ml), c.at<void>(c.p.o), c.st));
+      const size_t qoff = (size_t)seg * Tseg * s.qdim * s.act;
+      DG_TRY(launch_attention(bf, c.at<char>(c.p.q) + qoff, s.qdim, kc, vc, c_seq, c_head, cache->capacity, n_keys,
+                              L0, (causal && seg == 0) ? 1 : 0, seq_len, n_seq, s.nq, s.nkv, s.dh, split,
+                              c.at<float>(c.p.att_o), c.at<float2>(c.p.att_ml), c.at<char>(c.p.o) + qoff, c.st));
     }
     // O projection (split-K partials), residual, RMSNorm
     {
@@ -589,7 +600,7 @@ int lm_head_rows(const Ctx& c, int T, LmArgs lm) {
   lm.p_side_f32 = !bf;
   lm.vocab = s.V;
   GemmArgs a = base_args();
-  a.act = c.at<void>(c.p.n); a.act_ld = s.d; a.act_kind = bf ? ACT_BF16 : ACT_F32;
+  a.act = c.at<char>(c.p.n) + c.head_row0 * s.d * s.act; a.act_ld = s.d; a.act_kind = bf ? ACT_BF16 : ACT_F32;
   a.w0 = c.w->lm_head;
   a.alpha = c.w->lm_scale;
   a.M = T; a.N = s.V; a.K = s.d; a.n_main = 1; a.kt_main = s.d / 32;
@@ -838,6 +849,42 @@ int dg_commit_block(const dg_model_config* cfg, const dg_weights* w, dg_kv_cache
                             (hipStream_t)stream) == 0
              ? DG_OK
              : DG_ERR_HIP;
+}
+
+int dg_commit_and_step(const dg_model_config* cfg, const dg_weights* w, dg_kv_cache* cache, dg_canvas* cv,
+                       const dg_step_params* p_commit, const dg_step_params* p_next, void* d_ws, size_t ws_bytes,
+                       void* stream) {
+  DG_TRY(check_config(cfg));
+  DG_TRY(check_weights(cfg, w));
+  DG_TRY(check_canvas(cv, true));
+  DG_TRY(check_step(p_commit));
+  DG_TRY(check_step(p_next));
+  if (!cv->committed || p_next->t != 0 || p_next->block != p_commit->block + 1) return DG_ERR_INVALID_ARG;
+  if (cv->sc_probs) return DG_ERR_UNSUPPORTED;
+  DG_TRY(check_cache(cfg, cache, cv->batch));
+  const int C = cv->canvas, Tseg = cv->batch * C;
+  // the committed rows are appended, the next canvas's rows follow as scratch
+  if ((int64_t)cache->length + 2 * C > cache->capacity) return DG_ERR_KV_CAPACITY;
+  Ctx c;
+  c.s = shape_of(cfg);
+  c.p = make_plan(c.s, cv->batch, C);
+  DG_TRY(check_ws(c.p, d_ws, ws_bytes));
+  if (2 * Tseg > c.p.T || 2 * Tseg > std::min(kMaxStepTokens, route_max_tokens())) return DG_ERR_UNSUPPORTED;
+  c.ws = (char*)d_ws;
+  c.st = (hipStream_t)stream;
+  c.w = w;
+  const bool bf = c.s.dt == DG_DTYPE_BF16;
+  DG_TRY(launch_copy_i32(cv->committed, cv->argmax, Tseg, c.st));
+  DG_TRY(launch_init_canvas(cv->tokens, cv->seeds, cv->batch, C, p_next->block, cfg->vocab, c.st));
+  for (int seg = 0; seg < 2; ++seg)
+    DG_TRY(launch_embed_norm(bf, seg == 0 ? cv->committed : cv->tokens, w->embed, nullptr, 0, 0,
+                             c.at<float>(c.p.x) + (size_t)seg * Tseg * c.s.d,
+                             c.at<char>(c.p.n) + (size_t)seg * Tseg * c.s.d * c.s.act, Tseg, c.s.d, c.s.eps, c.st));
+  DG_TRY(run_layers(c, cache, cv->batch, C, cache->length, true, true, true));
+  cache->length += C;
+  c.head_row0 = Tseg;
+  DG_TRY(lm_head(c, cv, p_next, nullptr));
+  return sample_and_select(c, cv, p_next);
 }
 
 const char* dg_status_string(int status) {

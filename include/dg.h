@@ -246,6 +246,24 @@ int dg_commit_block(const dg_model_config* cfg, const dg_weights* w, dg_kv_cache
                     dg_canvas* canvas, const dg_step_params* p, void* d_ws, size_t ws_bytes,
                     void* stream);
 
+/* dg_commit_block followed by the first denoising step (t = 0) of the next
+ * block, in one pass through the layer stack (report Figure 4: stage 3 of
+ * one block and stage 2 of the next).  The committed block (the last step's
+ * argmax) is encoded causally and appended at rows [L, L + canvas); the
+ * canvas is re-noised for p_next->block and denoised over [cache ; committed
+ * block ; canvas] (its K/V in the scratch rows [L + canvas, L + 2 canvas)).
+ * The weights stream once for both.  Results equal those of the two calls
+ * up to floating-point summation order.  Requires p_next->t == 0,
+ * p_next->block == p_commit->block + 1 and committed != NULL (else
+ * DG_ERR_INVALID_ARG), no sc_probs, 2 * batch * canvas within the
+ * workspace's pass size (dg_workspace_bytes(cfg, batch, canvas) holds
+ * max(4096, batch * canvas) rows) and 16384 (else DG_ERR_UNSUPPORTED), and
+ * capacity >= length + 2 canvas (else DG_ERR_KV_CAPACITY).
+ * cache->length += canvas. */
+int dg_commit_and_step(const dg_model_config* cfg, const dg_weights* w, dg_kv_cache* cache,
+                       dg_canvas* canvas, const dg_step_params* p_commit,
+                       const dg_step_params* p_next, void* d_ws, size_t ws_bytes, void* stream);
+
 /* One autoregressive decode step on the same weights (DiffusionGemma
  * Technical Report digest, Figure 11: the single-token AR step the diffusion
  * step's latency is set against).  d_tokens [batch] (device int32, each in

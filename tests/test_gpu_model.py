@@ -163,7 +163,7 @@ def flip_margin_bound(got, want, dtype="bf16"):
 ROUTE_MEDIAN = {"f32": 1e-6, "bf16": 1e-4}
 
 
-def check_sampler_invariants(pb, t, n_steps, prev_before, adaptive=True):
+def check_sampler_invariants(pb, t, n_steps, prev_before, adaptive=True, block=0):
     """Properties every step must satisfy, checked on the GPU's own outputs
     against the sampler's definition (entropy-bounded acceptance, Philox
     re-noise, stop rule)."""
@@ -185,7 +185,7 @@ def check_sampler_invariants(pb, t, n_steps, prev_before, adaptive=True):
             assert H[b][acc[b]].sum() <= 0.1 + 1e-5
         if K < C:
             assert np.sort(H[b])[:K + 1].sum() > 0.1 - 1e-5      # one more would break the bound
-        fresh = smp.renoise_tokens(pb.seeds[b], t, 0, C, V)
+        fresh = smp.renoise_tokens(pb.seeds[b], t, block, C, V)
         assert np.array_equal(nxt[b], np.where(acc[b], samp[b], fresh))
         assert abs(mean[b] - H[b].mean()) < 1e-5
         want_stop = adaptive and t >= 1 and mean[b] < 0.005 and prev_before is not None and \
@@ -613,4 +613,48 @@ def test_many_canvases_match_oracle(env, B):
     torch.cuda.synchronize()
     check_sampler_invariants(pb, 0, 48, None)
     assert pb.cache.struct.length == prefix
+    pb.check_guards()
+
+
+@pytest.mark.parametrize("which", ["tiny", "mini", "mini8"])
+def test_commit_and_step_matches_oracle(env, which):
+    """dg_commit_and_step (commit of one block and the next block's first
+    step in one pass) against the oracle's commit and step: the appended K/V
+    rows (causal encode of the last step's argmax), the next canvas's noise,
+    the step's entropies (rows without a near-tie route) and its sampler
+    invariants."""
+    torch, dg, rt = env
+    shape, lm_scale, prefix, C, B = {
+        "tiny": (WORKLOADS["tiny"].model, WORKLOADS["tiny"].lm_scale, 24, 32, 1),
+        "mini": (MINI_BF16, 6.0, 40, 48, 2),
+        "mini8": (MINI_FP8, 6.0, 40, 48, 2),
+    }[which]
+    pb = Problem(env, shape, lm_scale, prefix, C, B=B, cap_extra=C + (-(prefix + 2 * C)) % 8)
+    pb.encode_prefix()
+    say(f"commit+step {which}")
+    dg.dg_init_canvas(pb.cfg, pb.canvas.struct, 0, pb.st)
+    for t in range(2):
+        dg.dg_denoise_step(pb.cfg, pb.model.weights, pb.cache.struct, pb.canvas.struct, rt.step_params(t, 2),
+                           pb.ws.ptr, pb.ws.size, pb.st)
+    torch.cuda.synchronize()
+    am = pb.canvas.argmax.cpu().numpy().reshape(B, C)
+    dg.dg_commit_and_step(pb.cfg, pb.model.weights, pb.cache.struct, pb.canvas.struct, rt.step_params(1, 2, 0),
+                          rt.step_params(0, 2, 1), pb.ws.ptr, pb.ws.size, pb.st)
+    torch.cuda.synchronize()
+    assert pb.cache.struct.length == prefix + C
+    assert np.array_equal(pb.canvas.committed.cpu().numpy().reshape(B, C), am)
+    ost.encode_append(shape, pb.W, pb.ocache, am)
+    pb.compare_cache(prefix + C)
+    tok = np.stack([smp.initial_canvas(pb.seeds[b], 1, C, shape.vocab) for b in range(B)])
+    tr = {}
+    zo = ost.denoise_logits(shape, pb.W, pb.ocache, tok, None, pb.lm_scale, trace=tr)
+    ok = np.all(_route_margins(shape, tr) >= AR_FLIP[shape.dtype], axis=0).reshape(B, C)  # [T] rows
+    say(f"commit+step {which}: {int(ok.sum())} of {ok.size} rows without a near-tie route")
+    assert ok.mean() >= 0.5
+    tau = smp.temperature(0, 2)
+    _, Ho, _ = smp.row_statistics(zo.reshape(-1, shape.vocab), tau)
+    Hg = pb.canvas.entropy.cpu().numpy().astype(np.float64)
+    tol = entropy_tolerance(zo.reshape(-1, shape.vocab), tau, pb.atol)
+    allclose_report(f"commit+step entropy {which}", Hg[ok.reshape(-1)], Ho[ok.reshape(-1)], tol[ok.reshape(-1)], 0.0)
+    check_sampler_invariants(pb, 0, 2, None, block=1)
     pb.check_guards()
