@@ -625,6 +625,23 @@ def main():
     ms48 = f0.elapsed_time(f1)
     cache.struct.length = L
 
+    # adaptive stop: up to 48 steps of one canvas, until every canvas's stop
+    # flag is set (one host read of the flags per step)
+    cache.struct.length = L
+    dg.dg_init_canvas(cfg, canvas.struct, 0, st)
+    torch.cuda.synchronize()
+    t_ad = time.time()
+    ad_steps = 48
+    for t in range(48):
+        dg.dg_denoise_step(cfg, model.weights, cache.struct, canvas.struct, rt.step_params(t, 48, 0, True),
+                           ws.ptr, ws.size, st)
+        if t >= 1 and bool(canvas.stop.bool().all().item()):
+            ad_steps = t + 1
+            break
+    torch.cuda.synchronize()
+    ad_ms = (time.time() - t_ad) * 1e3
+    ad_mean_h = float(canvas.mean_entropy.float().mean().item())
+
     # single-token greedy decode on the same weights and prefix cache: each
     # step's next token is the following step's input (rows L.. appended,
     # then dropped again)
@@ -733,6 +750,9 @@ def main():
         "canvas_tok_s_48_incl_commit": round(T / (ms48 * 1e-3), 2),
         "canvas_tok_s_48_excl_commit": round(T / (48 * step_ms * 1e-3), 2),
         **ar,
+        "adaptive_steps_taken": ad_steps,
+        "adaptive_canvas_ms": round(ad_ms, 2),
+        "adaptive_last_mean_entropy": round(ad_mean_h, 5),
         "accepted_last_step": n_acc,
         "accepted_per_step": acc_steps,
         "accepted_mean": round(sum(acc_steps) / len(acc_steps), 2),
