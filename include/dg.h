@@ -275,7 +275,7 @@ int dg_commit_and_step(const dg_model_config* cfg, const dg_weights* w, dg_kv_ca
  * Errors: DG_ERR_INVALID_ARG for null tokens / outputs or batch < 1,
  * DG_ERR_KV_CAPACITY if the cache is full (nothing written),
  * DG_ERR_WORKSPACE if the workspace is short, DG_ERR_UNSUPPORTED above the
- * routing limits (batch <= 16384, batch * top_k <= 32768). */
+ * routing limit (batch * top_k <= 32768). */
 int dg_ar_step(const dg_model_config* cfg, const dg_weights* w, dg_kv_cache* cache,
                const int32_t* d_tokens, int32_t batch, int32_t* d_next, void* d_ws,
                size_t ws_bytes, void* stream);
