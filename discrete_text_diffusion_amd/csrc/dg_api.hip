@@ -453,10 +453,13 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
         a.ws0_alt = lw.sh_d_scale; a.ws_alt_stride = 0;  // K slices of one matrix: same output features
       }
       if (bf) {
-        a.n_fb = (s.d + 127) / 128;
+        // fewer (token, slot) pairs than experts (the decode step): one
+        // 16-feature tile per wave, twice the workgroups for the few row tiles
+        const int nwt = (!s.ex8 && (int64_t)T * s.k < s.E) ? 1 : 2;
+        a.n_fb = (s.d + 64 * nwt - 1) / (64 * nwt);
         a.tile_fastest = 1;  // the row tiles of one (expert, feature block) run together (same XCD): a hot
                              // expert's weight slice comes from HBM once and from L2 for its other tiles
-        DG_TRY(launch_wsgemm(a, bm, 2, 64, false, c.st));
+        DG_TRY(launch_wsgemm(a, bm, nwt, 64, false, c.st));
       } else {
         DG_TRY(launch_gemm_simple(a, c.st));
       }
