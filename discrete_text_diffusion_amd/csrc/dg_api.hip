@@ -430,7 +430,25 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
         a.n_fb = (s.de + 63) / 64;
         a.tile_fastest = 1;  // the row tiles of one (expert, feature block) run together (same XCD): a hot
                              // expert's weight slice comes from HBM once and from L2 for its other tiles
-        DG_TRY(launch_wsgemm(a, bm, 1, bm == 128 ? 64 : s.d % 128 == 0 ? 128 : 64, true, c.st));
+        const int kc = bm == 128 ? 64 : s.d % 128 == 0 ? 128 : 64;
+        const int64_t rows_moe = (int64_t)T * (s.k + s.n_sh);
+        // Fewer (token, slot) pairs than experts (the decode step): a dozen
+        // row tiles x feature blocks cannot keep the weight stream going, so
+        // K is split four ways; gate and up partials go to the workspace and
+        // a summing kernel applies the GeGLU.
+        const int dsplit = 4;
+        if (!s.ex8 && (int64_t)T * s.k < s.E && s.d / kc >= dsplit &&
+            2 * dsplit * rows_moe * s.de <= (int64_t)c.p.g_rows * std::max(s.qkv, s.dsc)) {
+          a.k_split = ((s.d / kc + dsplit - 1) / dsplit) * kc;
+          a.n_split = (s.d + a.k_split - 1) / a.k_split;
+          a.epi = EPI_GEGLU_PARTS; a.out_f32 = c.at<float>(c.p.g_part); a.ldo = s.de;
+          a.split_stride = rows_moe * s.de;
+          DG_TRY(launch_wsgemm(a, bm, 1, kc, true, c.st));
+          DG_TRY(launch_geglu_splits(a.out_f32, a.n_split, a.split_stride, (int)rows_moe, s.de, c.at<void>(c.p.h), s.de,
+                                     c.st));
+        } else {
+          DG_TRY(launch_wsgemm(a, bm, 1, kc, true, c.st));
+        }
       } else {
         DG_TRY(launch_gemm_simple(a, c.st));
       }

@@ -18,6 +18,8 @@ enum GemmEpi : int32_t {
   EPI_GELU = 3,       // out_act[row][n] = act(gelu(acc))
   EPI_QKV = 4,        // q/k/v split, RoPE on q and k, activation rounding, k/v to their store
   EPI_STORE_ACT = 5,  // out_act[row][n] = act(alpha * acc)
+  EPI_GEGLU_PARTS = 6,  // GeGLU K-split: out_f32[split][row][n] = acc_gate,
+                        // out_f32[n_split + split][row][n] = acc_up
 };
 
 enum ActKind : int32_t {
@@ -110,6 +112,10 @@ int launch_wsgemm(const GemmArgs& a, int bm, int nwt, int kc, bool geglu, hipStr
 // partials (EPI_STORE_F32), or with lm != null the LM-head statistics.
 int launch_rowgemm(const GemmArgs& a, const LmArgs* lm, hipStream_t s);
 // Sum of K-split fp32 partials part[s][row][n] (pitch ldp), then a.epi.
+// h[row][n] = bf16(gelu(sum of gate partials) * sum of up partials) over the
+// EPI_GEGLU_PARTS layout (splits summed in split order)
+int launch_geglu_splits(const float* part, int n_split, int64_t split_stride, int rows, int N, void* out, int ldo,
+                        hipStream_t s);
 int launch_split_epilogue(const GemmArgs& a, const float* part, int n_split, int64_t split_stride, int ldp,
                           hipStream_t s);
 int launch_gemm_simple(const GemmArgs& a, hipStream_t s);

@@ -101,6 +101,12 @@ __device__ __forceinline__ void epi_pair(const GemmArgs& a, int ks, int orow, in
     case EPI_GEGLU:
       store_act2<TA>(a.out_act, (int64_t)orow * a.ldo + n, gelu_tanh(g0) * u0, gelu_tanh(g1) * u1);
       break;
+    case EPI_GEGLU_PARTS: {
+      float* o = a.out_f32 + (int64_t)ks * a.split_stride + (int64_t)orow * a.ldo + n;
+      *reinterpret_cast<float2*>(o) = make_float2(g0, g1);
+      *reinterpret_cast<float2*>(o + (int64_t)a.n_split * a.split_stride) = make_float2(u0, u1);
+      break;
+    }
     case EPI_GELU:
       store_act2<TA>(a.out_act, (int64_t)orow * a.ldo + n, gelu_tanh(g0), gelu_tanh(g1));
       break;
@@ -1096,6 +1102,34 @@ int launch_rowgemm(const GemmArgs& a0, const LmArgs* lm, hipStream_t s) {
   if (lm && a.w_fp8) hipLaunchKernelGGL((k_rowgemm<true, true>), grid, block, 0, s, a, l);
   else if (lm) hipLaunchKernelGGL((k_rowgemm<true, false>), grid, block, 0, s, a, l);
   else hipLaunchKernelGGL((k_rowgemm<false, false>), grid, block, 0, s, a, l);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+__global__ __launch_bounds__(kThreads) void k_geglu_splits(const float* part, int n_split, int64_t split_stride,
+                                                          int rows, int N, bf16_t* out, int ldo) {
+  const int64_t pairs = (int64_t)rows * (N >> 1);
+  const int64_t p = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (p >= pairs) return;
+  const int row = (int)(p / (N >> 1));
+  const int n = (int)(p - (int64_t)row * (N >> 1)) * 2;
+  const float* pg = part + (int64_t)row * N + n;
+  const float* pu = pg + (int64_t)n_split * split_stride;
+  float2 g = *reinterpret_cast<const float2*>(pg), u = *reinterpret_cast<const float2*>(pu);
+  for (int s = 1; s < n_split; ++s) {
+    const float2 gs = *reinterpret_cast<const float2*>(pg + s * split_stride);
+    const float2 us = *reinterpret_cast<const float2*>(pu + s * split_stride);
+    g.x += gs.x; g.y += gs.y;
+    u.x += us.x; u.y += us.y;
+  }
+  store_act2<bf16_t>(out, (int64_t)row * ldo + n, gelu_tanh(g.x) * u.x, gelu_tanh(g.y) * u.y);
+}
+
+int launch_geglu_splits(const float* part, int n_split, int64_t split_stride, int rows, int N, void* out, int ldo,
+                        hipStream_t s) {
+  if (n_split < 1 || rows < 1 || N % 2 || ldo % 2) return -1;
+  const int64_t pairs = (int64_t)rows * (N >> 1);
+  hipLaunchKernelGGL(k_geglu_splits, dim3((unsigned)DG_CEIL_DIV(pairs, kThreads)), dim3(kThreads), 0, s, part, n_split,
+                     split_stride, rows, N, reinterpret_cast<bf16_t*>(out), ldo);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
