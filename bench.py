@@ -473,6 +473,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--no-ar", action="store_true", help="skip the single-token decode timing")
+    ap.add_argument("--no-adaptive", action="store_true", help="skip the adaptive-stop canvas")
     ap.add_argument("--pmc-step", action="store_true", help="one denoising step only (counter runs)")
     ap.add_argument("--pmc-copy", action="store_true", help="counter calibration copy only")
     ap.add_argument("--pmc-summarize", nargs=5, metavar=("F", "W", "CF", "CW", "OUT"))
@@ -632,7 +633,7 @@ def main():
     torch.cuda.synchronize()
     t_ad = time.time()
     ad_steps = 48
-    for t in range(48):
+    for t in range(0 if args.no_adaptive else 48):
         dg.dg_denoise_step(cfg, model.weights, cache.struct, canvas.struct, rt.step_params(t, 48, 0, True),
                            ws.ptr, ws.size, st)
         if t >= 1 and bool(canvas.stop.bool().all().item()):
@@ -750,7 +751,7 @@ def main():
         "canvas_tok_s_48_incl_commit": round(T / (ms48 * 1e-3), 2),
         "canvas_tok_s_48_excl_commit": round(T / (48 * step_ms * 1e-3), 2),
         **ar,
-        "adaptive_steps_taken": ad_steps,
+        "adaptive_steps_taken": None if args.no_adaptive else ad_steps,
         "adaptive_canvas_ms": round(ad_ms, 2),
         "adaptive_last_mean_entropy": round(ad_mean_h, 5),
         "accepted_last_step": n_acc,
