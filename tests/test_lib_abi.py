@@ -76,3 +76,50 @@ def test_argument_errors_are_reported_before_launch(dg):
     with pytest.raises(dg.DGError):
         dg.dg_pack_weight_bf16(None, None, 17, 32, None)
     assert dg.dg_status_string(dg.DG_ERR_KV_CAPACITY) == "KV cache capacity exceeded"
+
+
+def _fake_structs(dg, shape, B, C, cap, length):
+    """Weights, cache and canvas whose device pointers are fake (aligned,
+    never dereferenced): every call below is rejected by the host-side checks
+    before anything is enqueued."""
+    fake = 1 << 40
+    layers = (dg.LayerWeights * shape.n_layers)(
+        *[dg.LayerWeights(*([fake] * 9 + [None] * 6)) for _ in range(shape.n_layers)])
+    w = dg.Weights(fake, fake, fake, fake, fake, layers, 1.0, None)
+    cache = dg.KVCache(fake, fake, B, cap, length)
+    cv = dg.Canvas(B, C, fake, fake, None, None, None, *([fake] * 9), fake)
+    return w, cache, cv, fake
+
+
+def test_new_entry_points_check_arguments_on_the_host(dg):
+    from synth.configs import TINY
+    from discrete_text_diffusion_amd.runtime import model_config
+    cfg = model_config(TINY)
+    step = lambda t, n, b: dg.StepParams(t, n, b, 1, 0.1, 0.005)  # noqa: E731
+
+    def status(fn, *args):
+        with pytest.raises(dg.DGError) as e:
+            fn(*args)
+        return e.value.status
+
+    w, cache, cv, fake = _fake_structs(dg, TINY, 1, 32, 64, 16)
+    big = 1 << 50
+    # commit + next step: the next step must be step 0 of the following block
+    assert status(dg.dg_commit_and_step, cfg, w, cache, cv, step(5, 12, 0), step(1, 12, 1), fake, big,
+                  None) == dg.DG_ERR_INVALID_ARG
+    assert status(dg.dg_commit_and_step, cfg, w, cache, cv, step(5, 12, 0), step(0, 12, 2), fake, big,
+                  None) == dg.DG_ERR_INVALID_ARG
+    # committed rows and the next canvas's scratch rows: 16 + 2 x 32 > 64
+    assert status(dg.dg_commit_and_step, cfg, w, cache, cv, step(5, 12, 0), step(0, 12, 1), fake, big,
+                  None) == dg.DG_ERR_KV_CAPACITY
+    # single-token decode: batch, full cache, workspace
+    assert status(dg.dg_ar_step, cfg, w, cache, fake, 0, fake, fake, big, None) == dg.DG_ERR_INVALID_ARG
+    full = dg.KVCache(fake, fake, 1, 64, 64)
+    assert status(dg.dg_ar_step, cfg, w, full, fake, 1, fake, fake, big, None) == dg.DG_ERR_KV_CAPACITY
+    assert status(dg.dg_ar_step, cfg, w, cache, fake, 1, fake, None, 0, None) == dg.DG_ERR_WORKSPACE
+    assert status(dg.dg_test_ar_step, cfg, w, cache, fake, 1, fake, None, fake, big, None) == dg.DG_ERR_INVALID_ARG
+    assert cache.length == 16 and full.length == 64
+    # more than 16384 canvas tokens in one denoising step
+    w2, cache2, cv2, _ = _fake_structs(dg, TINY, 17, 1024, 1024, 0)
+    assert status(dg.dg_denoise_step, cfg, w2, cache2, cv2, step(0, 12, 0), fake, big,
+                  None) == dg.DG_ERR_UNSUPPORTED
