@@ -277,7 +277,6 @@ int dense_gemm(const Ctx& c, GemmArgs a, int M, int N, int K, int max_split, int
       if (used_split) *used_split = a.n_split;
       return launch_rowgemm(a, nullptr, c.st);
     }
-    if (a.n_split == 1) return launch_rowgemm(a, nullptr, c.st);  // the epilogue in place
     if ((int64_t)M * N * a.n_split > g_cap) return DG_ERR_UNSUPPORTED;
     GemmArgs pa = a;
     pa.epi = EPI_STORE_F32; pa.out_f32 = c.at<float>(c.p.g_part); pa.ldo = N; pa.split_stride = (int64_t)M * N;

@@ -859,13 +859,8 @@ __global__ __launch_bounds__(RG_THREADS, 1) void k_rowgemm(GemmArgs a, LmArgs lm
         const int r = rh * 128 + j * 16 + (lane & 15);
         if (r < nrows) {
           const f32x4_t g = acc[i][j];
-          if (a.epi == EPI_STORE_F32) {
-            *reinterpret_cast<float4*>(a.out_f32 + (int64_t)ks * a.split_stride + (int64_t)(row0 + r) * a.ldo + n) =
-                make_float4(a.alpha * g[0], a.alpha * g[1], a.alpha * g[2], a.alpha * g[3]);
-          } else {  // one K split: the epilogue in place (pairs n, n + 1 and n + 2, n + 3)
-            epi_pair<bf16_t>(a, 0, row0 + r, n, g[0], g[1], g[0], g[1]);
-            epi_pair<bf16_t>(a, 0, row0 + r, n + 2, g[2], g[3], g[2], g[3]);
-          }
+          *reinterpret_cast<float4*>(a.out_f32 + (int64_t)ks * a.split_stride + (int64_t)(row0 + r) * a.ldo + n) =
+              make_float4(a.alpha * g[0], a.alpha * g[1], a.alpha * g[2], a.alpha * g[3]);
         }
       }
     }
@@ -1095,12 +1090,7 @@ int launch_rowgemm(const GemmArgs& a0, const LmArgs* lm, hipStream_t s) {
   if (a.tiles || a.row_map || a.w1 || a.act_kind != ACT_BF16 || a.M < 1 || a.N % 16 ||
       a.K % RG_KC || a.k_split % RG_KC || a.act_ld % 8)
     return -1;
-  // other epilogues (QKV, GELU, activation store) in place, without a K split
-  if (!lm && a.epi == EPI_STORE_F32 && (!a.out_f32 || a.ldo % 4)) return -1;
-  if (!lm && a.epi != EPI_STORE_F32 &&
-      (a.n_split != 1 || (a.epi != EPI_QKV && a.epi != EPI_GELU && a.epi != EPI_STORE_ACT) ||
-       (a.epi != EPI_QKV && (!a.out_act || a.ldo % 2))))
-    return -1;
+  if (!lm && (a.epi != EPI_STORE_F32 || !a.out_f32 || a.ldo % 4)) return -1;
   if (lm && a.N % 256) return -1;
   if (a.n_fb != (a.N + bn - 1) / bn || a.n_split < 1 || (int64_t)a.n_split * a.k_split < a.K) return -1;
   a.max_tiles = (a.M + RG_ROWS - 1) / RG_ROWS;
