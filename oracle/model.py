@@ -102,13 +102,16 @@ class Weights:
                 del self._cache[k]
 
 
-# Every product below is evaluated by mm().  By default it accumulates in
-# float64.  accumulation("f32") evaluates the same definition with float32
-# operands (exact copies of the bf16 values that feed each product) and
-# float32 sums: a second correct evaluation order, used only to measure how
-# far two such evaluations drift apart on a given problem (bf16 rounding of
-# activations turns last-bit differences into whole-ulp ones).  Expected values
-# always come from the float64 default.
+# Every product below is evaluated by mm(), every RMSNorm by norm(), every
+# attention softmax by attention(), every residual sum by resid().  By default
+# all of them work in float64.  accumulation("f32") evaluates the same
+# definition in float32 arithmetic (the operands of each product are exact
+# float32 copies of the bf16 values that feed it; products, sums, the norm's
+# mean of squares, the softmax and the residual stream in float32; storage
+# roundings unchanged): a second correct evaluation order, used only to
+# measure how far two such evaluations drift apart on a given problem (bf16
+# rounding of activations turns last-bit differences into whole-ulp ones).
+# Expected values always come from the float64 default.
 _ACC = ["f64"]
 
 
@@ -128,6 +131,21 @@ def mm(a, b) -> np.ndarray:
     if _ACC[0] == "f64":
         return np.asarray(a) @ np.asarray(b)
     return (np.asarray(a, dtype=np.float32) @ np.asarray(b, dtype=np.float32)).astype(np.float64)
+
+
+def norm(shape: ModelShape, x: np.ndarray) -> np.ndarray:
+    """RMSNorm (gain 1) in the current accumulation precision."""
+    if _ACC[0] == "f64":
+        return rmsnorm(x, shape.norm_eps)
+    x32 = np.asarray(x, dtype=np.float32)
+    ms = np.mean(x32 * x32, axis=-1, keepdims=True, dtype=np.float32)
+    return (x32 / np.sqrt(ms + np.float32(shape.norm_eps))).astype(np.float64)
+
+
+def resid(x: np.ndarray) -> np.ndarray:
+    """A residual-stream value: kept in float64 by default, float32 in the
+    float32 evaluation (the GPU's residual is float32)."""
+    return x if _ACC[0] == "f64" else np.asarray(x, dtype=np.float32).astype(np.float64)
 
 
 def round_act(shape: ModelShape, x: np.ndarray) -> np.ndarray:
@@ -157,7 +175,7 @@ def embed(shape: ModelShape, W: Weights, tokens: np.ndarray, sc_probs=None) -> n
         P = round_act(shape, np.asarray(sc_probs, dtype=np.float64))
         ebar = round_act(shape, mm(P, E))                       # expected embedding
         h = round_act(shape, gelu_tanh(mm(ebar, W.get("sc_up").T)))
-        x = x + mm(h, W.get("sc_down").T)
+        x = resid(x + mm(h, W.get("sc_down").T))
     return x
 
 
@@ -181,9 +199,11 @@ def attention(shape: ModelShape, q, k_all, v_all, n_prefix: int, causal: bool) -
         hk = h // group
         s = mm(q[:, h, :], k_all[hk].T) * scale
         s = np.where(mask, s, -np.inf)
+        if _ACC[0] == "f32":
+            s = s.astype(np.float32)
         s = s - s.max(axis=1, keepdims=True)
         e = np.exp(s)
-        pr = e / e.sum(axis=1, keepdims=True)
+        pr = (e / e.sum(axis=1, keepdims=True)).astype(np.float64)
         out[:, h, :] = mm(pr, v_all[hk])
     return out
 
@@ -238,7 +258,7 @@ def layer_forward(shape: ModelShape, W: Weights, layer: int, x: np.ndarray, cach
     B, n, d = x.shape
     L = cache.length
     s = shape
-    nrm = round_act(s, rmsnorm(x, s.norm_eps))
+    nrm = round_act(s, norm(s, x))
     qkv = mm(nrm, W.get("wqkv", layer).T)                           # [B, n, rows]
     q = qkv[..., : s.q_dim].reshape(B, n, s.n_q_heads, s.d_head)
     k = qkv[..., s.q_dim: s.q_dim + s.kv_dim].reshape(B, n, s.n_kv_heads, s.d_head)
@@ -256,17 +276,17 @@ def layer_forward(shape: ModelShape, W: Weights, layer: int, x: np.ndarray, cach
         cache.k[layer][:, :, L:L + n] = k.transpose(0, 2, 1, 3)
         cache.v[layer][:, :, L:L + n] = v.transpose(0, 2, 1, 3)
     o = round_act(s, o.reshape(B, n, s.q_dim))
-    x = x + mm(o, W.get("wo", layer).T)
-    n2 = round_act(s, rmsnorm(x, s.norm_eps)).reshape(B * n, d)
+    x = resid(x + mm(o, W.get("wo", layer).T))
+    n2 = round_act(s, norm(s, x)).reshape(B * n, d)
     y, r, ids, w = moe(s, W, layer, n2, ret_routing=True)
     if trace is not None:
         trace.setdefault("router_logits", []).append(r)
         trace.setdefault("expert_ids", []).append(ids)
         trace.setdefault("x_attn", []).append(x.copy())
-    return x + y.reshape(B, n, d)
+    return resid(x + y.reshape(B, n, d))
 
 
 def final_logits(shape: ModelShape, W: Weights, x: np.ndarray, lm_scale: float) -> np.ndarray:
     """z = s_lm * (RMSNorm(x) W_lm^T)."""
-    nrm = round_act(shape, rmsnorm(x, shape.norm_eps))
+    nrm = round_act(shape, norm(shape, x))
     return lm_scale * mm(nrm, W.get("lm_head").T)
