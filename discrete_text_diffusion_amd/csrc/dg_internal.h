@@ -35,7 +35,7 @@ struct QkvEpi {
   int64_t kv_b_stride;  // elements between sequences of the k/v store
   int64_t kv_h_stride;  // elements between kv heads (= capacity * d_head)
   int32_t kv_row0;      // first row written inside each head (cache length for append)
-  int32_t v_pitch;      // row pitch of the transposed V store ([d_head][rows] per head; fp16 for bf16 models)
+  int32_t v_pitch;      // row pitch of the transposed V store ([d_head][rows] per head)
   int32_t seq_len;      // tokens per sequence in this call
   int32_t pos0;         // absolute position of the first token of each sequence
   float rope_base;

@@ -8,9 +8,7 @@
 //
 // K is stored [seq][kv_head][row][d_head]; V is stored transposed,
 // [seq][kv_head][d_head][row] with row pitch vp, so that the V^T operand
-// streams as contiguous key runs.  bf16 models keep K in bf16 and V^T in fp16
-// (every bf16 value of magnitude >= 2^-17 is exact in fp16; V is rounded to
-// bf16 first).
+// streams as contiguous key runs.  bf16 models keep both in bf16.
 //
 // bf16 path (d_head = 256): one workgroup of 8 waves (two per SIMD) = one KV
 // head, 128 query rows (the G query heads sharing that KV head x 128/G
@@ -21,9 +19,12 @@
 // ahead of the MFMAs.  S^T = K Q^T comes from v_mfma_f32_16x16x32_bf16 with
 // the key rows of each 16-row MFMA chosen so that every lane ends up with 8
 // consecutive keys per 32-key step: the exponentiated scores are directly
-// the B operand of O^T = V^T P^T (v_mfma_f32_16x16x32_f16, P split into two
-// fp16 parts so the product keeps fp32 accuracy), and the V^T operand is one
-// 16-byte read.  Online softmax in the exp2 domain.  Splits write (m, l, O)
+// the B operand of O^T = V^T P^T (the same bf16 MFMA), and the V^T operand is
+// one 16-byte read.  P is split into two bf16 parts, hi = bf16(p) and lo =
+// bf16(p - hi), two MFMAs each, so the weights keep 2^-18 relative accuracy:
+// with a single bf16 P the output over thousands of diffuse keys carries an
+// error close to its own bf16 rounding step, and a large share of those
+// roundings flip.  Online softmax in the exp2 domain.  Splits write (m, l, O)
 // partials merged in split order.
 #include "dg_internal.h"
 
@@ -47,8 +48,6 @@ struct AttnArgs {
   float2* part_ml;        // [split][T][n_q] (m in log2 units, l)
   void* out;              // [T][n_q * d]
 };
-
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int ATT_D = 256;
 constexpr int ATT_KT = 64;                  // keys per tile
@@ -211,7 +210,7 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void k_attn_mfma(AttnArgs a) {
     // no per-element mask (every tile but a split's last, and in the causal
     // encode those below the wave's diagonal).
     const bool full = (k0 + ATT_KT <= ke) && (!a.causal || k0 + ATT_KT - 1 <= a.n_prefix + qi0);
-    f16x8_t pf[ATT_QT][2], pl[ATT_QT][2];
+    bf16x8_t pf[ATT_QT][2], pl[ATT_QT][2];
 #pragma unroll
     for (int qt = 0; qt < ATT_QT; ++qt) {
       float sv[16];
@@ -242,8 +241,8 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void k_attn_mfma(AttnArgs a) {
       mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
       // The reference point m_run moves only when the tile's maximum exceeds
       // it by more than 8 (log2 units), so the weights 2^(s - m_run) stay
-      // <= 2^8 (exact in the fp16 hi/lo pair) and the O rescale is rare.  O
-      // and l always share the same reference, so O / l is unchanged.
+      // <= 2^8 and the O rescale is rare.  O and l always share the same
+      // reference, so O / l is unchanged.
       // (Hardware exp2: arguments <= 8; results below 2^-126 flush to zero.)
       float alpha = 1.f;
       if (mt > m_run[qt] + 8.f) {  // also the first visible key (m_run = -inf)
@@ -258,10 +257,10 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void k_attn_mfma(AttnArgs a) {
         for (int e = 0; e < 4; ++e) {
           const float p = __builtin_amdgcn_exp2f(sv[x * 4 + e] - shift);
           ps += p;
-          const _Float16 hi = (_Float16)p;
+          const __bf16 hi = (__bf16)p;  // round to nearest even
           const int kk = x >> 1, ep = 4 * (x & 1) + e;
           pf[qt][kk][ep] = hi;
-          pl[qt][kk][ep] = (_Float16)(p - (float)hi);
+          pl[qt][kk][ep] = (__bf16)(p - (float)hi);
         }
       l_run[qt] = l_run[qt] * alpha + ps;
       if (__ballot(alpha != 1.f)) {
@@ -275,11 +274,11 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void k_attn_mfma(AttnArgs a) {
       const int dd = t * 16 + c16;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const f16x8_t vf = *reinterpret_cast<const f16x8_t*>(vs + dd * 128 + (((4 * kk + g) ^ (dd & 7)) << 4));
+        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(vs + dd * 128 + (((4 * kk + g) ^ (dd & 7)) << 4));
 #pragma unroll
         for (int qt = 0; qt < ATT_QT; ++qt) {
-          o[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[qt][kk], o[qt][t], 0, 0, 0);
-          o[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pl[qt][kk], o[qt][t], 0, 0, 0);
+          o[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qt][kk], o[qt][t], 0, 0, 0);
+          o[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[qt][kk], o[qt][t], 0, 0, 0);
         }
       }
     }
@@ -436,7 +435,7 @@ __global__ __launch_bounds__(64) void k_attn_simple(AttnArgs a) {
 }  // namespace
 
 // Host launcher.  dtype: 0 = fp32 activations (plain path), 1 = bf16 (MFMA
-// path: d = 256, K bf16, V^T fp16, vp a multiple of 8).
+// path: d = 256, K and V^T bf16, vp a multiple of 8).
 int launch_attention(int dtype, const void* q, int64_t q_ld, const void* k, const void* v, int64_t s_seq,
                      int64_t s_head, int vp, int n_keys, int n_prefix, int causal, int seq_len, int n_seq, int n_q,
                      int n_kv, int d, int n_split, float* part_o, float2* part_ml, void* out, hipStream_t s) {

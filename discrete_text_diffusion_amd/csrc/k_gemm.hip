@@ -140,13 +140,7 @@ __device__ __forceinline__ void epi_pair(const GemmArgs& a, int ks, int orow, in
         const int64_t head = (int64_t)seq * q.kv_b_stride + (int64_t)h * q.kv_h_stride;
         if (is_k) {
           store_act2<TA>(q.k, head + (int64_t)(q.kv_row0 + i) * q.d_head + dd, v0, v1);
-        } else if constexpr (sizeof(TA) == 2) {
-          // V is stored transposed, [d_head][rows], in fp16: the bf16-rounded
-          // value, exact in fp16 from 2^-17 up
-          _Float16* vb = reinterpret_cast<_Float16*>(q.v) + head + (int64_t)dd * q.v_pitch + q.kv_row0 + i;
-          vb[0] = (_Float16)bf2f(f2bf(v0));
-          vb[q.v_pitch] = (_Float16)bf2f(f2bf(v1));
-        } else {  // fp32 models: V^T in fp32
+        } else {  // V is stored transposed, [d_head][rows], in the activation type
           TA* vb = reinterpret_cast<TA*>(q.v) + head + (int64_t)dd * q.v_pitch + q.kv_row0 + i;
           vb[0] = to_act<TA>(v0);
           vb[q.v_pitch] = to_act<TA>(v1);

@@ -150,8 +150,7 @@ class DeviceCache:
         n = shape.n_layers * batch * shape.n_kv_heads * capacity * shape.d_head
         dt = _tdtype(shape)
         self.k = torch.zeros(n, dtype=dt, device=device)
-        # bf16 models keep V^T in fp16 (exact for the bf16-rounded values)
-        self.v = torch.zeros(n, dtype=torch.float16 if dt == torch.bfloat16 else dt, device=device)
+        self.v = torch.zeros(n, dtype=dt, device=device)  # V^T, [d_head][row] per head
         self.shape = shape
         self.struct = KVCache(self.k.data_ptr(), self.v.data_ptr(), batch, capacity, 0)
 

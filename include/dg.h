@@ -120,10 +120,9 @@ typedef struct dg_weights {
 
 /* KV cache, rows [0, length) valid:
  *   k: [n_layers][batch][n_kv][capacity][d_head]   post-RoPE keys, model dtype
- *   v: [n_layers][batch][n_kv][d_head][capacity]   values, stored transposed so
- *      that attention streams contiguous runs of keys per dimension; fp32 for
- *      fp32 models, fp16 for bf16 models (the bf16-rounded value, exact in
- *      fp16 from magnitude 2^-17 up).
+ *   v: [n_layers][batch][n_kv][d_head][capacity]   values, model dtype, stored
+ *      transposed so that attention streams contiguous runs of keys per
+ *      dimension.
  * bf16 models: capacity a multiple of 8 (else DG_ERR_UNSUPPORTED).
  * Rows [length, capacity) are scratch: the denoiser writes its canvas K/V to
  * rows [length, length + canvas) without changing `length`.
