@@ -124,6 +124,8 @@ _t_route = _sig("dg_test_route_from_logits", c_int32, _P(ModelConfig), c_void_p,
 _t_logits = _sig("dg_test_forward_logits", c_int32, _P(ModelConfig), _P(Weights), _P(KVCache), _P(Canvas),
                  _P(StepParams), c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p)
 
+_t_step = _sig("dg_test_denoise_step", c_int32, _P(ModelConfig), _P(Weights), _P(KVCache), _P(Canvas),
+               _P(StepParams), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p)
 _t_encode = _sig("dg_test_encode_append", c_int32, _P(ModelConfig), _P(Weights), _P(KVCache), c_void_p, c_int32,
                  c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p)
 _t_ar = _sig("dg_test_ar_step", c_int32, _P(ModelConfig), _P(Weights), _P(KVCache), c_void_p, c_int32, c_void_p,
@@ -134,7 +136,7 @@ EXPORTED = ("dg_temperature", "dg_workspace_bytes", "dg_pack_weight_bf16", "dg_p
             "dg_init_canvas", "dg_encode_append", "dg_denoise_step", "dg_commit_block", "dg_status_string",
             "dg_test_sample_from_logits", "dg_test_route_from_logits", "dg_test_forward_logits",
             "dg_denoise_step_traced", "dg_encode_append_traced", "dg_test_encode_append", "dg_ar_step", "dg_commit_and_step",
-            "dg_test_ar_step")
+            "dg_test_ar_step", "dg_test_denoise_step")
 
 
 def _check(rc: int, where: str):
@@ -216,6 +218,13 @@ def dg_test_forward_logits(cfg, weights, cache, canvas, params, d_force_ids, d_r
     _check(_t_logits(ctypes.byref(cfg), ctypes.byref(weights), ctypes.byref(cache), ctypes.byref(canvas),
                      ctypes.byref(params), d_force_ids, d_router_logits, d_logits, ws, ws_bytes, stream),
            "dg_test_forward_logits")
+
+
+def dg_test_denoise_step(cfg, weights, cache, canvas, params, d_force_ids, d_router_logits, d_logits, ws,
+                         ws_bytes: int, stream, d_teacher_x=None, d_layer_out=None) -> None:
+    _check(_t_step(ctypes.byref(cfg), ctypes.byref(weights), ctypes.byref(cache), ctypes.byref(canvas),
+                   ctypes.byref(params), d_force_ids, d_router_logits, d_logits, d_teacher_x, d_layer_out, ws,
+                   ws_bytes, stream), "dg_test_denoise_step")
 
 
 def dg_denoise_step_traced(cfg, weights, cache, canvas, params, ws, ws_bytes: int, stream, trace) -> None:

@@ -83,13 +83,18 @@ struct Plan {
   int Tdn;      // denoise tokens
   int att_rows; // attention partial rows (split x tokens)
   int g_rows;   // rows (x the widest N) of the split-epilogue partial buffer
+  int64_t o_rows;  // rows (x d_model) of the O-projection K-split partials
   size_t x, n, q, o, att_o, att_ml, o_part, r_part, ids, wts, row_token, inv, offsets, tiles,
       n_tiles, h, Y, lm_f, lm_i, logits, e_part, ebar, hsc, g_part, rcnt, total;
 };
 
-Plan make_plan(const Shape& s, int batch, int max_canvas) {
+// step_only: a plan for denoising steps alone (no encode passes), whose
+// buffers hold batch * max_canvas tokens.  Its launches are the same as the
+// full plan's for those steps: every dispatch choice reads either the step's
+// own sizes or a capacity both plans give the same value at these sizes.
+Plan make_plan(const Shape& s, int batch, int max_canvas, bool step_only = false) {
   Plan p;
-  p.T = max_tokens(s, batch, max_canvas);
+  p.T = step_only ? batch * max_canvas : max_tokens(s, batch, max_canvas);
   p.Tdn = batch * max_canvas;
   p.att_rows = std::max(4096, kMaxSplit * p.Tdn);
   const size_t T = p.T, Tdn = p.Tdn;
@@ -103,7 +108,10 @@ Plan make_plan(const Shape& s, int batch, int max_canvas) {
   p.o = take(T * s.qdim * s.act);
   p.att_o = take((size_t)p.att_rows * s.nq * s.dh * 4);
   p.att_ml = take((size_t)p.att_rows * s.nq * 8);
-  p.o_part = take(8 * T * s.d * 4);
+  // O-projection partials: up to min(16, o_rows / rows) K splits (16 for a
+  // step of at most 2048 tokens under either plan)
+  p.o_rows = step_only ? 16 * (int64_t)Tdn : 8 * (int64_t)T;
+  p.o_part = take((size_t)p.o_rows * s.d * 4);
   p.r_part = take(16 * T * s.E * 4);  // router K-split partials (up to 16)
   p.ids = take(T * s.k * 4);
   p.wts = take(T * s.k * 4);
@@ -138,6 +146,8 @@ struct Ctx {
   dg_trace* tr = nullptr;
   const int32_t* force_ids = nullptr;  // test path: [n_layers][T][k] expert ids
   float* router_out = nullptr;         // test path: [n_layers][T][E] router logits
+  const float* teacher_x = nullptr;    // test path: [n_layers + 1][T][d] residual each layer (and the head) starts from
+  float* layer_out = nullptr;          // test path: [n_layers + 1][T][d] embedding output, then each layer's output
   size_t head_row0 = 0;                // first row of the normalised output the LM head reads
   template <typename T> T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
 };
@@ -330,6 +340,8 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
   void* xn = c.at<void>(c.p.n);
   for (int l = 0; l < s.L; ++l) {
     const dg_layer_weights& lw = c.w->layers[l];
+    if (c.teacher_x)  // test path: this layer starts from the given residual
+      DG_TRY(launch_set_norm(bf, c.teacher_x + (int64_t)l * T * s.d, c.at<float>(c.p.x), xn, T, s.d, s.eps, c.st));
     char* kc = reinterpret_cast<char*>(cache->k) + (size_t)l * layer_elems * s.act;
     char* vc = reinterpret_cast<char*>(cache->v) + (size_t)l * layer_elems * s.act;
     // q, k, v with RoPE
@@ -384,7 +396,7 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
       a.w0 = lw.wo;
       a.epi = EPI_STORE_F32; a.out_f32 = c.at<float>(c.p.o_part); a.ldo = s.d; a.split_stride = (int64_t)T * s.d;
       int n_split = 1;
-      DG_TRY(dense_gemm(c, a, T, s.d, s.qdim, std::min(16, 8 * c.p.T / T), &n_split));
+      DG_TRY(dense_gemm(c, a, T, s.d, s.qdim, (int)std::min<int64_t>(16, c.p.o_rows / T), &n_split));
       DG_TRY(launch_resid_norm(bf, c.at<float>(c.p.x), c.at<float>(c.p.o_part), n_split, (int64_t)T * s.d, xn, T, s.d,
                                s.eps, c.st));
     }
@@ -487,6 +499,9 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
       DG_TRY(launch_combine_norm(bf, c.at<float>(c.p.x), c.at<float>(c.p.Y), c.at<int32_t>(c.p.inv),
                                  c.at<float>(c.p.wts), T, s.k, s.n_sh, xn, s.d, s.eps, c.st));
     }
+    if (c.layer_out)  // test path: this layer's output residual
+      DG_TRY(launch_copy_i32(reinterpret_cast<int32_t*>(c.layer_out + (int64_t)(l + 1) * T * s.d),
+                             c.at<int32_t>(c.p.x), T * s.d, c.st));
   }
   return DG_OK;
 }
@@ -644,11 +659,11 @@ int lm_head_rows(const Ctx& c, int T, LmArgs lm) {
 }
 
 // The canvas LM head: statistics at the step's temperature, the next step's
-// self-conditioning input (unless the logits are being captured).
-int lm_head(const Ctx& c, const dg_canvas* cv, const dg_step_params* p, float* logits_out) {
+// self-conditioning input (unless the logits are being captured without it).
+int lm_head(const Ctx& c, const dg_canvas* cv, const dg_step_params* p, float* logits_out, bool side = false) {
   LmArgs lm;
   memset(&lm, 0, sizeof(lm));
-  lm.p_side = logits_out ? nullptr : cv->p_side;
+  lm.p_side = (logits_out && !side) ? nullptr : cv->p_side;
   lm.logits = logits_out;
   lm.inv_tau = 1.0f / dg_temperature(p->t, p->n_steps);
   lm.seeds = cv->seeds;
@@ -719,6 +734,10 @@ int check_step(const dg_step_params* p) {
 static int encode_impl(const dg_model_config* cfg, const dg_weights* w, dg_kv_cache* cache, const int32_t* d_tokens,
                        int32_t batch, int32_t n_tokens, void* d_ws, size_t ws_bytes, void* stream, dg_trace* trace,
                        const int32_t* force_ids, float* router_out);
+static int denoise_impl(const dg_model_config* cfg, const dg_weights* w, const dg_kv_cache* cache, dg_canvas* cv,
+                        const dg_step_params* p, void* d_ws, size_t ws_bytes, void* stream, dg_trace* trace,
+                        const int32_t* force_ids, float* router_out, float* logits_out, bool step_only = false,
+                        const float* teacher_x = nullptr, float* layer_out = nullptr);
 
 extern "C" {
 
@@ -823,6 +842,22 @@ int dg_denoise_step(const dg_model_config* cfg, const dg_weights* w, const dg_kv
 
 int dg_denoise_step_traced(const dg_model_config* cfg, const dg_weights* w, const dg_kv_cache* cache, dg_canvas* cv,
                            const dg_step_params* p, void* d_ws, size_t ws_bytes, void* stream, dg_trace* trace) {
+  return denoise_impl(cfg, w, cache, cv, p, d_ws, ws_bytes, stream, trace, nullptr, nullptr, nullptr);
+}
+
+int dg_test_denoise_step(const dg_model_config* cfg, const dg_weights* w, const dg_kv_cache* cache, dg_canvas* cv,
+                         const dg_step_params* p, const int32_t* d_force_ids, float* d_router_logits, float* d_logits,
+                         const float* d_teacher_x, float* d_layer_out, void* d_ws, size_t ws_bytes, void* stream) {
+  return denoise_impl(cfg, w, cache, cv, p, d_ws, ws_bytes, stream, nullptr, d_force_ids, d_router_logits, d_logits,
+                      false, d_teacher_x, d_layer_out);
+}
+
+}  // extern "C"
+
+static int denoise_impl(const dg_model_config* cfg, const dg_weights* w, const dg_kv_cache* cache, dg_canvas* cv,
+                        const dg_step_params* p, void* d_ws, size_t ws_bytes, void* stream, dg_trace* trace,
+                        const int32_t* force_ids, float* router_out, float* logits_out, bool step_only,
+                        const float* teacher_x, float* layer_out) {
   DG_TRY(check_config(cfg));
   DG_TRY(check_weights(cfg, w));
   DG_TRY(check_canvas(cv, true));
@@ -830,7 +865,7 @@ int dg_denoise_step_traced(const dg_model_config* cfg, const dg_weights* w, cons
   DG_TRY(check_denoise_cache(cfg, cache, cv));
   Ctx c;
   c.s = shape_of(cfg);
-  c.p = make_plan(c.s, cv->batch, cv->canvas);
+  c.p = make_plan(c.s, cv->batch, cv->canvas, step_only);
   DG_TRY(check_ws(c.p, d_ws, ws_bytes));
   if ((int64_t)cv->batch * cv->canvas > std::min(kMaxStepTokens, route_max_tokens())) return DG_ERR_UNSUPPORTED;
   c.ws = (char*)d_ws;
@@ -838,11 +873,23 @@ int dg_denoise_step_traced(const dg_model_config* cfg, const dg_weights* w, cons
   c.w = w;
   if (trace && (!trace->events || !trace->phase || trace->capacity < 0)) return DG_ERR_INVALID_ARG;
   c.tr = trace;
+  c.force_ids = force_ids;
+  c.router_out = router_out;
+  c.teacher_x = teacher_x;
+  c.layer_out = layer_out;
+  const int T = cv->batch * cv->canvas;
   DG_TRY(embed_canvas(c, cv, p));
+  if (layer_out)  // test path: the embedding (+ self-conditioning) output
+    DG_TRY(launch_copy_i32(reinterpret_cast<int32_t*>(layer_out), c.at<int32_t>(c.p.x), T * c.s.d, c.st));
   DG_TRY(run_layers(c, cache, cv->batch, cv->canvas, cache->length, false));
-  DG_TRY(lm_head(c, cv, p, nullptr));
+  if (teacher_x)  // test path: the LM head reads the given final residual
+    DG_TRY(launch_set_norm(c.s.dt == DG_DTYPE_BF16, teacher_x + (int64_t)c.s.L * T * c.s.d, c.at<float>(c.p.x),
+                           c.at<void>(c.p.n), T, c.s.d, c.s.eps, c.st));
+  DG_TRY(lm_head(c, cv, p, logits_out, true));
   return sample_and_select(c, cv, p);
 }
+
+extern "C" {
 
 int dg_ar_step(const dg_model_config* cfg, const dg_weights* w, dg_kv_cache* cache, const int32_t* d_tokens,
                int32_t batch, int32_t* d_next, void* d_ws, size_t ws_bytes, void* stream) {

@@ -137,6 +137,8 @@ int launch_attention(int dtype, const void* q, int64_t q_ld, const void* k, cons
 // k_misc.hip
 int launch_embed_norm(int dtype, const int32_t* tok, const void* emb, const float* add, int n_add, int64_t add_stride,
                       float* x, void* n, int T, int d, float eps, hipStream_t s);
+// x = src; n = RMSNorm(x) per row (T rows of d)
+int launch_set_norm(int dtype, const float* src, float* x, void* n, int T, int d, float eps, hipStream_t s);
 int launch_resid_norm(int dtype, float* x, const float* part, int n_split, int64_t split_stride, void* n, int T, int d,
                       float eps, hipStream_t s);
 int launch_combine_norm(int dtype, float* x, const float* Y, const int32_t* inv, const float* w, int T, int k, int n_sh,

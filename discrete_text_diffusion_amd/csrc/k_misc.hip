@@ -51,6 +51,18 @@ __global__ __launch_bounds__(256) void k_embed_norm(const int32_t* tok, const TA
   write_norm<TA>(xr, n + t * d, d, eps, red);
 }
 
+// x[t] = src[t]; n[t] = RMSNorm(x[t])  (a residual given from outside: the
+// teacher-forced test path).
+template <typename TA>
+__global__ __launch_bounds__(256) void k_set_norm(const float* src, float* x, TA* n, int d, float eps) {
+  __shared__ float red[4];
+  const int64_t t = blockIdx.x;
+  float* xr = x + t * d;
+  for (int i = threadIdx.x; i < d; i += 256) xr[i] = src[t * d + i];
+  __syncthreads();
+  write_norm<TA>(xr, n + t * d, d, eps, red);
+}
+
 // x[t] += sum_s part[s][t] (split order); n[t] = RMSNorm(x[t]).
 template <typename TA>
 __global__ __launch_bounds__(256) void k_resid_norm(float* x, const float* part, int n_split, int64_t split_stride,
@@ -261,6 +273,15 @@ int launch_embed_norm(int dtype, const int32_t* tok, const void* emb, const floa
   else
     hipLaunchKernelGGL(k_embed_norm<float>, dim3(T), dim3(256), 0, s, tok, (const float*)emb, add, n_add, add_stride,
                        x, (float*)n, d, eps);
+  return DG_OK_OR_HIP();
+}
+
+int launch_set_norm(int dtype, const float* src, float* x, void* n, int T, int d, float eps, hipStream_t s) {
+  if (T < 1 || d < 1) return -1;
+  if (dtype == 1)
+    hipLaunchKernelGGL(k_set_norm<bf16_t>, dim3(T), dim3(256), 0, s, src, x, (bf16_t*)n, d, eps);
+  else
+    hipLaunchKernelGGL(k_set_norm<float>, dim3(T), dim3(256), 0, s, src, x, (float*)n, d, eps);
   return DG_OK_OR_HIP();
 }
 

@@ -350,6 +350,29 @@ int dg_test_forward_logits(const dg_model_config* cfg, const dg_weights* w, cons
                            float* d_router_logits, float* d_logits, void* d_ws, size_t ws_bytes,
                            void* stream);
 
+/* The whole denoising step of dg_denoise_step (every canvas output written:
+ * entropy, sample, argmax, accepted set, next tokens, mean entropy, stop,
+ * flags, and the carried self-conditioning input p_side / p_scale), with
+ * optional test hooks (device pointers, NULL for none):
+ *   d_force_ids / d_router_logits: every layer's routing forced / observed as
+ *     in dg_test_forward_logits;
+ *   d_logits [B*C][vocab] fp32: the logits captured as well;
+ *   d_teacher_x [n_layers + 1][B*C][d_model] fp32: teacher forcing, layer l
+ *     starts from the residual d_teacher_x[l] (its RMSNorm recomputed)
+ *     instead of the previous layer's output, and the LM head reads
+ *     d_teacher_x[n_layers]; the canvas K/V of layer l come from that input;
+ *   d_layer_out [n_layers + 1][B*C][d_model] fp32: row 0 receives the
+ *     embedding output (token embedding plus the self-conditioning term, from
+ *     the canvas tokens and the carried or external input), row l + 1 layer
+ *     l's output residual.
+ * Lets a comparison run the product's carried self-conditioning path and
+ * every layer on the oracle's routes and inputs.  Same workspace and errors
+ * as dg_denoise_step. */
+int dg_test_denoise_step(const dg_model_config* cfg, const dg_weights* w, const dg_kv_cache* cache,
+                         dg_canvas* canvas, const dg_step_params* p, const int32_t* d_force_ids,
+                         float* d_router_logits, float* d_logits, const float* d_teacher_x, float* d_layer_out,
+                         void* d_ws, size_t ws_bytes, void* stream);
+
 /* Causal encode-and-append as in dg_encode_append, with the routing of every
  * layer optionally forced and observed as in dg_test_forward_logits:
  * d_force_ids [n_layers][batch*n_tokens][top_k] (rank order), d_router_logits

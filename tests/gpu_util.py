@@ -79,6 +79,83 @@ def bar_or_twin(name, got, want, twin, atol, rtol, factor=2.0):
         f"fp32 twin {te[0]:.2e}/{te[1]:.2e}/{te[2]:.2e}/{te[3]:.2e}; outside the bar: gpu {out}, "
         f"twin {int(np.sum(terr > lim))}")
     if out == 0:
-        return
+        return 0
     bad = [f"q{q}" for q, g, t in zip(qs, ge, te) if g > factor * max(t, 1e-12)]
     assert not bad, f"{name}: {out} elements outside the bar and beyond {factor}x the fp32 twin at {bad}"
+    return out
+
+
+def bar_then_twin(name, got, want, twin_fn, atol, rtol, factor=2.0):
+    """bar_or_twin with the fp32 twin evaluated only when some element is
+    outside the elementwise bar (twin_fn() returns it).  Returns the number
+    of elements outside the bar."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    err = np.abs(got - want)
+    out = int(np.sum(err > atol + rtol * np.abs(want)))
+    if out == 0:
+        q = np.quantile(err.reshape(-1), (0.5, 0.99, 1.0)) if err.size else np.zeros(3)
+        say(f"{name}: gpu |err| median/p99/max {q[0]:.2e}/{q[1]:.2e}/{q[2]:.2e}; all within the bar")
+        return 0
+    say(f"{name}: {out} of {err.size} elements outside the bar; evaluating the fp32 twin")
+    return bar_or_twin(name, got, want, twin_fn(), atol, rtol, factor)
+
+
+def compare_step_decisions(name, z, H, am, acc, samp, nxt, stop, o, max_ties=4):
+    """One canvas's step decisions from the GPU's own logits z [C, V] and
+    entropies H [C] against the oracle's sampler output o on the same inputs.
+
+    Each decision must be equal wherever the oracle's margin for it exceeds
+    what the measured errors can move: argmax by twice the largest logit
+    error; the accepted set by (K + 2) times the largest entropy error (K
+    boundary sums of entropies, plus the gap across the boundary); the sample
+    of a position accepted on both sides by the total variation between the
+    two tempered distributions (the GPU's recomputed from its logits), which
+    bounds the difference of the two CDFs.  Re-noised positions are equal
+    (Philox stream 1), and so is the stop flag.  Returns the number of
+    near-tie mismatches."""
+    from oracle import sampler as smp
+    z = np.asarray(z, dtype=np.float64)
+    dz = float(np.abs(z - np.asarray(o["z"], dtype=np.float64)).max())  # o["z"]: the oracle's logits
+    dH = float(np.abs(np.asarray(H, dtype=np.float64) - o["H"]).max())
+    ties = compare_decisions(f"{name} argmax", am, o["argmax"], o["margin_argmax"], 2 * dz + 1e-6, max_ties)
+    K = int(o["n_accepted"])
+    ties += compare_decisions(f"{name} accepted", acc, o["accepted"], o["margin_accept"], (K + 2) * dH + 1e-6,
+                              max_ties)
+    pg, _, _ = smp.row_statistics(z, o["tau"])
+    tv = float(np.abs(pg - o["p"]).sum(axis=1).max())
+    both = acc & o["accepted"]
+    ties += compare_decisions(f"{name} sample (accepted)", samp[both], o["sample"][both], o["margin_sample"][both],
+                              tv + 1e-6, max_ties)
+    same = acc == o["accepted"]
+    assert np.array_equal(nxt[same & ~acc], o["next_tokens"][same & ~acc]), f"{name}: re-noised tokens differ"
+    assert int(stop) == int(o["stop"]) or o["margin_stop"] < dH, f"{name}: stop flag differs"
+    say(f"{name}: accepted {int(acc.sum())} (oracle {K}), max |dz| {dz:.2e}, max |dH| {dH:.2e}, "
+        f"sample TV bound {tv:.2e}, near-tie decisions {ties}")
+    return ties
+
+
+def entropy_check(name, H, z_gpu, z_oracle, H_oracle, tau, frac_literal=0.99):
+    """Device entropies against the oracle's: every position within 1e-3
+    nats or, where its logits differ (within the logit bar), within the
+    first-order change those measured differences cause,
+    |dH| <= sum_v p_v |a_v - E_p a| |da_v| (a = z / tau), with 50% slack
+    plus the second-order term max|da|^2 and 1e-5 for the fp32 statistics;
+    and at least frac_literal of the positions within the literal 1e-3.
+    Returns the number of positions beyond 1e-3."""
+    from oracle import sampler as smp
+    zo = np.asarray(z_oracle, dtype=np.float64)
+    da = (np.asarray(z_gpu, dtype=np.float64) - zo) / tau
+    p, _, _ = smp.row_statistics(zo, tau)
+    a = zo / tau
+    abar = (p * a).sum(-1, keepdims=True)
+    first = (p * np.abs(a - abar) * np.abs(da)).sum(-1)
+    bound = np.maximum(1e-3, 1.5 * first + np.max(da * da, axis=-1) + 1e-5)
+    err = np.abs(np.asarray(H, dtype=np.float64) - np.asarray(H_oracle, dtype=np.float64))
+    beyond = int(np.sum(err > 1e-3))
+    i = int(np.argmax(err))
+    say(f"{name}: max |dH| {err.max():.3e} (its logit-propagated bound {bound[i]:.3e}); {beyond} of {err.size} "
+        f"positions beyond 1e-3 nats")
+    assert np.all(err <= bound), f"{name}: {int(np.sum(err > bound))} positions beyond the propagated bound"
+    assert beyond <= (1.0 - frac_literal) * err.size, f"{name}: {beyond} positions beyond 1e-3 nats"
+    return beyond

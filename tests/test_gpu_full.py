@@ -23,7 +23,8 @@ from oracle import sampler as smp
 from oracle import step as ost
 from synth.configs import WORKLOADS
 
-from .gpu_util import allclose_report, bar_or_twin, compare_decisions, say
+from .gpu_util import (allclose_report, bar_or_twin, bar_then_twin, compare_decisions,
+                       compare_step_decisions, entropy_check, say)
 from .test_gpu_model import (ATOL, RTOL, ROUTE_EPS, _err_summary, _route_margins, entropy_tolerance,
                              flip_margin_bound)
 
@@ -213,12 +214,14 @@ def test_full_layer_without_selfcond(env, layer1):
 
 
 def test_full_layer_dense_selfcond_entropy(env, layer1):
-    """Dense Dirichlet(0.05) self-conditioning.  The expected embedding sums
-    262144 products; its fp32 sum differs from the exact one by enough to move
-    about 1% of its bf16 roundings, which the bf16 layer then amplifies, so
-    the logit bar is not a property of any fp32 implementation here.  The
-    entropies (the quantities the sampler decides on) keep the 1e-3 nats bar;
-    the logit error is reported."""
+    """Dense Dirichlet(0.05) self-conditioning, the workload's own input.  The
+    expected embedding sums 262144 products; its fp32 sum differs from the
+    exact one by enough to move about 1% of its bf16 roundings, which the bf16
+    layer then amplifies, so the elementwise logit bar is not a property of
+    any fp32 implementation here: the logits are held to the bar or, where
+    it is exceeded, to the fp32-twin criterion (the oracle's definition with
+    fp32 products and sums on the same routes); the entropies (the quantities
+    the sampler decides on) to 1e-3 nats."""
     f = layer1
     shape, wl = f["shape"], f["wl"]
     P = f["P"].astype(np.float64)
@@ -228,6 +231,12 @@ def test_full_layer_dense_selfcond_entropy(env, layer1):
     z, rg = _layer1_forward(env, f, P, force=np.stack(tr["expert_ids"]))
     _err_summary("layer1 dense router logits (oracle routes)", rg, np.stack(tr["router_logits"]))
     _err_summary("layer1 dense logits (oracle routes)", z, zo)
+
+    def twin():
+        with om.accumulation("f32"):
+            return _forced_oracle_logits(f, P, tr["expert_ids"], {})
+
+    bar_then_twin("layer1 dense logits (oracle routes)", z, zo, twin, ATOL, RTOL)
     tau = smp.temperature(wl.first_step, wl.n_steps)
     _, Hg, _ = smp.row_statistics(z, tau)
     _, Ho, _ = smp.row_statistics(zo, tau)
@@ -406,3 +415,256 @@ def test_full30_step_properties(env, full30):
     nxt = cv.tokens.cpu().numpy()
     assert np.array_equal(nxt, smp.initial_canvas(0, 1, C, V))
     cache.struct.length = L
+
+
+def _oracle_canvas_forward(shape, W, oc, tok, sc, lm_scale, fixed_ids=None, acc="f64", keep_x=False):
+    """The oracle's denoiser forward over a canvas, one layer at a time (each
+    layer's weights regenerated and dropped after use, which keeps the host
+    memory of a 30-layer model bounded), with every layer's experts fixed to
+    `fixed_ids` when given and products accumulated in `acc`.
+    Returns (logits [B, C, V], trace); with keep_x, trace["xs"] holds the
+    residual after the embedding and after every layer."""
+    trace = {}
+    orig = om.route
+    if fixed_ids is not None:
+        ids = list(fixed_ids)
+
+        def fixed(shape_, r):
+            sel = ids.pop(0)
+            s_ = np.take_along_axis(r, sel, axis=1)
+            e = np.exp(s_ - s_.max(axis=1, keepdims=True))
+            return sel, e / e.sum(axis=1, keepdims=True)
+
+        om.route = fixed
+    try:
+        with om.accumulation(acc):
+            x = om.embed(shape, W, tok, sc)
+            xs = [x.copy()] if keep_x else None
+            for layer in range(shape.n_layers):
+                x = om.layer_forward(shape, W, layer, x, oc, causal=False, append=False, trace=trace)
+                trace.pop("x_attn", None)
+                W.drop_layer(layer)
+                if keep_x:
+                    xs.append(x.copy())
+            z = om.final_logits(shape, W, x, lm_scale)
+    finally:
+        om.route = orig
+    if keep_x:
+        trace["xs"] = xs
+    return z, trace
+
+
+def _oracle_layer_twin(shape, W, oc, x_in, layer, ids):
+    """One layer of the oracle's denoiser with fp32 products and sums on the
+    given input and experts (the per-layer fp32 twin).  Returns (output
+    residual, router logits)."""
+    orig = om.route
+
+    def fixed(shape_, r):
+        s_ = np.take_along_axis(r, ids, axis=1)
+        e = np.exp(s_ - s_.max(axis=1, keepdims=True))
+        return ids, e / e.sum(axis=1, keepdims=True)
+
+    om.route = fixed
+    tr = {}
+    try:
+        with om.accumulation("f32"):
+            x = om.layer_forward(shape, W, layer, x_in, oc, causal=False, append=False, trace=tr)
+    finally:
+        om.route = orig
+    return x, tr["router_logits"][0]
+
+
+@pytest.fixture(scope="module")
+def full30_rc(env, full30):
+    """The 30-layer model over a seeded N(0,1) cache of 4096 rows in every
+    layer, which both sides read from synth (an fp64 encode of the 4096-token
+    prompt through 30 layers is out of the oracle's reach; the one-layer
+    workload's cache recipe).  The weights are the bench's model."""
+    torch, dg, rt = env
+    wl, shape, model = full30["wl"], full30["shape"], full30["model"]
+    L, C = wl.prefix, wl.canvas
+    say("full30 step parity: seeded N(0,1) cache of 4096 rows x 30 layers")
+    cache = rt.DeviceCache(shape, 1, L + C)
+    cache.fill_random(L, seed=0, std=1.0)
+    oc = om.KVCache(shape, 1, L + C)
+    for name, tid in (("k", synth.TID["kv_k"]), ("v", synth.TID["kv_v"])):
+        vals = synth.normal(0, tid, (shape.n_layers, 1, shape.n_kv_heads, L, shape.d_head), 1.0)
+        for l in range(shape.n_layers):
+            getattr(oc, name)[l][:, :, :L] = synth.bf16_bits_to_f32(vals[l]).astype(np.float64)
+        del vals
+    oc.length = L
+    cv = rt.DeviceCanvas(shape, 1, C, [0])
+    torch.cuda.synchronize()
+    return dict(wl=wl, shape=shape, model=model, cache=cache, oc=oc, cv=cv, ws=full30["ws"], W=om.Weights(shape))
+
+
+def _gpu_step(env, f, t, N, force=None, teacher=None, adaptive=False):
+    """dg_test_denoise_step on the GPU canvas: the product's whole step, the
+    routes forced when given, every layer teacher-forced from the given
+    residuals [n_layers + 1][C][d] when given.  Returns (logits [C, V],
+    router logits [L, C, E], residuals [n_layers + 1][C][d]: the embedding
+    output, then every layer's output)."""
+    torch, dg, rt = env
+    shape, C = f["shape"], f["wl"].canvas
+    out = torch.empty(C * shape.vocab, dtype=torch.float32, device="cuda")
+    rout = torch.empty(shape.n_layers * C * shape.n_experts, dtype=torch.float32, device="cuda")
+    xo = torch.empty((shape.n_layers + 1) * C * shape.d_model, dtype=torch.float32, device="cuda")
+    d_force = d_teach = None
+    if force is not None:
+        d_force = torch.from_numpy(np.ascontiguousarray(force, dtype=np.int32).reshape(-1)).cuda()
+    if teacher is not None:
+        d_teach = torch.from_numpy(np.ascontiguousarray(teacher, dtype=np.float32).reshape(-1)).cuda()
+    dg.dg_test_denoise_step(f["model"].cfg, f["model"].weights, f["cache"].struct, f["cv"].struct,
+                            rt.step_params(t, N, 0, adaptive), d_force.data_ptr() if d_force is not None else None,
+                            rout.data_ptr(), out.data_ptr(), f["ws"].ptr, f["ws"].size, rt.stream_handle(),
+                            d_teach.data_ptr() if d_teach is not None else None, xo.data_ptr())
+    torch.cuda.synchronize()
+    return (out.cpu().numpy().reshape(C, shape.vocab), rout.cpu().numpy().reshape(shape.n_layers, C, shape.n_experts),
+            xo.cpu().numpy().reshape(shape.n_layers + 1, C, shape.d_model))
+
+
+def _teacher_step_checks(name, env, f, t, N, tok, sc, zo, tr, o):
+    """One step of the 30-layer model against the oracle, teacher-forced:
+    every layer starts from the oracle's residual and runs the oracle's
+    experts, so each layer, the LM head and the sampler are compared on the
+    same inputs.  Checks: the embedding output (with the GPU's own
+    self-conditioning input when sc is given), every layer's output residual
+    and the router logits within the bar (or the fp32-twin criterion), the
+    logits within 2e-2 + 1e-2|z| (or the twin criterion), the device's own
+    entropies within 1e-3 nats, decisions equal up to margin-certified
+    near-ties."""
+    shape, W, oc, cv = f["shape"], f["W"], f["oc"], f["cv"]
+    xs = np.stack(tr["xs"])[:, 0]                       # [L + 1][C][d]
+    ids = np.stack(tr["expert_ids"])
+    z, rg, xg = _gpu_step(env, f, t, N, force=ids, teacher=xs)
+    # embedding output: E[tok] (exact) plus the self-conditioning term
+    emb = W.get("embed")[tok]
+    if sc is None:
+        assert np.array_equal(xg[0], emb.astype(np.float32)), f"{name}: embedding rows differ"
+    else:
+        def twin0():
+            with om.accumulation("f32"):
+                return om.embed(shape, W, tok[None], sc[None])[0] - emb
+        bar_then_twin(f"{name} self-conditioning term", xg[0] - emb, xs[0] - emb, twin0, ATOL, RTOL)
+        assert np.abs(xs[0] - emb).max() > 1e-3  # the term is not negligible
+    outside = 0
+    ro = np.stack(tr["router_logits"])
+    for l in range(shape.n_layers):
+        twin = {}
+
+        def layer_twin(l=l):
+            if not twin:
+                twin["x"], twin["r"] = _oracle_layer_twin(shape, W, oc, xs[l][None], l, ids[l])
+            return twin
+
+        outside += bar_then_twin(f"{name} layer {l} output", xg[l + 1], xs[l + 1], lambda: layer_twin()["x"][0],
+                                 ATOL, RTOL)
+        bar_then_twin(f"{name} layer {l} router logits", rg[l], ro[l], lambda: layer_twin()["r"], ROUTE_EPS["bf16"],
+                      0.0)
+        W.drop_layer(l)
+    say(f"{name}: per-layer outputs, {outside} elements outside the bar in all (twin criterion there)")
+
+    def twin_head():
+        with om.accumulation("f32"):
+            return om.final_logits(shape, W, xs[-1][None], f["wl"].lm_scale)[0]
+
+    bar_then_twin(f"{name} logits", z, zo[0], twin_head, ATOL, RTOL)
+    H = cv.entropy.cpu().numpy().astype(np.float64)
+    entropy_check(f"{name} device entropy", H, z, zo[0], o["H"], o["tau"])
+    compare_step_decisions(name, z, H, cv.argmax.cpu().numpy(), cv.accepted.cpu().numpy().astype(bool),
+                           cv.sample.cpu().numpy(), cv.tokens.cpu().numpy(), int(cv.stop.item()), dict(o, z=zo[0]))
+    return z
+
+
+def test_full30_step_matches_oracle(env, full30_rc):
+    """The 30-layer bf16 denoising step at its full size (256-token canvas,
+    4096-row cache, 262144-id vocabulary) against the oracle.
+
+    Over 30 layers two correct evaluations of the same definition drift
+    apart: every layer rounds four GEMM inputs to bf16, and an
+    accumulation-order difference that moves a value across a rounding
+    boundary becomes a whole-ulp difference, which later layers carry on; at
+    the last layer the oracle's own definition evaluated with fp32 products
+    and sums (the fp32 twin) is off the fp64 values by ~1% of the logits'
+    spread.  So the step is compared in two ways:
+
+    * teacher-forced (dg_test_denoise_step with the oracle's residuals and
+      experts): every layer, the LM head and the sampler on the same inputs,
+      held to the logit bar, 1e-3 nats and certified decisions; step t = 0,
+      then t = 1 of the same 12-step schedule, whose embedding output carries
+      the GPU's own bf16 self-conditioning input (its step-0 distribution,
+      normalised in place by its sampler) against the oracle's fp64 one;
+    * end to end on the oracle's routes: logits, router logits and the
+      device's entropies held to twice the fp32 twin's error distribution.
+
+    The sampler's decisions are bit-exact from the oracle's own logits; one
+    unforced step shows route flips only at oracle near-ties in layer 0."""
+    torch, dg, rt = env
+    f = full30_rc
+    shape, wl, cv, W, oc = f["shape"], f["wl"], f["cv"], f["W"], f["oc"]
+    C, V, N, s = wl.canvas, shape.vocab, wl.n_steps, wl.lm_scale
+    cfg, st = f["model"].cfg, rt.stream_handle()
+    dg.dg_init_canvas(cfg, cv.struct, 0, st)
+    cv.prev_argmax.fill_(-1)
+    torch.cuda.synchronize()
+    tok0 = cv.tokens.cpu().numpy()
+    assert np.array_equal(tok0, smp.initial_canvas(0, 0, C, V))
+    # ---- step 0
+    say("full30 step parity: oracle step 0 (30 layers, fp64)")
+    zo0, tr0 = _oracle_canvas_forward(shape, W, oc, tok0[None], None, s, keep_x=True)
+    o0 = smp.sample_from_logits(zo0[0], 0, N, 0, 0, None, False)
+    ids0 = np.stack(tr0["expert_ids"])
+    m0 = _route_margins(shape, tr0)
+    say(f"full30 step 0: oracle route margin min {m0.min():.2e}; accepted {o0['n_accepted']}")
+    _teacher_step_checks("full30 t=0 teacher-forced", env, f, 0, N, tok0, None, zo0, tr0, o0)
+    # the sampler from the oracle's own logits: decisions bit-exact
+    cv2 = rt.DeviceCanvas(shape, 1, C, [0])
+    d_z = torch.from_numpy(zo0[0].astype(np.float32)).cuda()
+    dg.dg_test_sample_from_logits(cfg, d_z.data_ptr(), cv2.struct, rt.step_params(0, N, 0, False), f["ws"].ptr,
+                                  f["ws"].size, st)
+    torch.cuda.synchronize()
+    o32 = smp.sample_from_logits(zo0[0].astype(np.float32).astype(np.float64), 0, N, 0, 0, None, False)
+    allclose_report("full30 t=0 sampler entropy (oracle logits)", cv2.entropy.cpu().numpy(), o32["H"], 1e-3, 0.0)
+    assert np.array_equal(cv2.argmax.cpu().numpy(), o32["argmax"])
+    compare_decisions("full30 t=0 sample (oracle logits)", cv2.sample.cpu().numpy(), o32["sample"],
+                      o32["margin_sample"], 1e-5)
+    compare_decisions("full30 t=0 accepted (oracle logits)", cv2.accepted.cpu().numpy().astype(bool),
+                      o32["accepted"], o32["margin_accept"], 1e-5)
+    nx = cv2.tokens.cpu().numpy()
+    ok = cv2.accepted.cpu().numpy().astype(bool) == o32["accepted"]
+    assert np.array_equal(nx[ok], o32["next_tokens"][ok])
+    del cv2, d_z
+    # ---- step 1: the GPU's carried self-conditioning (from its teacher-forced step 0) against the oracle's p
+    tok1 = o0["next_tokens"].astype(np.int32)
+    cv.tokens.copy_(torch.from_numpy(tok1))
+    torch.cuda.synchronize()
+    say("full30 step parity: oracle step 1 (self-conditioning from its step-0 distribution)")
+    zo1, tr1 = _oracle_canvas_forward(shape, W, oc, tok1[None], o0["p"][None], s, keep_x=True)
+    o1 = smp.sample_from_logits(zo1[0], 1, N, 0, 0, o0["argmax"], False)
+    _teacher_step_checks("full30 t=1 teacher-forced (carried self-conditioning)", env, f, 1, N, tok1, o0["p"], zo1,
+                         tr1, o1)
+    assert np.abs(zo1 - zo0).max() > 0.1  # step 1 differs from step 0 (new tokens, self-conditioning)
+    del tr1
+    # ---- end to end on the oracle's routes (step 0), against the fp32 twin's drift
+    dg.dg_init_canvas(cfg, cv.struct, 0, st)
+    z, rg, _ = _gpu_step(env, f, 0, N, force=ids0)
+    say("full30 end to end: fp32 twin forward (30 layers)")
+    zt, trt = _oracle_canvas_forward(shape, W, oc, tok0[None], None, s, ids0, "f32")
+    bar_or_twin("full30 t=0 end-to-end logits", z, zo0[0], zt[0], ATOL, RTOL)
+    bar_or_twin("full30 t=0 end-to-end router logits", rg, np.stack(tr0["router_logits"]),
+                np.stack(trt["router_logits"]), ROUTE_EPS["bf16"], 0.0)
+    Ht = smp.row_statistics(zt[0], o0["tau"])[1]
+    bar_or_twin("full30 t=0 end-to-end device entropy", cv.entropy.cpu().numpy(), o0["H"], Ht, 1e-3, 0.0)
+    # ---- unforced step 0: the product's own routing
+    dg.dg_init_canvas(cfg, cv.struct, 0, st)
+    zu, ru, _ = _gpu_step(env, f, 0, N)
+    k = shape.top_k
+    bound = flip_margin_bound(rg[0], np.stack(tr0["router_logits"])[0])
+    gtop = np.sort(np.argsort(-ru, axis=2, kind="stable")[:, :, :k], axis=2)
+    otop = np.sort(ids0, axis=2)
+    flips = np.any(gtop != otop, axis=2)  # [layer, token]
+    say(f"full30 unforced t=0: route flips per layer {flips.sum(axis=1).tolist()} (layer-0 bound {bound:.2e}); "
+        f"layer-0 flip margins {m0[0][flips[0]]}")
+    assert np.all(m0[0][flips[0]] < bound)  # layer 0 sees the same inputs: flips only at near-ties
+    f["cache"].struct.length = wl.prefix

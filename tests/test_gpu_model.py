@@ -14,7 +14,7 @@ from synth.configs import MINI_BF16, TINY, WORKLOADS
 # the small bf16 shape with fp8 expert and LM-head weights
 MINI_FP8 = replace(MINI_BF16, expert_dtype="fp8", lm_dtype="fp8")
 
-from .gpu_util import allclose_report, bar_or_twin, compare_decisions, say
+from .gpu_util import allclose_report, bar_or_twin, bar_then_twin, compare_decisions, compare_step_decisions, say
 
 pytestmark = pytest.mark.gpu
 
@@ -368,6 +368,91 @@ def test_denoise_loop_and_commit_match_oracle(which, request):
     pb.check_guards()
 
 
+@pytest.mark.parametrize("which", ["tiny", "mini", "mini8"])
+def test_forced_route_loop_matches_oracle(which, request):
+    """Every step of a 12-step schedule compared with the oracle on the
+    oracle's routes (dg_test_denoise_step: the product's whole step with
+    every layer's experts forced).  The GPU carries its own self-conditioning
+    input from step to step (the previous step's tempered distribution,
+    normalised in place by its sampler: bf16 for the bf16 models), while the
+    oracle uses its own fp64 distribution; each step's canvas tokens and
+    previous argmax are the oracle's, so a near-tie decision in one step does
+    not end the comparison.  Per step: logits within the bar (or the fp32-twin
+    criterion), the device's own entropies within the entropy bar, decisions
+    equal up to margin-certified near-ties."""
+    pb = request.getfixturevalue(which)
+    torch, dg, rt = pb.env
+    shape, B, C, V = pb.shape, pb.B, pb.C, pb.shape.vocab
+    N = 12
+    say(f"forced-route loop {which}")
+    dg.dg_init_canvas(pb.cfg, pb.canvas.struct, 0, pb.st)
+    pb.canvas.prev_argmax.fill_(-1)
+    torch.cuda.synchronize()
+    otok = np.stack([smp.initial_canvas(s, 0, C, V) for s in pb.seeds])
+    assert np.array_equal(pb.canvas.tokens.cpu().numpy().reshape(B, C), otok)
+    oprev, osc = None, None
+    worst_dz, worst_dh, ties = 0.0, 0.0, 0
+    out = torch.empty(B * C * V, dtype=torch.float32, device="cuda")
+    for t in range(N):
+        tr = {}
+        zo, outs = ost.denoise_step(shape, pb.W, pb.ocache, otok, osc, t, N, pb.seeds, 0, pb.lm_scale, oprev, True,
+                                    trace=tr)
+        pb.canvas.tokens.copy_(torch.from_numpy(np.ascontiguousarray(otok, dtype=np.int32).reshape(-1)))
+        if oprev is not None:
+            pb.canvas.prev_argmax.copy_(torch.from_numpy(np.ascontiguousarray(oprev, dtype=np.int32).reshape(-1)))
+        d_force = torch.from_numpy(np.ascontiguousarray(_forced_ids(tr), dtype=np.int32).reshape(-1)).cuda()
+        dg.dg_test_denoise_step(pb.cfg, pb.model.weights, pb.cache.struct, pb.canvas.struct,
+                                rt.step_params(t, N, block=0, adaptive=True), d_force.data_ptr(), None,
+                                out.data_ptr(), pb.ws.ptr, pb.ws.size, pb.st)
+        torch.cuda.synchronize()
+        z = out.cpu().numpy().reshape(B, C, V)
+        H = pb.canvas.entropy.cpu().numpy().reshape(B, C).astype(np.float64)
+        am = pb.canvas.argmax.cpu().numpy().reshape(B, C)
+        acc = pb.canvas.accepted.cpu().numpy().reshape(B, C).astype(bool)
+        samp = pb.canvas.sample.cpu().numpy().reshape(B, C)
+        nxt = pb.canvas.tokens.cpu().numpy().reshape(B, C)
+        stop = pb.canvas.stop.cpu().numpy()
+
+        def twin():
+            with om.accumulation("f32"):
+                return _f32_twin_on_inputs(pb, otok, osc, tr["expert_ids"])
+
+        bar_then_twin(f"loop {which} t{t} logits", z, zo, twin, pb.atol, RTOL)
+        for b, o in enumerate(outs):
+            tol = entropy_tolerance(zo[b], o["tau"], pb.atol)
+            allclose_report(f"loop {which} t{t} b{b} device entropy", H[b], o["H"], tol, 0.0)
+            ties += compare_step_decisions(f"loop {which} t{t} b{b}", z[b], H[b], am[b], acc[b], samp[b], nxt[b],
+                                           stop[b], dict(o, z=zo[b]))
+        worst_dz = max(worst_dz, float(np.abs(z - zo).max()))
+        worst_dh = max(worst_dh, float(np.abs(H - np.stack([o["H"] for o in outs])).max()))
+        oprev = np.stack([o["argmax"] for o in outs])
+        otok = np.stack([o["next_tokens"] for o in outs])
+        osc = np.stack([o["p"] for o in outs])
+    say(f"forced-route loop {which}: {N} steps compared; max |dz| {worst_dz:.2e}, max |dH| {worst_dh:.2e}, "
+        f"near-tie decisions {ties}")
+    pb.check_guards()
+
+
+def _f32_twin_on_inputs(pb, tok, sc, expert_ids):
+    """The oracle's logits on the given canvas and self-conditioning input,
+    every layer's experts fixed to expert_ids (used inside an accumulation
+    context)."""
+    ids = list(expert_ids)
+    orig = om.route
+
+    def fixed(shape_, r):
+        sel = ids.pop(0)
+        s_ = np.take_along_axis(r, sel, axis=1)
+        e = np.exp(s_ - s_.max(axis=1, keepdims=True))
+        return sel, e / e.sum(axis=1, keepdims=True)
+
+    om.route = fixed
+    try:
+        return ost.denoise_logits(pb.shape, pb.W, pb.ocache, tok, sc, pb.lm_scale)
+    finally:
+        om.route = orig
+
+
 @pytest.mark.parametrize("which", ["mini", "mini8"])
 def test_skewed_routing_matches_oracle(which, request):
     """Every token of every layer routed to the same k experts (in one order):
@@ -576,6 +661,78 @@ def _f32_twin_on_routes(pb, tok, expert_ids):
     finally:
         om.route = orig
     return zt, trt
+
+
+def test_long_prefill_matches_oracle(env):
+    """Prompt encoding at length: a 4096-token prompt through a 3-layer bf16
+    model in one causal pass (the attention splits the keys and merges the
+    splits; every later layer's K/V rows depend on the earlier layers' causal
+    attention over up to 4096 keys).  With the oracle's routes forced, every
+    K/V row of every layer is compared with the oracle's causal encode (the
+    bar, or the fp32-twin criterion); the product encode (its own routing) is
+    compared below the first oracle route near-tie of the layers before."""
+    torch, dg, rt = env
+    shape = replace(MINI_BF16, n_layers=3)
+    n = 4096
+    pb = Problem(env, shape, 6.0, n, 8, B=1, cap_extra=-8)
+    assert pb.cap == n
+    say(f"long prefill: oracle encode of {n} tokens, {shape.n_layers} layers")
+    tr = {}
+    ost.encode_append(shape, pb.W, pb.ocache, pb.prompt, trace=tr)
+    ids = np.stack(tr["expert_ids"])  # [layers][n][k]
+    margins = _route_margins(shape, tr)
+    d_tok = torch.from_numpy(pb.prompt.astype(np.int32).reshape(-1)).cuda()
+    d_force = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32).reshape(-1)).cuda()
+    say("long prefill: GPU encode on the oracle's routes")
+    dg.dg_test_encode_append(pb.cfg, pb.model.weights, pb.cache.struct, d_tok.data_ptr(), 1, n, d_force.data_ptr(),
+                             None, pb.ws.ptr, pb.ws.size, pb.st)
+    torch.cuda.synchronize()
+    assert pb.cache.length == n
+    twin = {}
+
+    def twin_cache():
+        if not twin:
+            say("long prefill: fp32 twin encode on the oracle's routes")
+            tc = om.KVCache(shape, 1, n)
+            left = list(ids)
+            orig = om.route
+
+            def fixed(shape_, r):
+                sel = left.pop(0)
+                s_ = np.take_along_axis(r, sel, axis=1)
+                e = np.exp(s_ - s_.max(axis=1, keepdims=True))
+                return sel, e / e.sum(axis=1, keepdims=True)
+
+            om.route = fixed
+            try:
+                with om.accumulation("f32"):
+                    ost.encode_append(shape, pb.W, tc, pb.prompt)
+            finally:
+                om.route = orig
+            twin["c"] = tc
+        return twin["c"]
+
+    gk, gv = pb.cache.view("k").float().cpu().numpy(), pb.cache.view("v").float().cpu().numpy()
+    for l in range(shape.n_layers):
+        bar_then_twin(f"long prefill forced k L{l}", gk[l], pb.ocache.k[l], lambda: twin_cache().k[l], pb.atol, RTOL)
+        bar_then_twin(f"long prefill forced v L{l}", gv[l], pb.ocache.v[l], lambda: twin_cache().v[l], pb.atol, RTOL)
+    # the product encode, own routing: rows below the first near-tie of any earlier layer
+    pc = rt.DeviceCache(shape, 1, n)
+    dg.dg_encode_append(pb.cfg, pb.model.weights, pc.struct, d_tok.data_ptr(), 1, n, pb.ws.ptr, pb.ws.size, pb.st)
+    torch.cuda.synchronize()
+    pk, pv = pc.view("k").float().cpu().numpy(), pc.view("v").float().cpu().numpy()
+    rows = n
+    for l in range(shape.n_layers):
+        if rows == 0:
+            break
+        bar_then_twin(f"long prefill product k L{l} rows<{rows}", pk[l][:, :, :rows], pb.ocache.k[l][:, :, :rows],
+                      lambda: twin_cache().k[l][:, :, :rows], pb.atol, RTOL)
+        bar_then_twin(f"long prefill product v L{l} rows<{rows}", pv[l][:, :, :rows], pb.ocache.v[l][:, :, :rows],
+                      lambda: twin_cache().v[l][:, :, :rows], pb.atol, RTOL)
+        ties = np.nonzero(margins[l] < ROUTE_EPS["bf16"])[0]
+        rows = min(rows, int(ties[0]) if ties.size else n)
+    say(f"long prefill: product encode compared below row {rows} after the last layer")
+    pb.check_guards()
 
 
 @pytest.mark.parametrize("B", [24, 48])
