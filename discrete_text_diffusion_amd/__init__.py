@@ -29,6 +29,8 @@ DG_ERR_UNSUPPORTED = -2
 DG_ERR_KV_CAPACITY = -3
 DG_ERR_WORKSPACE = -4
 DG_ERR_HIP = -5
+DG_ERR_SCRATCH_LIMIT = -6
+DG_NOALLOC_SCRATCH_BYTES = 320 << 20
 DG_DTYPE_F32 = 0
 DG_DTYPE_BF16 = 1
 DG_DTYPE_FP8_E4M3 = 2
@@ -124,6 +126,8 @@ _t_route = _sig("dg_test_route_from_logits", c_int32, _P(ModelConfig), c_void_p,
 _t_logits = _sig("dg_test_forward_logits", c_int32, _P(ModelConfig), _P(Weights), _P(KVCache), _P(Canvas),
                  _P(StepParams), c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p)
 
+_noalloc = _sig("dg_denoise_step_noalloc", c_int32, _P(ModelConfig), _P(Weights), _P(KVCache), _P(Canvas),
+                _P(StepParams), c_void_p)
 _t_step = _sig("dg_test_denoise_step", c_int32, _P(ModelConfig), _P(Weights), _P(KVCache), _P(Canvas),
                _P(StepParams), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p)
 _t_encode = _sig("dg_test_encode_append", c_int32, _P(ModelConfig), _P(Weights), _P(KVCache), c_void_p, c_int32,
@@ -136,7 +140,7 @@ EXPORTED = ("dg_temperature", "dg_workspace_bytes", "dg_pack_weight_bf16", "dg_p
             "dg_init_canvas", "dg_encode_append", "dg_denoise_step", "dg_commit_block", "dg_status_string",
             "dg_test_sample_from_logits", "dg_test_route_from_logits", "dg_test_forward_logits",
             "dg_denoise_step_traced", "dg_encode_append_traced", "dg_test_encode_append", "dg_ar_step", "dg_commit_and_step",
-            "dg_test_ar_step", "dg_test_denoise_step")
+            "dg_test_ar_step", "dg_test_denoise_step", "dg_denoise_step_noalloc")
 
 
 def _check(rc: int, where: str):
@@ -180,6 +184,11 @@ def dg_encode_append(cfg, weights, cache, d_tokens, batch: int, n_tokens: int, w
 def dg_denoise_step(cfg, weights, cache, canvas, params, ws, ws_bytes: int, stream) -> None:
     _check(_denoise(ctypes.byref(cfg), ctypes.byref(weights), ctypes.byref(cache), ctypes.byref(canvas),
                     ctypes.byref(params), ws, ws_bytes, stream), "dg_denoise_step")
+
+
+def dg_denoise_step_noalloc(cfg, weights, cache, canvas, params, stream) -> None:
+    _check(_noalloc(ctypes.byref(cfg), ctypes.byref(weights), ctypes.byref(cache), ctypes.byref(canvas),
+                    ctypes.byref(params), stream), "dg_denoise_step_noalloc")
 
 
 def dg_commit_block(cfg, weights, cache, canvas, params, ws, ws_bytes: int, stream) -> None:

@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/dg.h"
 #include "dg_internal.h"
@@ -845,6 +846,51 @@ int dg_denoise_step_traced(const dg_model_config* cfg, const dg_weights* w, cons
   return denoise_impl(cfg, w, cache, cv, p, d_ws, ws_bytes, stream, trace, nullptr, nullptr, nullptr);
 }
 
+}  // extern "C"
+
+// Scratch of dg_denoise_step_noalloc: a module global, so every GPU the
+// library runs on holds its own copy, allocated when the code object loads
+// there and kept until the process ends.  Host code never uses the array's
+// name as an address (on the host it is only a stand-in for the symbol): the
+// device address comes from hipGetSymbolAddress, taken once per device with
+// that device current, and kept in noalloc_ptr[device].
+static __device__ __align__(256) unsigned char scratch[DG_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex noalloc_mu;
+void* noalloc_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (looked up on the first call there).
+int noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DG_ERR_HIP;
+  std::lock_guard<std::mutex> lock(noalloc_mu);
+  if (!noalloc_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return DG_ERR_HIP;
+    noalloc_ptr[dev] = ptr;
+  }
+  *out = noalloc_ptr[dev];
+  return DG_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int dg_denoise_step_noalloc(const dg_model_config* cfg, const dg_weights* w, const dg_kv_cache* cache,
+                            dg_canvas* cv, const dg_step_params* p, void* stream) {
+  DG_TRY(check_config(cfg));
+  DG_TRY(check_canvas(cv, true));
+  // the step-only plan of this call must fit the static scratch
+  if (make_plan(shape_of(cfg), cv->batch, cv->canvas, true).total > (size_t)DG_NOALLOC_SCRATCH_BYTES)
+    return DG_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  DG_TRY(noalloc_scratch(&ws));
+  return denoise_impl(cfg, w, cache, cv, p, ws, (size_t)DG_NOALLOC_SCRATCH_BYTES, stream, nullptr, nullptr, nullptr,
+                      nullptr, true);
+}
+
 int dg_test_denoise_step(const dg_model_config* cfg, const dg_weights* w, const dg_kv_cache* cache, dg_canvas* cv,
                          const dg_step_params* p, const int32_t* d_force_ids, float* d_router_logits, float* d_logits,
                          const float* d_teacher_x, float* d_layer_out, void* d_ws, size_t ws_bytes, void* stream) {
@@ -963,6 +1009,7 @@ const char* dg_status_string(int status) {
     case DG_ERR_KV_CAPACITY: return "KV cache capacity exceeded";
     case DG_ERR_WORKSPACE: return "workspace too small";
     case DG_ERR_HIP: return "HIP launch error";
+    case DG_ERR_SCRATCH_LIMIT: return "step needs more than the no-allocation scratch (DG_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

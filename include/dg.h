@@ -45,6 +45,7 @@ extern "C" {
 #define DG_ERR_KV_CAPACITY (-3)
 #define DG_ERR_WORKSPACE (-4)
 #define DG_ERR_HIP (-5)
+#define DG_ERR_SCRATCH_LIMIT (-6) /* dg_denoise_step_noalloc: the step needs more scratch than it holds */
 
 #define DG_DTYPE_F32 0
 #define DG_DTYPE_BF16 1
@@ -278,6 +279,26 @@ int dg_commit_and_step(const dg_model_config* cfg, const dg_weights* w, dg_kv_ca
 int dg_ar_step(const dg_model_config* cfg, const dg_weights* w, dg_kv_cache* cache,
                const int32_t* d_tokens, int32_t batch, int32_t* d_next, void* d_ws,
                size_t ws_bytes, void* stream);
+
+/* dg_denoise_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same inputs, outputs, launches and
+ * results as dg_denoise_step with a caller workspace; calls no hipMalloc,
+ * hipFree or allocating library routine.  Its scratch is a static device
+ * array of DG_NOALLOC_SCRATCH_BYTES (320 MiB) in the library, one per GPU the
+ * library runs on, held until the process ends; the call uses the current
+ * device's (the stream's device must be the current device).  It holds one
+ * step of batch * canvas <= 256 tokens at the pages' full width (d_model
+ * 2816, 16/8 heads of 256, 128 experts top-8 + shared, vocab 262144); a step
+ * needing more returns DG_ERR_SCRATCH_LIMIT before anything is enqueued.
+ * Nothing in the scratch needs to start at zero; every call on one GPU
+ * shares its array and leaves its contents, so calls whose work overlaps on
+ * one GPU (other streams or threads, before the previous call's work has
+ * finished) race: serialise them on one stream.  Other errors as
+ * dg_denoise_step. */
+#define DG_NOALLOC_SCRATCH_BYTES (320u << 20)
+int dg_denoise_step_noalloc(const dg_model_config* cfg, const dg_weights* w, const dg_kv_cache* cache,
+                            dg_canvas* canvas, const dg_step_params* p, void* stream);
 
 const char* dg_status_string(int status);
 

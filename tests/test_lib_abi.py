@@ -123,3 +123,24 @@ def test_new_entry_points_check_arguments_on_the_host(dg):
     w2, cache2, cv2, _ = _fake_structs(dg, TINY, 17, 1024, 1024, 0)
     assert status(dg.dg_denoise_step, cfg, w2, cache2, cv2, step(0, 12, 0), fake, big,
                   None) == dg.DG_ERR_UNSUPPORTED
+
+
+def test_noalloc_step_limit_is_checked_on_the_host(dg):
+    """dg_denoise_step_noalloc refuses a step whose scratch exceeds its static
+    array before touching the GPU: two 256-token canvases at the pages' full
+    width need about 560 MiB of the 320 MiB it holds; a malformed call is an
+    argument error first."""
+    from synth.configs import FULL_LAYER
+    from discrete_text_diffusion_amd.runtime import model_config
+    cfg = model_config(FULL_LAYER)
+    step = dg.StepParams(0, 12, 0, 1, 0.1, 0.005)
+    w, cache, cv, fake = _fake_structs(dg, FULL_LAYER, 2, 256, 2048 + 256, 2048)
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_denoise_step_noalloc(cfg, w, cache, cv, step, None)
+    assert e.value.status == dg.DG_ERR_SCRATCH_LIMIT
+    assert "no-allocation scratch" in dg.dg_status_string(dg.DG_ERR_SCRATCH_LIMIT)
+    bad = dg.Canvas(0, 256, fake, fake, None, None, None, *([fake] * 9), fake)
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_denoise_step_noalloc(cfg, w, cache, bad, step, None)
+    assert e.value.status == dg.DG_ERR_INVALID_ARG
+    assert dg.DG_NOALLOC_SCRATCH_BYTES == 320 << 20
