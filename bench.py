@@ -305,7 +305,9 @@ def profile_summary(trace_dir, bench_json, out, command):
     b = json.loads(open(bench_json).read().strip().splitlines()[-1])
     stats = {}
     for _, name, ns in rows:
-        short = name.split("(")[0].replace("(anonymous namespace)::", "")
+        short = name.replace("(anonymous namespace)::", "")
+        short = short[5:] if short.startswith("void ") else short
+        short = short.split("(")[0]
         st = stats.setdefault(short, [0, 0.0, float("inf"), 0.0])
         st[0] += 1
         st[1] += ns

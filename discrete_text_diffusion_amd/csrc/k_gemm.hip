@@ -41,13 +41,12 @@ __device__ __forceinline__ void decode_block(const GemmArgs& a, int lb, int ntil
   const int per_split = ntiles * a.n_fb;
   ks = lb / per_split;
   const int r = lb - ks * per_split;
-  if (a.tile_fastest) {
-    tile = r % ntiles;
-    fb = r / ntiles;
-  } else {
-    fb = r % a.n_fb;
-    tile = r / a.n_fb;
-  }
+  // (selects of values: a select between the two references made the
+  // compiler round-trip them through scratch memory)
+  const int fast = a.tile_fastest ? ntiles : a.n_fb;
+  const int lo = r % fast, hi = r / fast;
+  tile = a.tile_fastest ? lo : hi;
+  fb = a.tile_fastest ? hi : lo;
 }
 
 // The workgroup's (tile, feature block, split), or false if it has none.
@@ -555,6 +554,7 @@ __device__ __forceinline__ void tile_stats4(const float* z0, int64_t pitch, int 
       if (ex[k] > 0.f) lastc = max(lastc, 64 * (k >> 2) + 4 * sl + (k & 3));
     cand = row16_max(lastc);
   }
+  if (cand < 0) cand = bc;  // no id with mass at all (non-finite logits): the argmax, still a valid id
   if (r >= nrows) return;
   const int row = row0 + r;
   const int64_t col = (int64_t)vt * 256;
