@@ -532,6 +532,148 @@ def cpu_baseline(wl, target_s: float):
     }
 
 
+def longctx_run(workload: str = "longctx"):
+    """Long-context generation on the one-layer full-width model: the
+    32768-token prompt encoded, then 8 consecutive 256-token canvases of up to
+    48 steps with the adaptive stop on (the host reads the stop flag after each
+    step), each committed by a causal encode-and-append.  Every step and
+    commit is bracketed by HIP events on the stream, so the per-step times
+    exclude the host's reads between steps; one JSON line with the step time
+    against the cache length."""
+    import torch
+    from discrete_text_diffusion_amd import runtime as rt
+    import discrete_text_diffusion_amd as dg
+    import synth
+    from synth.configs import WORKLOADS
+    wl = WORKLOADS[workload]
+    shape, C = wl.model, wl.canvas
+    st = rt.stream_handle()
+    print(f"[longctx] building {workload}", file=sys.stderr, flush=True)
+    model = rt.DeviceModel(shape, wl.lm_scale)
+    cfg = model.cfg
+    cache = rt.DeviceCache(shape, 1, wl.prefix + wl.n_blocks * C)
+    ws = rt.Workspace(cfg, 1, C)
+    prompt = torch.empty(wl.prefix, dtype=torch.int32, device="cuda")
+    synth.dev_tokens(prompt.data_ptr(), wl.prefix, wl.prompt_seed, synth.TID["prompt"], shape.vocab, st)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    e0, e1 = ev(), ev()
+    e0.record()
+    dg.dg_encode_append(cfg, model.weights, cache.struct, prompt.data_ptr(), 1, wl.prefix, ws.ptr, ws.size, st)
+    e1.record()
+    torch.cuda.synchronize()
+    prefill_ms = e0.elapsed_time(e1)
+    print(f"[longctx] prefill {wl.prefix} tokens: {prefill_ms:.1f} ms", file=sys.stderr, flush=True)
+    cv = rt.DeviceCanvas(shape, 1, C, [5])
+    dg.dg_init_canvas(cfg, cv.struct, 0, st)
+    blocks, t0 = [], time.time()
+    gpu_ms = 0.0
+    for block in range(wl.n_blocks):
+        L = cache.length
+        cv.prev_argmax.fill_(-1)
+        pairs = []
+        t_used = 0
+        for t in range(wl.n_steps):
+            a, b = ev(), ev()
+            a.record()
+            dg.dg_denoise_step(cfg, model.weights, cache.struct, cv.struct,
+                               rt.step_params(t, wl.n_steps, block, wl.adaptive), ws.ptr, ws.size, st)
+            b.record()
+            pairs.append((a, b))
+            t_used = t + 1
+            if int(cv.stop.item()):
+                break
+        a, b = ev(), ev()
+        a.record()
+        dg.dg_commit_block(cfg, model.weights, cache.struct, cv.struct,
+                           rt.step_params(t_used - 1, wl.n_steps, block), ws.ptr, ws.size, st)
+        b.record()
+        torch.cuda.synchronize()
+        step_ms = [x.elapsed_time(y) for x, y in pairs]
+        commit_ms = a.elapsed_time(b)
+        gpu_ms += sum(step_ms) + commit_ms
+        blocks.append({"block": block, "cache_rows": L, "steps": t_used,
+                       "step_ms_mean": round(sum(step_ms) / len(step_ms), 4),
+                       "step_ms_min": round(min(step_ms), 4), "commit_ms": round(commit_ms, 3),
+                       "last_mean_entropy": round(float(cv.mean_entropy.item()), 5)})
+        print(f"[longctx] block {block}: cache {L}, {t_used} steps of {blocks[-1]['step_ms_mean']:.3f} ms",
+              file=sys.stderr, flush=True)
+    wall_s = time.time() - t0
+    tokens = wl.n_blocks * C
+    first, last = blocks[0], blocks[-1]
+    print(json.dumps({
+        "workload": workload, "layers": shape.n_layers, "dtype": shape.dtype, "prefix": wl.prefix,
+        "canvases": wl.n_blocks, "max_steps": wl.n_steps, "adaptive": wl.adaptive,
+        "prefill_ms": round(prefill_ms, 2), "final_cache_rows": cache.length,
+        "canvas_tok_s_gpu": round(tokens / (gpu_ms * 1e-3), 1),
+        "canvas_tok_s_gpu_definition": "canvases x 256 tokens / the summed event times of every step and commit",
+        "canvas_tok_s_wall": round(tokens / wall_s, 1),
+        "canvas_tok_s_wall_definition": "the same tokens / host wall time of the loop, with a host read of the "
+                                        "stop flag after each step",
+        "step_ms_first_block": first["step_ms_mean"], "step_ms_last_block": last["step_ms_mean"],
+        "kv_bytes_per_step_first_block": 2 * (first["cache_rows"] + C) * shape.n_kv_heads * shape.d_head * 2 *
+        shape.n_layers,
+        "blocks": blocks, "data": "synthetic (seeded random-init weights, uniform prompt tokens)"}))
+
+
+def fp8batch_run(workload: str = "fp8batch4", reps: int = 3):
+    """The fp8 batch-4 workload: four independent canvases, each over its own
+    8192-row prefix (seeded N(0,1) cache rows: the step's work depends on the
+    cache values only through the routing they lead to), sampler seeds 0..3,
+    12 steps from fresh noise with the self-conditioning input carried from
+    step to step, timed with events around the 12 steps (no host work
+    between); the median of `reps` runs after one untimed run, then one traced
+    step for the phases.  One JSON line: aggregate canvas tok/s of the four."""
+    import torch
+    from discrete_text_diffusion_amd import runtime as rt
+    import discrete_text_diffusion_amd as dg
+    from synth.configs import WORKLOADS
+    wl = WORKLOADS[workload]
+    shape, B, C, N = wl.model, wl.batch, wl.canvas, wl.n_steps
+    st = rt.stream_handle()
+    hip = _hip()
+    print(f"[fp8batch] building {workload}", file=sys.stderr, flush=True)
+    model = rt.DeviceModel(shape, wl.lm_scale)
+    cfg = model.cfg
+    cache = rt.DeviceCache(shape, B, wl.prefix + C)
+    cache.fill_random(wl.prefix)
+    cache.struct.length = wl.prefix
+    cv = rt.DeviceCanvas(shape, B, C, list(wl.sampler_seeds)[:B])
+    ws = rt.Workspace(cfg, B, C)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    runs, acc = [], []
+    for rep in range(reps + 1):
+        dg.dg_init_canvas(cfg, cv.struct, 0, st)
+        cv.prev_argmax.fill_(-1)
+        e0.record()
+        for t in range(N):
+            dg.dg_denoise_step(cfg, model.weights, cache.struct, cv.struct, rt.step_params(t, N, 0, False),
+                               ws.ptr, ws.size, st)
+        e1.record()
+        torch.cuda.synchronize()
+        if rep:
+            runs.append(e0.elapsed_time(e1))
+            acc.append(cv.n_accepted.cpu().tolist())
+    ms12 = sorted(runs)[len(runs) // 2]
+    pool = EventPool(hip, 2 * (shape.n_layers * 8 + 8))
+    tr = pool.trace(dg, (1 << len(dg.PHASES)) - 1)
+    dg.dg_denoise_step_traced(cfg, model.weights, cache.struct, cv.struct, rt.step_params(1, N, 0, False), ws.ptr,
+                              ws.size, st, tr)
+    torch.cuda.synchronize()
+    phases = {}
+    for ph, pms in pool.durations(tr):
+        phases[dg.PHASES[ph]] = phases.get(dg.PHASES[ph], 0.0) + pms
+    print(json.dumps({
+        "workload": workload, "layers": shape.n_layers, "weights": "fp8 e4m3 experts (shared included) and LM head, "
+        "per-output-channel fp32 scales; bf16 activations", "batch": B, "canvas": C, "prefix": wl.prefix,
+        "denoise_steps": N, "canvas_ms_12_steps": round(ms12, 3), "runs_ms": [round(x, 3) for x in runs],
+        "denoise_step_ms": round(ms12 / N, 4),
+        "canvas_tok_s_12_steps_aggregate": round(B * C / (ms12 * 1e-3), 1),
+        "canvas_tok_s_12_steps_per_canvas": round(C / (ms12 * 1e-3), 1),
+        "tokens_per_expert_mean": B * C * shape.top_k / shape.n_experts,
+        "accepted_last_step": acc[-1], "phase_ms_one_step": {k: round(v, 4) for k, v in phases.items()},
+        "data": "synthetic (seeded random-init weights, seeded N(0,1) prefix cache)"}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -552,7 +694,17 @@ def main():
     ap.add_argument("--ar-profile", type=int, metavar="N", help="N single-token decode steps only (kernel profiles)")
     ap.add_argument("--sweep", metavar="B,B,...", help="denoising-step time at these canvas counts (own JSON line)")
     ap.add_argument("--prefill", metavar="N,N,...", help="prompt encoding time at these lengths (own JSON line)")
+    ap.add_argument("--longctx", action="store_true",
+                    help="32768-token prompt, 8 committed canvases on the one-layer model (own JSON line)")
+    ap.add_argument("--fp8batch", action="store_true",
+                    help="fp8 one-layer model, 4 canvases over 8192-row prefixes, 12 steps (own JSON line)")
     args = ap.parse_args()
+    if args.longctx:
+        longctx_run()
+        return
+    if args.fp8batch:
+        fp8batch_run()
+        return
     if args.prefill:
         prefill_run(args.workload, [int(n) for n in args.prefill.split(",")])
         return
