@@ -29,7 +29,8 @@ added to the token embedding; untied LM head multiplied by the workload's
 LM-head scale.
 
 Storage/rounding contract (bf16 models): weights as stored (fp8 weights:
-E4M3 code times its output row's fp32 scale, exact in float64); residual stream
+E4M3 code times its output row's fp32 scale; MXFP4 weights: E2M1 code times
+the E8M0 scale of its block of 32 inputs; both exact in float64); residual stream
 fp32 on the GPU (fp64 here); GEMM inputs (norm outputs, attention output,
 GeGLU hidden, expected embedding, self-cond hidden, self-cond probabilities)
 rounded to bf16; q/k/v rounded to bf16 after RoPE (k, v are the cache
@@ -44,7 +45,7 @@ import numpy as np
 import synth
 from synth.configs import ModelShape
 
-from .numerics import e4m3_decode, gelu_tanh, rmsnorm, rope, round_bf16
+from .numerics import e4m3_decode, gelu_tanh, mxfp4_dequantize, rmsnorm, rope, round_bf16
 
 
 class Weights:
@@ -87,6 +88,14 @@ class Weights:
             rows = int(np.prod(shp[:-1]))
             codes, sc = synth.e4m3_rows(self.shape.weight_seed, tid, rows, shp[-1], self.shape.weight_std)
             w = (e4m3_decode(codes) * sc.astype(np.float64)[:, None]).reshape(shp)
+            if self._cache is not None:
+                self._cache[key] = w
+            return w
+        if dt == "mxfp4":
+            # stored E2M1 codes and an E8M0 scale per 32 inputs, dequantised exactly
+            rows = int(np.prod(shp[:-1]))
+            codes, sc = synth.mxfp4_rows(self.shape.weight_seed, tid, rows, shp[-1], self.shape.weight_std)
+            w = mxfp4_dequantize(codes, sc).reshape(shp)
             if self._cache is not None:
                 self._cache[key] = w
             return w

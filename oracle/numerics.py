@@ -102,3 +102,41 @@ _E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
 def e4m3_decode(codes) -> np.ndarray:
     """float64 values of an array of E4M3 codes (the 256 values of e4m3_value)."""
     return _E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def e2m1_value(code: int) -> float:
+    """Value of one FP4 E2M1 element code (OCP Microscaling Formats v1.0, the
+    FP4 element type): sign bit, 2 exponent bits with bias 1, 1 mantissa bit;
+    exponent field 0 holds the subnormal m/2; no infinities or NaN."""
+    sign = -1.0 if code & 0x8 else 1.0
+    e, m = (code >> 1) & 0x3, code & 0x1
+    if e == 0:
+        return sign * (m / 2.0)
+    return sign * (1.0 + m / 2.0) * 2.0 ** (e - 1)
+
+
+_E2M1_TABLE = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """float64 values of an array of E2M1 codes (one code per byte, 0..15)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    if np.any(c > 15):
+        raise ValueError("E2M1 codes are 4-bit")
+    return _E2M1_TABLE[c]
+
+
+def e8m0_decode(codes) -> np.ndarray:
+    """float64 values of E8M0 scale codes (OCP Microscaling Formats v1.0, the
+    shared scale): 2^(code - 127), code 255 is NaN."""
+    c = np.asarray(codes, dtype=np.int64)
+    v = np.ldexp(1.0, c - 127)
+    return np.where(c == 255, np.nan, v)
+
+
+def mxfp4_dequantize(codes, scales) -> np.ndarray:
+    """The values of an MXFP4 tensor [rows][cols]: element code (r, c) times
+    the scale of its block of 32, (r, c / 32), exactly in float64."""
+    codes = np.asarray(codes)
+    sc = e8m0_decode(scales)
+    return e2m1_decode(codes) * np.repeat(sc, 32, axis=-1)

@@ -69,6 +69,8 @@ def _get_lib():
         lib.synth_tokens.argtypes = [u64, u64, u64, u64, ctypes.c_uint32, vp]
         lib.synth_dirichlet_rows.argtypes = [u64, u64, i64, i64, ctypes.c_double, vp]
         lib.synth_e4m3_rows.argtypes = [u64, u64, i64, i64, f32, vp, vp]
+        lib.synth_mxfp4_quantize.argtypes = [vp, i64, i64, vp, vp]
+        lib.synth_mxfp4_rows.argtypes = [u64, u64, i64, i64, f32, vp, vp]
         _lib = lib
     return _lib
 
@@ -119,6 +121,31 @@ def e4m3_rows(seed: int, tensor: int, rows: int, cols: int, std: float):
     sc = np.empty(rows, dtype=np.float32)
     _get_lib().synth_e4m3_rows(seed, tensor, rows, cols, ctypes.c_float(scale_for_std(std)), codes.ctypes.data,
                                sc.ctypes.data)
+    return codes, sc
+
+
+def mxfp4_quantize(w: np.ndarray):
+    """MXFP4 form of the float32 values w [rows][cols] (cols % 32 == 0), by
+    blocks of 32 consecutive values of a row: (element codes uint8
+    [rows][cols], one E2M1 code per byte; E8M0 scale codes uint8
+    [rows][cols / 32]).  The recipe is stated in gen.c."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rows, cols = w.shape
+    if cols % 32:
+        raise ValueError("cols must be a multiple of 32")
+    codes = np.empty((rows, cols), dtype=np.uint8)
+    sc = np.empty((rows, cols // 32), dtype=np.uint8)
+    _get_lib().synth_mxfp4_quantize(w.ctypes.data, rows, cols, codes.ctypes.data, sc.ctypes.data)
+    return codes, sc
+
+
+def mxfp4_rows(seed: int, tensor: int, rows: int, cols: int, std: float):
+    """MXFP4 form of the bf16 normal tensor [rows][cols]: (codes uint8
+    [rows][cols], scale codes uint8 [rows][cols / 32])."""
+    codes = np.empty((rows, cols), dtype=np.uint8)
+    sc = np.empty((rows, cols // 32), dtype=np.uint8)
+    _get_lib().synth_mxfp4_rows(seed, tensor, rows, cols, ctypes.c_float(scale_for_std(std)), codes.ctypes.data,
+                                sc.ctypes.data)
     return codes, sc
 
 
@@ -188,8 +215,9 @@ def _get_dev_lib():
         lib.synth_dev_tokens.argtypes = [vp, u64, u64, u64, u64, ctypes.c_uint32, vp]
         lib.synth_dev_normal_f32_transposed.argtypes = [vp, u64, u64, u64, u64, ctypes.c_float, vp]
         lib.synth_dev_e4m3_rows.argtypes = [vp, vp, u64, u64, u64, u64, ctypes.c_float, vp]
+        lib.synth_dev_mxfp4_rows.argtypes = [vp, vp, u64, u64, u64, u64, ctypes.c_float, vp]
         for f in (lib.synth_dev_normal_bf16, lib.synth_dev_normal_f32, lib.synth_dev_tokens,
-                  lib.synth_dev_normal_f32_transposed, lib.synth_dev_e4m3_rows):
+                  lib.synth_dev_normal_f32_transposed, lib.synth_dev_e4m3_rows, lib.synth_dev_mxfp4_rows):
             f.restype = ctypes.c_int
         _dev_lib = lib
     return _dev_lib
@@ -224,3 +252,12 @@ def dev_e4m3_rows(codes_ptr: int, scale_ptr: int, rows: int, cols: int, seed: in
     sc = ctypes.c_float(scale_for_std(std))
     if _get_dev_lib().synth_dev_e4m3_rows(codes_ptr, scale_ptr, seed, tensor, rows, cols, sc, stream) != 0:
         raise RuntimeError("synth device fp8 fill failed")
+
+
+def dev_mxfp4_rows(codes_ptr: int, scale_ptr: int, rows: int, cols: int, seed: int, tensor: int, std: float,
+                   stream: int) -> None:
+    """Device twin of mxfp4_rows: codes [rows][cols] (uint8, one E2M1 code
+    each) and scale codes [rows][cols / 32] (uint8, E8M0)."""
+    sc = ctypes.c_float(scale_for_std(std))
+    if _get_dev_lib().synth_dev_mxfp4_rows(codes_ptr, scale_ptr, seed, tensor, rows, cols, sc, stream) != 0:
+        raise RuntimeError("synth device mxfp4 fill failed")

@@ -24,7 +24,7 @@ class ModelShape:
     vocab: int
     d_selfcond: int
     dtype: str = "bf16"          # dense weights and activation storage: "f32" | "bf16"
-    expert_dtype: str = "bf16"   # routed and shared experts: "f32" | "bf16" | "fp8"
+    expert_dtype: str = "bf16"   # routed and shared experts: "f32" | "bf16" | "fp8" | "mxfp4"
     lm_dtype: str = "bf16"       # "f32" | "bf16" | "fp8"
     rope_base: float = 10000.0
     norm_eps: float = 1e-6
@@ -93,6 +93,12 @@ FULL_30 = replace(FULL_LAYER, n_layers=30)
 
 FULL_LAYER_FP8 = replace(FULL_LAYER, expert_dtype="fp8", lm_dtype="fp8")
 
+# 4-bit experts (OCP MXFP4: E2M1 elements, an E8M0 scale per 32 inputs), the
+# rest bf16: the 30-layer model and the one-layer model of the fp8 workload
+# with its experts in MXFP4 instead of fp8 (LM head fp8).
+FULL_30_MX4 = replace(FULL_30, expert_dtype="mxfp4")
+FULL_LAYER_MX4 = replace(FULL_LAYER, expert_dtype="mxfp4", lm_dtype="fp8")
+
 # Small bf16 shape for parity tests of the MFMA path: several K chunks, 16
 # vocabulary tiles, ragged expert segments, a shared expert split in two
 # d_expert-wide slices.  Not one of the pages' workloads.
@@ -120,6 +126,13 @@ WORKLOADS = {
     # fp8 experts + LM head, 4 independent canvases over 8192-row prefixes (random N(0,1)
     # cache as in the one-layer workload), 12 steps, sampler seeds 0..3.
     "fp8batch4": Workload("fp8batch4", FULL_LAYER_FP8, batch=4, canvas=256, prefix=8192,
+                          prefix_mode="random_kv", n_steps=12, adaptive=False, lm_scale=1.0,
+                          sampler_seeds=(0, 1, 2, 3)),
+    # the 30-layer workload with MXFP4 experts (same LM-head scale)
+    "full30_mx4": Workload("full30_mx4", FULL_30_MX4, batch=1, canvas=256, prefix=4096, n_steps=12,
+                           adaptive=False, lm_scale=7.6),
+    # the fp8 batch-4 workload with MXFP4 experts
+    "mx4batch4": Workload("mx4batch4", FULL_LAYER_MX4, batch=4, canvas=256, prefix=8192,
                           prefix_mode="random_kv", n_steps=12, adaptive=False, lm_scale=1.0,
                           sampler_seeds=(0, 1, 2, 3)),
 }

@@ -25,6 +25,15 @@
  *                    code[r][c] = E4M3 code of fp32(w[r][c] / s_r), rounded to
  *                    nearest even, |x| >= 464 saturating to 448 (OCP FP8 E4M3:
  *                    exponent bias 7, 3 mantissa bits, no infinities).
+ *   MXFP4 weights  = the bf16 normal tensor quantised in blocks of 32
+ *                    consecutive values of a row (OCP Microscaling Formats
+ *                    v1.0): shared exponent E = floor(log2(max |w|)) - 2 (2 is
+ *                    the largest E2M1 exponent), clamped to [-127, 127], stored
+ *                    as the E8M0 code E + 127; element codes E2M1(w / 2^E)
+ *                    (sign, 2 exponent bits with bias 1, 1 mantissa bit:
+ *                    0, 0.5, 1, 1.5, 2, 3, 4, 6), rounded to nearest even on
+ *                    that grid, |x| > 6 saturating to 6.  An all-zero block
+ *                    gets the code 0 and zero elements.
  */
 #include <math.h>
 #include <stdint.h>
@@ -119,6 +128,72 @@ void synth_e4m3_rows(uint64_t seed, uint64_t tensor, int64_t rows, int64_t cols,
       float w;
       memcpy(&w, &u, 4);
       codes[r * cols + c] = synth_e4m3_rne(w / s);
+    }
+  }
+}
+
+/* E2M1 code of x (finite), round to nearest even on the grid
+ * {0, 0.5, 1, 1.5, 2, 3, 4, 6}: the thresholds are the grid's midpoints, a
+ * midpoint going to the neighbour whose code is even; |x| > 6 gives 6. */
+static inline uint8_t synth_e2m1_rne(float x) {
+  const uint8_t sign = signbit(x) ? 8u : 0u;
+  const float a = fabsf(x);
+  uint8_t c;
+  if (a <= 0.25f) c = 0;
+  else if (a < 0.75f) c = 1;
+  else if (a <= 1.25f) c = 2;
+  else if (a < 1.75f) c = 3;
+  else if (a <= 2.5f) c = 4;
+  else if (a < 3.5f) c = 5;
+  else if (a <= 5.0f) c = 6;
+  else c = 7;
+  return sign | c;
+}
+
+/* MXFP4 form of one block of 32 fp32 values: codes[32] (one E2M1 code per
+ * byte) and the E8M0 scale code. */
+static void synth_mxfp4_block(const float* w, uint8_t* codes, uint8_t* scale) {
+  float mx = 0.0f;
+  for (int i = 0; i < 32; ++i)
+    if (fabsf(w[i]) > mx) mx = fabsf(w[i]);
+  if (mx == 0.0f) {
+    *scale = 0;
+    for (int i = 0; i < 32; ++i) codes[i] = 0;
+    return;
+  }
+  int e2;
+  frexpf(mx, &e2); /* mx = f 2^e2, f in [0.5, 1): floor(log2 mx) = e2 - 1 */
+  int E = e2 - 1 - 2;
+  if (E < -127) E = -127;
+  if (E > 127) E = 127;
+  *scale = (uint8_t)(E + 127);
+  for (int i = 0; i < 32; ++i) codes[i] = synth_e2m1_rne(ldexpf(w[i], -E));
+}
+
+/* MXFP4 form of w[rows][cols] (cols % 32 == 0): codes [rows][cols], scales
+ * [rows][cols / 32]. */
+void synth_mxfp4_quantize(const float* w, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t b = 0; b < cols / 32; ++b)
+      synth_mxfp4_block(w + r * cols + b * 32, codes + r * cols + b * 32, scales + r * (cols / 32) + b);
+}
+
+/* MXFP4 form of the bf16 normal tensor [rows][cols] (element r*cols + c of
+ * the tensor's stream). */
+void synth_mxfp4_rows(uint64_t seed, uint64_t tensor, int64_t rows, int64_t cols, float scale, uint8_t* codes,
+                      uint8_t* scales) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    float w[32];
+    for (int64_t b = 0; b < cols / 32; ++b) {
+      for (int i = 0; i < 32; ++i) {
+        const uint32_t u =
+            (uint32_t)synth_bf16_rne(synth_normal_value(synth_hash(seed, tensor, (uint64_t)(r * cols + b * 32 + i)), scale))
+            << 16;
+        memcpy(&w[i], &u, 4);
+      }
+      synth_mxfp4_block(w, codes + r * cols + b * 32, scales + r * (cols / 32) + b);
     }
   }
 }

@@ -83,6 +83,45 @@ __global__ __launch_bounds__(256) void k_e4m3_rows(uint8_t* codes, float* row_sc
     codes[r * cols + c] = synth_e4m3_rne(__fdiv_rn(synth_bf16_value(seed, tensor, r * cols + c, scale), s));
 }
 
+// E2M1 code of x (finite), round to nearest even on {0, 0.5, 1, 1.5, 2, 3, 4, 6}
+// (the host file's definition).
+__device__ __forceinline__ uint8_t synth_e2m1_rne(float x) {
+  const uint8_t sign = (__float_as_uint(x) >> 31) ? 8u : 0u;
+  const float a = fabsf(x);
+  uint8_t c;
+  if (a <= 0.25f) c = 0;
+  else if (a < 0.75f) c = 1;
+  else if (a <= 1.25f) c = 2;
+  else if (a < 1.75f) c = 3;
+  else if (a <= 2.5f) c = 4;
+  else if (a < 3.5f) c = 5;
+  else if (a <= 5.0f) c = 6;
+  else c = 7;
+  return sign | c;
+}
+
+// One thread per block of 32 values of a row: shared exponent, then the codes.
+__global__ __launch_bounds__(256) void k_mxfp4_rows(uint8_t* codes, uint8_t* scales, uint64_t seed, uint64_t tensor,
+                                                    uint64_t rows, uint64_t cols, float scale) {
+  const uint64_t nb = cols / 32;
+  for (uint64_t q = (uint64_t)blockIdx.x * 256 + threadIdx.x; q < rows * nb; q += (uint64_t)gridDim.x * 256) {
+    const uint64_t r = q / nb, b = q - r * nb;
+    const uint64_t i0 = r * cols + b * 32;
+    float mx = 0.0f;
+    for (int i = 0; i < 32; ++i) mx = fmaxf(mx, fabsf(synth_bf16_value(seed, tensor, i0 + i, scale)));
+    if (mx == 0.0f) {
+      scales[q] = 0;
+      for (int i = 0; i < 32; ++i) codes[i0 + i] = 0;
+      continue;
+    }
+    int e2;
+    frexpf(mx, &e2);
+    const int E = min(127, max(-127, e2 - 1 - 2));
+    scales[q] = (uint8_t)(E + 127);
+    for (int i = 0; i < 32; ++i) codes[i0 + i] = synth_e2m1_rne(ldexpf(synth_bf16_value(seed, tensor, i0 + i, scale), -E));
+  }
+}
+
 dim3 grid_for(uint64_t count) {
   uint64_t b = (count + 255) / 256;
   if (b > 65536) b = 65536;
@@ -127,6 +166,14 @@ int synth_dev_e4m3_rows(void* codes, void* row_scale, uint64_t seed, uint64_t te
   if (rows == 0 || rows > 0x7FFFFFFFull) return -1;
   hipLaunchKernelGGL(k_e4m3_rows, dim3((unsigned)rows), dim3(256), 0, (hipStream_t)stream, (uint8_t*)codes,
                      (float*)row_scale, seed, tensor, cols, scale);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+int synth_dev_mxfp4_rows(void* codes, void* scales, uint64_t seed, uint64_t tensor, uint64_t rows, uint64_t cols,
+                         float scale, void* stream) {
+  if (rows == 0 || cols % 32) return -1;
+  hipLaunchKernelGGL(k_mxfp4_rows, grid_for(rows * (cols / 32)), dim3(256), 0, (hipStream_t)stream, (uint8_t*)codes,
+                     (uint8_t*)scales, seed, tensor, rows, cols, scale);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
