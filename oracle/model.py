@@ -136,10 +136,33 @@ def accumulation(kind: str):
         _ACC[0] = old
 
 
+# The float32 evaluation sums each product's K terms in the BLAS order of the
+# operands as given ("fwd") or with the K axis reversed ("rev"): two correct
+# float32 evaluations of the same definition, so that the spread between
+# such evaluations is measured with more than one sample.
+_ORDER = ["fwd"]
+
+
+@contextlib.contextmanager
+def twin_order(kind: str):
+    if kind not in ("fwd", "rev"):
+        raise ValueError(kind)
+    old = _ORDER[0]
+    _ORDER[0] = kind
+    try:
+        yield
+    finally:
+        _ORDER[0] = old
+
+
 def mm(a, b) -> np.ndarray:
     if _ACC[0] == "f64":
         return np.asarray(a) @ np.asarray(b)
-    return (np.asarray(a, dtype=np.float32) @ np.asarray(b, dtype=np.float32)).astype(np.float64)
+    a32, b32 = np.asarray(a, dtype=np.float32), np.asarray(b, dtype=np.float32)
+    if _ORDER[0] == "rev":
+        a32 = np.ascontiguousarray(a32[..., ::-1])
+        b32 = np.ascontiguousarray(np.flip(b32, axis=-2))
+    return (a32 @ b32).astype(np.float64)
 
 
 def norm(shape: ModelShape, x: np.ndarray) -> np.ndarray:

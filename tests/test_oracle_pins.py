@@ -15,6 +15,7 @@ term, a wrong normalisation.
 from dataclasses import replace
 
 import numpy as np
+import pytest
 import torch
 
 from synth.configs import TINY
@@ -187,3 +188,29 @@ def test_denoise_logits_without_layers_is_embedding_then_head():
     xin = E[3] + np.array([0.0, 0.0, 20.0, 0.0])  # (0, 1, 20, 0)
     n = xin / np.sqrt(np.mean(xin ** 2) + 1e-6)
     assert np.allclose(z[0, 0], np.concatenate([n, [0.0]]), rtol=1e-12, atol=1e-15)
+
+
+def test_float32_twin_orders():
+    """The float32 evaluations used to measure drift: both orders are float32
+    sums of the exact products (within K * 2^-24 relative of the float64
+    result), they differ from each other in the last bits, and neither
+    changes the float64 default."""
+    rng = np.random.default_rng(5)
+    a = rng.standard_normal((8, 4096))
+    b = rng.standard_normal((4096, 16))
+    exact = a @ b
+    with om.twin_order("rev"):
+        assert np.array_equal(om.mm(a, b), exact)          # f64 default unaffected
+    a32 = a.astype(np.float32).astype(np.float64)
+    b32 = b.astype(np.float32).astype(np.float64)
+    ref = a32 @ b32
+    bound = 4096 * 2.0 ** -24 * (np.abs(a32) @ np.abs(b32))
+    with om.accumulation("f32"):
+        fwd = om.mm(a, b)
+        with om.twin_order("rev"):
+            rev = om.mm(a, b)
+    assert np.all(np.abs(fwd - ref) <= bound) and np.all(np.abs(rev - ref) <= bound)
+    assert not np.array_equal(fwd, rev)
+    with pytest.raises(ValueError):
+        with om.twin_order("sideways"):
+            pass
