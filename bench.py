@@ -50,7 +50,7 @@ HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 GEMM_SRC = os.path.join(ROOT, "discrete_text_diffusion_amd", "csrc", "k_gemm.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "moe_up_gate_up_traffic.md")
-MOE_UP_KERNEL = "k_wsgemm<32, 1, 128, true, 0, false, 2>"
+MOE_UP_KERNEL = "k_wsgemm<32, 1, 128, true, 0, 0, 2>"
 COPY_BYTES = 1 << 30       # bytes read (and written) by one calibration copy
 
 
@@ -400,6 +400,13 @@ class EventPool:
         return out
 
 
+def expert_weight_bytes(shape, n):
+    """Stored bytes of n expert weights: bf16 2 each, fp8 1 (+ a 4-byte scale
+    per output row, left out), MXFP4 17 per 32 (16 bytes of E2M1 codes and
+    one E8M0 scale)."""
+    return {"fp8": n, "mxfp4": n * 17 / 32, "f32": 4 * n}.get(shape.expert_dtype, 2 * n)
+
+
 def moe_up_bytes(shape, T, experts=None):
     """Algorithmic HBM bytes of one routed + shared gate/up launch: the gate and
     up weights of every expert that receives a token (`experts`, by default
@@ -409,7 +416,7 @@ def moe_up_bytes(shape, T, experts=None):
     d, de, ds = shape.d_model, shape.d_expert, shape.d_shared
     if experts is None:
         experts = min(shape.n_experts, T * shape.top_k)
-    w = experts * 2 * de * d * 2 + 2 * ds * d * 2
+    w = expert_weight_bytes(shape, experts * 2 * de * d + 2 * ds * d)
     act = T * d * 2
     rows = T * shape.top_k + (ds // de) * T
     return w + act + rows * de * 2
@@ -473,10 +480,9 @@ def ar_step_bytes(shape, L):
     activations (a few KB) are left out."""
     d = shape.d_model
     wb = 4 if shape.dtype == "f32" else 2
-    eb = 1 if shape.expert_dtype == "fp8" else wb
     lb = 1 if shape.lm_dtype == "fp8" else wb
     dense = (shape.qkv_rows * d + d * shape.q_dim + shape.n_experts * d) * wb
-    experts = (shape.top_k * shape.d_expert + shape.d_shared) * 3 * d * eb
+    experts = expert_weight_bytes(shape, (shape.top_k * shape.d_expert + shape.d_shared) * 3 * d)
     kv = 2 * (L + 1) * shape.kv_dim * wb
     return shape.n_layers * (dense + experts + kv) + shape.vocab * d * lb
 
@@ -1084,13 +1090,13 @@ def main():
         "accepted_mean": round(sum(acc_steps) / len(acc_steps), 2),
         "phase_ms_one_step": breakdown,
         "roofline": {
-            "kernel": "routed+shared expert gate/up GEMM (k_wsgemm<32,1,128,GeGLU>)",
+            "kernel": f"routed+shared expert gate/up GEMM (k_wsgemm<32,1,128,GeGLU>, {shape.expert_dtype} weights)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": stored_traffic(),
+            "traffic": stored_traffic() if args.workload == "full30" else None,  # counters taken on full30
             "achieved_definition": "sum over the timed launches of each launch's algorithmic bytes (the experts "
                                    "its own routing touched) / sum of their HIP-event durations",
             "algorithmic_bytes_per_launch": int(up_bytes.mean()),

@@ -34,6 +34,7 @@ DG_NOALLOC_SCRATCH_BYTES = 320 << 20
 DG_DTYPE_F32 = 0
 DG_DTYPE_BF16 = 1
 DG_DTYPE_FP8_E4M3 = 2
+DG_DTYPE_MXFP4 = 3
 DG_FLAG_NONFINITE = 1
 DG_ENTROPY_BOUND = 0.1
 DG_STOP_THRESHOLD = 0.005
@@ -103,6 +104,7 @@ _ws_bytes = _sig("dg_workspace_bytes", c_size_t, _P(ModelConfig), c_int32, c_int
 _pack = _sig("dg_pack_weight_bf16", c_int32, c_void_p, c_void_p, c_int64, c_int64, c_void_p)
 _pack_t = _sig("dg_pack_weight_bf16_transposed", c_int32, c_void_p, c_void_p, c_int64, c_int64, c_void_p)
 _pack8 = _sig("dg_pack_weight_fp8", c_int32, c_void_p, c_void_p, c_int64, c_int64, c_void_p)
+_pack4 = _sig("dg_pack_weight_mxfp4", c_int32, c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_void_p)
 _init_canvas = _sig("dg_init_canvas", c_int32, _P(ModelConfig), _P(Canvas), c_int32, c_void_p)
 _encode = _sig("dg_encode_append", c_int32, _P(ModelConfig), _P(Weights), _P(KVCache), c_void_p, c_int32, c_int32,
                c_void_p, c_size_t, c_void_p)
@@ -136,7 +138,7 @@ _t_ar = _sig("dg_test_ar_step", c_int32, _P(ModelConfig), _P(Weights), _P(KVCach
              c_void_p, c_void_p, c_size_t, c_void_p)
 
 EXPORTED = ("dg_temperature", "dg_workspace_bytes", "dg_pack_weight_bf16", "dg_pack_weight_bf16_transposed",
-            "dg_pack_weight_fp8",
+            "dg_pack_weight_fp8", "dg_pack_weight_mxfp4",
             "dg_init_canvas", "dg_encode_append", "dg_denoise_step", "dg_commit_block", "dg_status_string",
             "dg_test_sample_from_logits", "dg_test_route_from_logits", "dg_test_forward_logits",
             "dg_denoise_step_traced", "dg_encode_append_traced", "dg_test_encode_append", "dg_ar_step", "dg_commit_and_step",
@@ -170,6 +172,10 @@ def dg_pack_weight_bf16_transposed(dst, src, rows: int, cols: int, stream) -> No
 
 def dg_pack_weight_fp8(dst, src, rows: int, cols: int, stream) -> None:
     _check(_pack8(dst, src, rows, cols, stream), "dg_pack_weight_fp8")
+
+
+def dg_pack_weight_mxfp4(dst, codes, scales, rows: int, cols: int, stream) -> None:
+    _check(_pack4(dst, codes, scales, rows, cols, stream), "dg_pack_weight_mxfp4")
 
 
 def dg_init_canvas(cfg, canvas, block: int, stream) -> None:

@@ -27,6 +27,7 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 struct Shape {
   int L, d, nq, nkv, dh, E, k, de, ds, V, dsc, dt;
   bool ex8, lm8;  // fp8 expert / LM-head weights
+  bool ex4;       // MXFP4 expert weights
   float rope_base, eps;
   int qdim, kvdim, qkv, n_sh, nvt;
   size_t act;  // bytes per activation element
@@ -39,6 +40,7 @@ Shape shape_of(const dg_model_config* c) {
   s.dsc = c->d_selfcond; s.dt = c->dtype;
   s.ex8 = c->expert_dtype == DG_DTYPE_FP8_E4M3;
   s.lm8 = c->lm_dtype == DG_DTYPE_FP8_E4M3;
+  s.ex4 = c->expert_dtype == DG_DTYPE_MXFP4;
   s.rope_base = c->rope_base; s.eps = c->norm_eps;
   s.qdim = s.nq * s.dh; s.kvdim = s.nkv * s.dh; s.qkv = s.qdim + 2 * s.kvdim;
   s.n_sh = s.de > 0 ? s.ds / s.de : 0;
@@ -56,8 +58,13 @@ int check_config(const dg_model_config* c) {
   if (c->dtype != DG_DTYPE_F32 && c->dtype != DG_DTYPE_BF16) return DG_ERR_UNSUPPORTED;
   // fp8 weights (experts, LM head) only in bf16 models
   for (int wd : {c->expert_dtype, c->lm_dtype})
-    if (wd != c->dtype && !(wd == DG_DTYPE_FP8_E4M3 && c->dtype == DG_DTYPE_BF16)) return DG_ERR_UNSUPPORTED;
+    if (wd != c->dtype && !(wd == DG_DTYPE_FP8_E4M3 && c->dtype == DG_DTYPE_BF16) &&
+        !(wd == DG_DTYPE_MXFP4 && wd == c->expert_dtype && c->dtype == DG_DTYPE_BF16))
+      return DG_ERR_UNSUPPORTED;
+  if (c->lm_dtype == DG_DTYPE_MXFP4) return DG_ERR_UNSUPPORTED;
   if (c->expert_dtype == DG_DTYPE_FP8_E4M3 && c->d_model % 128) return DG_ERR_UNSUPPORTED;
+  if (c->expert_dtype == DG_DTYPE_MXFP4 && (c->d_model % 64 || c->d_expert % 64 || c->d_shared % 64))
+    return DG_ERR_UNSUPPORTED;
   if (c->n_q_heads % c->n_kv_heads || c->d_shared % c->d_expert || c->vocab % 256 || c->d_head % 2 ||
       c->top_k > 16 || c->n_experts > 255 || c->d_head > 256)
     return DG_ERR_UNSUPPORTED;
@@ -202,7 +209,7 @@ constexpr int64_t kRowPartBytes = 32ll << 20;
 // average expert's rows span several tiles, so that each weight fragment a
 // wave loads feeds more MFMAs.  fp8 experts keep 32.
 int moe_bm(const Shape& s, int T) {
-  if (s.ex8) return kMoeBM;
+  if (s.ex8 || s.ex4) return kMoeBM;
   const int64_t per_expert = (int64_t)T * s.k / s.E;
   return per_expert >= 512 ? 128 : per_expert >= 128 ? 64 : kMoeBM;
 }
@@ -439,6 +446,7 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
         a.ws0 = lw.ex_g_scale; a.ws1 = lw.ex_u_scale; a.ws_group_stride = s.de;
         a.ws0_alt = lw.sh_g_scale; a.ws1_alt = lw.sh_u_scale; a.ws_alt_stride = s.de;  // slice c: features c*de..
       }
+      a.w_mx4 = s.ex4;
       if (bf) {
         a.n_fb = (s.de + 63) / 64;
         a.tile_fastest = 1;  // the row tiles of one (expert, feature block) run together (same XCD): a hot
@@ -450,7 +458,7 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
         // K is split four ways; gate and up partials go to the workspace and
         // a summing kernel applies the GeGLU.
         const int dsplit = 4;
-        if (!s.ex8 && (int64_t)T * s.k < s.E && s.d / kc >= dsplit &&
+        if (!s.ex8 && !s.ex4 && (int64_t)T * s.k < s.E && s.d / kc >= dsplit &&
             2 * dsplit * rows_moe * s.de <= (int64_t)c.p.g_rows * std::max(s.qkv, s.dsc)) {
           a.k_split = ((s.d / kc + dsplit - 1) / dsplit) * kc;
           a.n_split = (s.d + a.k_split - 1) / a.k_split;
@@ -483,10 +491,11 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
         a.ws0 = lw.ex_d_scale; a.ws_group_stride = s.d;
         a.ws0_alt = lw.sh_d_scale; a.ws_alt_stride = 0;  // K slices of one matrix: same output features
       }
+      a.w_mx4 = s.ex4;
       if (bf) {
         // fewer (token, slot) pairs than experts (the decode step): one
         // 16-feature tile per wave, twice the workgroups for the few row tiles
-        const int nwt = (!s.ex8 && (int64_t)T * s.k < s.E) ? 1 : 2;
+        const int nwt = (!s.ex8 && !s.ex4 && (int64_t)T * s.k < s.E) ? 1 : 2;
         a.n_fb = (s.d + 64 * nwt - 1) / (64 * nwt);
         a.tile_fastest = 1;  // the row tiles of one (expert, feature block) run together (same XCD): a hot
                              // expert's weight slice comes from HBM once and from L2 for its other tiles
@@ -768,6 +777,16 @@ int dg_pack_weight_fp8(void* d_dst, const void* d_src, int64_t rows, int64_t col
   if (!d_dst || !d_src || rows <= 0 || cols <= 0 || rows % 16 || cols % 32) return DG_ERR_INVALID_ARG;
   return launch_pack_fp8((uint8_t*)d_dst, (const uint8_t*)d_src, rows, cols, (hipStream_t)stream) == 0 ? DG_OK
                                                                                                       : DG_ERR_HIP;
+}
+
+int dg_pack_weight_mxfp4(void* d_dst, const void* d_codes, const void* d_scales, int64_t rows, int64_t cols,
+                         void* stream) {
+  if (!d_dst || !d_codes || !d_scales || rows <= 0 || cols <= 0 || rows % 16 || cols % 64)
+    return DG_ERR_INVALID_ARG;
+  return launch_pack_mxfp4((uint8_t*)d_dst, (const uint8_t*)d_codes, (const uint8_t*)d_scales, rows, cols,
+                           (hipStream_t)stream) == 0
+             ? DG_OK
+             : DG_ERR_HIP;
 }
 
 int dg_init_canvas(const dg_model_config* cfg, dg_canvas* cv, int32_t block, void* stream) {

@@ -22,6 +22,18 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint2 w) {
   return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// Eight MXFP4 elements (the E2M1 codes in the nibbles of q, lowest first)
+// times their block scale 2^(code - 127), as eight bf16: exact for scale
+// codes 1..254 (every such product is a bf16 value); code 0 gives zeros.
+__device__ __forceinline__ bf16x8_t mx4x8_to_bf16(uint32_t q, uint32_t scale_code) {
+  const float sc = __uint_as_float(scale_code << 23);
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 0);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 1);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 2);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 3);
+  return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 __device__ __forceinline__ float bf2f(bf16_t u) { return __uint_as_float((uint32_t)u << 16); }
 
 // fp32 -> bf16, round to nearest even (finite inputs).

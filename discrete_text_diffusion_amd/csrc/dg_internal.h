@@ -60,6 +60,9 @@ struct GemmArgs {
   // lane order), each output feature n scaled by an fp32 factor: main group g
   // reads ws0/ws1[g * ws_group_stride + n], alt group c ws0_alt/ws1_alt[c * ws_alt_stride + n]
   int32_t w_fp8;
+  // MXFP4 weights: 16 x 64 superblocks of 544 B (E2M1 codes in A-operand lane
+  // order, then the 32 E8M0 block scales), see dg_pack_weight_mxfp4
+  int32_t w_mx4;
   const float* ws0;
   const float* ws1;
   int64_t ws_group_stride;
@@ -121,6 +124,8 @@ int launch_split_epilogue(const GemmArgs& a, const float* part, int n_split, int
 int launch_gemm_simple(const GemmArgs& a, hipStream_t s);
 int launch_pack_bf16(bf16_t* dst, const bf16_t* src, int64_t rows, int64_t cols, int transposed, hipStream_t s);
 int launch_pack_fp8(uint8_t* dst, const uint8_t* src, int64_t rows, int64_t cols, hipStream_t s);
+int launch_pack_mxfp4(uint8_t* dst, const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                      hipStream_t s);
 int launch_lm_partials_from_logits(const float* logits, int rows, const LmArgs& lm, hipStream_t s);
 // k_route.hip
 int launch_topk(const float* part, int n_split, int64_t split_stride, int T, int E, int k, const int32_t* forced,

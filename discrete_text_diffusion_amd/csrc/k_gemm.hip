@@ -182,21 +182,30 @@ struct GroupW {
   int kt, kt_off;
 };
 
+// Weight formats of the streaming kernel.
+constexpr int WF_BF16 = 0, WF_FP8 = 1, WF_MX4 = 2;
+
+// Bytes of `elems` weights in format wf (MXFP4: 17 bytes per 32 weights, 16
+// of E2M1 codes and one scale; elems is a multiple of 16 x 64).
+__device__ __forceinline__ int64_t weight_bytes(int64_t elems, int wf) {
+  return wf == WF_MX4 ? elems / 32 * 17 : elems * (wf == WF_FP8 ? 1 : 2);
+}
+
 // Weight and scale bases of group g (an expert, or a shared-expert slice).
-// esize: bytes per weight element (2 bf16, 1 fp8 code).
-__device__ __forceinline__ GroupW group_weights(const GemmArgs& a, int g, int esize) {
+__device__ __forceinline__ GroupW group_weights(const GemmArgs& a, int g, int wf) {
   GroupW r;
   if (g < a.n_main) {
-    r.w0 = reinterpret_cast<const char*>(a.w0) + (int64_t)g * a.w_group_stride * esize;
-    r.w1 = a.w1 ? reinterpret_cast<const char*>(a.w1) + (int64_t)g * a.w_group_stride * esize : nullptr;
+    r.w0 = reinterpret_cast<const char*>(a.w0) + weight_bytes((int64_t)g * a.w_group_stride, wf);
+    r.w1 = a.w1 ? reinterpret_cast<const char*>(a.w1) + weight_bytes((int64_t)g * a.w_group_stride, wf) : nullptr;
     r.s0 = a.ws0 ? a.ws0 + (int64_t)g * a.ws_group_stride : nullptr;
     r.s1 = a.ws1 ? a.ws1 + (int64_t)g * a.ws_group_stride : nullptr;
     r.kt = a.kt_main;
     r.kt_off = 0;
   } else {
     const int c = g - a.n_main;
-    r.w0 = reinterpret_cast<const char*>(a.w0_alt) + (int64_t)c * a.w_alt_stride * esize;
-    r.w1 = a.w1_alt ? reinterpret_cast<const char*>(a.w1_alt) + (int64_t)c * a.w_alt_stride * esize : nullptr;
+    r.w0 = reinterpret_cast<const char*>(a.w0_alt) + weight_bytes((int64_t)c * a.w_alt_stride, wf);
+    r.w1 = a.w1_alt ? reinterpret_cast<const char*>(a.w1_alt) + weight_bytes((int64_t)c * a.w_alt_stride, wf)
+                    : nullptr;
     r.s0 = a.ws0_alt ? a.ws0_alt + (int64_t)c * a.ws_alt_stride : nullptr;
     r.s1 = a.ws1_alt ? a.ws1_alt + (int64_t)c * a.ws_alt_stride : nullptr;
     r.kt = a.kt_alt;
@@ -205,17 +214,25 @@ __device__ __forceinline__ GroupW group_weights(const GemmArgs& a, int g, int es
   return r;
 }
 
-// Weight operand registers: one 16-byte bf16 fragment, or 8 fp8 codes
-// converted to bf16 when the MFMA consumes them.
-template <bool FP8> struct WFrag { typedef bf16x8_t type; };
-template <> struct WFrag<true> { typedef uint2 type; };
+// Weight operand registers per 32-wide K step: one 16-byte bf16 fragment, or
+// 8 fp8 codes converted to bf16 when the MFMA consumes them.  MXFP4 holds one
+// 64-wide superblock per two K steps (entry s / 2): the lane's 8 bytes of E2M1
+// codes (K step 2j in .q.x, 2j + 1 in .q.y) and its row's two scale codes
+// (low byte for step 2j).
+struct Mx4Frag {
+  uint2 q;
+  uint32_t s;
+};
+template <int WF> struct WFrag { typedef bf16x8_t type; };
+template <> struct WFrag<WF_FP8> { typedef uint2 type; };
+template <> struct WFrag<WF_MX4> { typedef Mx4Frag type; };
 __device__ __forceinline__ bf16x8_t wfrag_bf16(bf16x8_t w) { return w; }
 __device__ __forceinline__ bf16x8_t wfrag_bf16(uint2 w) { return fp8x8_to_bf16(w); }
 
 // Main loop of the weight-streaming kernel.  WS: stages of
 // the weight register ring (weights are loaded WS - 1 chunks ahead of their
 // MFMAs); activations are always one chunk ahead, double buffered in LDS.
-template <int BM, int NWT, int KC, bool GEGLU, int ACT, bool FP8 = false, int WS = 2>
+template <int BM, int NWT, int KC, bool GEGLU, int ACT, int WF = WF_BF16, int WS = 2>
 __device__ __forceinline__ void wsgemm_mainloop(const GemmArgs& a, const GemmTile& td, const GroupW& gw, int fb,
                                                 int ks, bf16_t* xs, f32x4_t (&acc)[NWT][BM / 16],
                                                 f32x4_t (&accu)[NWT][BM / 16]) {
@@ -226,9 +243,12 @@ __device__ __forceinline__ void wsgemm_mainloop(const GemmArgs& a, const GemmTil
   constexpr int NV = BM * VPR;         // vectors per chunk
   constexpr int VPT = (NV + kThreads - 1) / kThreads;
 
+  constexpr bool FP8 = WF == WF_FP8, MX4 = WF == WF_MX4;
+  static_assert(!MX4 || KC % 64 == 0, "MXFP4 chunks are whole 64-wide superblocks");
   constexpr int TILE_B = FP8 ? 512 : 1024;  // bytes of one 16 x 32 weight tile
   constexpr int LANE_B = FP8 ? 8 : 16;      // bytes of one lane's fragment
-  using W_t = typename WFrag<FP8>::type;
+  constexpr int SB_B = 544;                 // MXFP4: one 16 x 64 superblock
+  using W_t = typename WFrag<WF>::type;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
 #pragma unroll
@@ -264,7 +284,8 @@ __device__ __forceinline__ void wsgemm_mainloop(const GemmArgs& a, const GemmTil
   for (int i = 0; i < NWT; ++i) {
     const int ft = (fb * 4 + wave) * NWT + i;
     wval[i] = ft * 16 < a.N;
-    const int64_t off = ((int64_t)(wval[i] ? ft : 0) * gw.kt + gw.kt_off) * TILE_B + lane * LANE_B;
+    const int64_t off = MX4 ? ((int64_t)(wval[i] ? ft : 0) * (gw.kt >> 1) + (gw.kt_off >> 1)) * SB_B + lane * 8
+                            : ((int64_t)(wval[i] ? ft : 0) * gw.kt + gw.kt_off) * TILE_B + lane * LANE_B;
     wp0[i] = gw.w0 + off;
     wp1[i] = GEGLU ? gw.w1 + off : nullptr;
   }
@@ -279,16 +300,35 @@ __device__ __forceinline__ void wsgemm_mainloop(const GemmArgs& a, const GemmTil
   // every path keep the compiler's wait counts exact; a load under a branch
   // makes it wait, conservatively, for the next chunk's loads before the
   // current chunk's MFMAs.
+  // MXFP4: the lane's scale codes sit 512 + 2 (row) bytes into the superblock
+  const int sofs = 512 - lane * 8 + 2 * (lane & 15);
   auto load_w = [&](auto BUF, int k0) {
     constexpr int buf = decltype(BUF)::value;
-    const int kt0 = k0 >> 5;
+    if constexpr (MX4) {
+      const int sb0 = k0 >> 6;
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
+      for (int s = 0; s < KS / 2; ++s)
 #pragma unroll
-      for (int i = 0; i < NWT; ++i) {
-        wa[buf][s][i] = *reinterpret_cast<const W_t*>(wp0[i] + (int64_t)(kt0 + s) * TILE_B);
-        if constexpr (GEGLU) wb[buf][s][i] = *reinterpret_cast<const W_t*>(wp1[i] + (int64_t)(kt0 + s) * TILE_B);
-      }
+        for (int i = 0; i < NWT; ++i) {
+          const char* p = wp0[i] + (int64_t)(sb0 + s) * SB_B;
+          wa[buf][s][i].q = *reinterpret_cast<const uint2*>(p);
+          wa[buf][s][i].s = *reinterpret_cast<const uint16_t*>(p + sofs);
+          if constexpr (GEGLU) {
+            const char* p1 = wp1[i] + (int64_t)(sb0 + s) * SB_B;
+            wb[buf][s][i].q = *reinterpret_cast<const uint2*>(p1);
+            wb[buf][s][i].s = *reinterpret_cast<const uint16_t*>(p1 + sofs);
+          }
+        }
+    } else {
+      const int kt0 = k0 >> 5;
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int i = 0; i < NWT; ++i) {
+          wa[buf][s][i] = *reinterpret_cast<const W_t*>(wp0[i] + (int64_t)(kt0 + s) * TILE_B);
+          if constexpr (GEGLU) wb[buf][s][i] = *reinterpret_cast<const W_t*>(wp1[i] + (int64_t)(kt0 + s) * TILE_B);
+        }
+    }
   };
   auto load_x = [&](int k0) {
 #pragma unroll
@@ -321,9 +361,20 @@ __device__ __forceinline__ void wsgemm_mainloop(const GemmArgs& a, const GemmTil
 #pragma unroll
       for (int i = 0; i < NWT; ++i) {
         if (!wval[i]) continue;
-        const bf16x8_t wai = wfrag_bf16(wa[cur][s][i]);
-        bf16x8_t wbi = wai;
-        if constexpr (GEGLU) wbi = wfrag_bf16(wb[cur][s][i]);
+        bf16x8_t wai, wbi;
+        if constexpr (MX4) {
+          const Mx4Frag fa = wa[cur][s >> 1][i];
+          wai = mx4x8_to_bf16((s & 1) ? fa.q.y : fa.q.x, ((s & 1) ? fa.s >> 8 : fa.s) & 0xffu);
+          wbi = wai;
+          if constexpr (GEGLU) {
+            const Mx4Frag fb_ = wb[cur][s >> 1][i];
+            wbi = mx4x8_to_bf16((s & 1) ? fb_.q.y : fb_.q.x, ((s & 1) ? fb_.s >> 8 : fb_.s) & 0xffu);
+          }
+        } else {
+          wai = wfrag_bf16(wa[cur][s][i]);
+          wbi = wai;
+          if constexpr (GEGLU) wbi = wfrag_bf16(wb[cur][s][i]);
+        }
 #pragma unroll
         for (int j = 0; j < MW; ++j) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wai, bx[j], acc[i][j], 0, 0, 0);
@@ -356,7 +407,7 @@ __device__ __forceinline__ void wsgemm_mainloop(const GemmArgs& a, const GemmTil
 
 // Epilogue of a 4-wave streaming workgroup: wave w holds features
 // ((fb * 4 + w) * NWT + i) * 16 + 4 (lane / 16) + e of rows j * 16 + lane % 16.
-template <int BM, int NWT, bool GEGLU, bool FP8>
+template <int BM, int NWT, bool GEGLU, int WF>
 __device__ __forceinline__ void ws_epilogue(const GemmArgs& a, const GemmTile& td, const GroupW& gw, int fb, int ks,
                                             const f32x4_t (&acc)[NWT][BM / 16], const f32x4_t (&accu)[NWT][BM / 16]) {
   constexpr int MW = BM / 16;
@@ -367,6 +418,7 @@ __device__ __forceinline__ void ws_epilogue(const GemmArgs& a, const GemmTile& t
     const int n = ft * 16 + (lane >> 4) * 4;
     // fp8: per-feature scales of the four features this lane holds
     f32x4_t sg = f32x4_t{1.f, 1.f, 1.f, 1.f}, su = sg;
+    constexpr bool FP8 = WF == WF_FP8;
     if constexpr (FP8) {
       if (ft * 16 < a.N) {
         const float4 v0 = *reinterpret_cast<const float4*>(gw.s0 + n);
@@ -396,7 +448,7 @@ __device__ __forceinline__ void ws_epilogue(const GemmArgs& a, const GemmTile& t
   }
 }
 
-template <int BM, int NWT, int KC, bool GEGLU, int ACT, bool FP8, int WS = 2>
+template <int BM, int NWT, int KC, bool GEGLU, int ACT, int WF, int WS = 2>
 __global__ __launch_bounds__(kThreads) void k_wsgemm(GemmArgs a) {
   constexpr int MW = BM / 16;
   constexpr int LD = KC + 8;
@@ -410,10 +462,10 @@ __global__ __launch_bounds__(kThreads) void k_wsgemm(GemmArgs a) {
   if (td.nrows <= 0) return;
 
   f32x4_t acc[NWT][MW], accu[NWT][MW];
-  const GroupW gw = group_weights(a, td.group, FP8 ? 1 : 2);
-  wsgemm_mainloop<BM, NWT, KC, GEGLU, ACT, FP8, WS>(a, td, gw, fb, ks, xs, acc, accu);
+  const GroupW gw = group_weights(a, td.group, WF);
+  wsgemm_mainloop<BM, NWT, KC, GEGLU, ACT, WF, WS>(a, td, gw, fb, ks, xs, acc, accu);
 
-  ws_epilogue<BM, NWT, GEGLU, FP8>(a, td, gw, fb, ks, acc, accu);
+  ws_epilogue<BM, NWT, GEGLU, WF>(a, td, gw, fb, ks, acc, accu);
 }
 
 // ---------------------------------------------------------------------------
@@ -988,6 +1040,37 @@ __global__ __launch_bounds__(kThreads) void k_pack_fp8(uint8_t* dst, const uint8
   *reinterpret_cast<uint2*>(dst + t * 512 + lane * 8) = *reinterpret_cast<const uint2*>(src + r * cols + c);
 }
 
+// Logical MXFP4 element codes [rows][cols] (one per byte) and block scale
+// codes [rows][cols / 32] -> MXFP4 weight layout: 16 x 64 superblocks of
+// 544 B, superblock (nt, kb) at byte (nt * cols / 64 + kb) * 544; lane l's 8
+// bytes at 8 l: the 8 codes (row nt*16 + l%16, k = kb*64 + 32h + 8(l/16) ...)
+// of half h in bytes 4h..4h+3, two per byte, lower k in the low nibble; then
+// the 16 rows' two scale codes at 512 + 2 (row) + h.  One wave per superblock.
+__global__ __launch_bounds__(kThreads) void k_pack_mxfp4(uint8_t* dst, const uint8_t* codes, const uint8_t* scales,
+                                                         int64_t rows, int64_t cols) {
+  const int64_t sbn = cols / 64;
+  const int64_t nsb = (rows / 16) * sbn;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= nsb) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t nt = t / sbn, kb = t - nt * sbn;
+  const int64_t r = nt * 16 + (lane & 15);
+  uint8_t* o = dst + t * 544;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint8_t* src = codes + r * cols + kb * 64 + 32 * h + (lane >> 4) * 8;
+    uint32_t word = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) word |= (uint32_t)((src[2 * q] & 15u) | ((src[2 * q + 1] & 15u) << 4)) << (8 * q);
+    *reinterpret_cast<uint32_t*>(o + lane * 8 + 4 * h) = word;
+  }
+  if (lane < 16) {
+    const uint8_t* sr = scales + (nt * 16 + lane) * (cols / 32) + kb * 2;
+    o[512 + 2 * lane] = sr[0];
+    o[512 + 2 * lane + 1] = sr[1];
+  }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -998,15 +1081,16 @@ static void launch_t(const GemmArgs& a0, int act, hipStream_t s) {
   GemmArgs a = a0;
   a.nblocks = round8(a.n_split * a.max_tiles * a.n_fb);
   dim3 grid(a.nblocks);
-  if (act == ACT_BF16) hipLaunchKernelGGL((k_wsgemm<BM, NWT, KC, GEGLU, ACT_BF16, false, WS>), grid, dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL((k_wsgemm<BM, NWT, KC, GEGLU, ACT_F32, false, WS>), grid, dim3(kThreads), 0, s, a);
+  if (act == ACT_BF16) hipLaunchKernelGGL((k_wsgemm<BM, NWT, KC, GEGLU, ACT_BF16, WF_BF16, WS>), grid, dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL((k_wsgemm<BM, NWT, KC, GEGLU, ACT_F32, WF_BF16, WS>), grid, dim3(kThreads), 0, s, a);
 }
 
-template <int BM, int NWT, int KC, bool GEGLU, int WS = 2>
-static void launch_fp8(const GemmArgs& a0, hipStream_t s) {
+// quantised weights (fp8 or MXFP4), bf16 activations
+template <int BM, int NWT, int KC, bool GEGLU, int WF, int WS = 2>
+static void launch_q(const GemmArgs& a0, hipStream_t s) {
   GemmArgs a = a0;
   a.nblocks = round8(a.n_split * a.max_tiles * a.n_fb);
-  hipLaunchKernelGGL((k_wsgemm<BM, NWT, KC, GEGLU, ACT_BF16, true, WS>), dim3(a.nblocks), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((k_wsgemm<BM, NWT, KC, GEGLU, ACT_BF16, WF, WS>), dim3(a.nblocks), dim3(kThreads), 0, s, a);
 }
 
 int launch_wsgemm(const GemmArgs& a, int bm, int nwt, int kc, bool geglu, hipStream_t s) {
@@ -1020,8 +1104,20 @@ int launch_wsgemm(const GemmArgs& a, int bm, int nwt, int kc, bool geglu, hipStr
         reinterpret_cast<uintptr_t>(a.ws1) % 16 || reinterpret_cast<uintptr_t>(a.ws0_alt) % 16 ||
         reinterpret_cast<uintptr_t>(a.ws1_alt) % 16)
       return -1;
-    if (bm == 32 && nwt == 1 && kc == 128 && geglu) launch_fp8<32, 1, 128, true>(a, s);
-    else if (bm == 32 && nwt == 2 && kc == 64 && !geglu) launch_fp8<32, 2, 64, false>(a, s);
+    if (bm == 32 && nwt == 1 && kc == 128 && geglu) launch_q<32, 1, 128, true, WF_FP8>(a, s);
+    else if (bm == 32 && nwt == 2 && kc == 64 && !geglu) launch_q<32, 2, 64, false, WF_FP8>(a, s);
+    else return -2;
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+  }
+  if (a.w_mx4) {
+    // MXFP4 weights: whole 64-wide superblocks per chunk and per K split,
+    // every group's K offset on a superblock boundary
+    if (a.act_kind != ACT_BF16 || kc % 64 || a.K % 64 || a.k_split % 64 || a.kt_main % 2 || a.kt_alt % 2 ||
+        a.kt_off_alt % 2)
+      return -1;
+    if (bm == 32 && nwt == 1 && kc == 128 && geglu) launch_q<32, 1, 128, true, WF_MX4>(a, s);
+    else if (bm == 32 && nwt == 1 && kc == 64 && geglu) launch_q<32, 1, 64, true, WF_MX4>(a, s);
+    else if (bm == 32 && nwt == 2 && kc == 64 && !geglu) launch_q<32, 2, 64, false, WF_MX4>(a, s);
     else return -2;
     return hipGetLastError() == hipSuccess ? 0 : -5;
   }
@@ -1066,6 +1162,15 @@ int launch_pack_fp8(uint8_t* dst, const uint8_t* src, int64_t rows, int64_t cols
   if (rows % 16 || cols % 32) return -1;
   const int64_t tiles = (rows / 16) * (cols / 32);
   hipLaunchKernelGGL(k_pack_fp8, dim3((unsigned)DG_CEIL_DIV(tiles, 4)), dim3(kThreads), 0, s, dst, src, rows, cols);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+int launch_pack_mxfp4(uint8_t* dst, const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                      hipStream_t s) {
+  if (rows % 16 || cols % 64) return -1;
+  const int64_t sbs = (rows / 16) * (cols / 64);
+  hipLaunchKernelGGL(k_pack_mxfp4, dim3((unsigned)DG_CEIL_DIV(sbs, 4)), dim3(kThreads), 0, s, dst, codes, scales, rows,
+                     cols);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

@@ -15,8 +15,8 @@ import synth
 from synth.configs import ModelShape
 
 from . import (Canvas, KVCache, LayerWeights, ModelConfig, StepParams, Weights, DG_DTYPE_BF16, DG_DTYPE_F32,
-               DG_DTYPE_FP8_E4M3, dg_pack_weight_bf16, dg_pack_weight_bf16_transposed, dg_pack_weight_fp8,
-               dg_workspace_bytes)
+               DG_DTYPE_FP8_E4M3, DG_DTYPE_MXFP4, dg_pack_weight_bf16, dg_pack_weight_bf16_transposed,
+               dg_pack_weight_fp8, dg_pack_weight_mxfp4, dg_workspace_bytes)
 
 
 def stream_handle(stream: torch.cuda.Stream | None = None) -> int:
@@ -24,7 +24,7 @@ def stream_handle(stream: torch.cuda.Stream | None = None) -> int:
     return s.cuda_stream
 
 
-_DTYPE = {"f32": DG_DTYPE_F32, "bf16": DG_DTYPE_BF16, "fp8": DG_DTYPE_FP8_E4M3}
+_DTYPE = {"f32": DG_DTYPE_F32, "bf16": DG_DTYPE_BF16, "fp8": DG_DTYPE_FP8_E4M3, "mxfp4": DG_DTYPE_MXFP4}
 
 
 def model_config(shape: ModelShape) -> ModelConfig:
@@ -68,9 +68,25 @@ class DeviceModel:
             self.tensors[name + "_scale"] = sc
             return t
 
-        def fill(name, tid, rows, cols, groups=1, pack=True, keep_plain=False, fp8=False):
+        def fill4(name, tid, rows, cols, groups=1):
+            # MXFP4: E2M1 codes (one per byte) and E8M0 block scales, packed to
+            # the MXFP4 layout (17 bytes per 32 weights)
+            n = groups * rows * cols
+            codes = tmp.view(torch.uint8)[:n]
+            sc = torch.empty(n // 32, dtype=torch.uint8, device=self.device)
+            synth.dev_mxfp4_rows(codes.data_ptr(), sc.data_ptr(), groups * rows, cols, shape.weight_seed, tid,
+                                 shape.weight_std, st)
+            t = torch.empty(n // 32 * 17, dtype=torch.uint8, device=self.device)
+            dg_pack_weight_mxfp4(t.data_ptr(), codes.data_ptr(), sc.data_ptr(), groups * rows, cols, st)
+            torch.cuda.synchronize()  # sc is freed on return
+            self.tensors[name] = t
+            return t
+
+        def fill(name, tid, rows, cols, groups=1, pack=True, keep_plain=False, fp8=False, mx4=False):
             if fp8:
                 return fill8(name, tid, rows, cols, groups)
+            if mx4:
+                return fill4(name, tid, rows, cols, groups)
             n = groups * rows * cols
             if not self.bf:
                 t = torch.empty(n, dtype=torch.float32, device=self.device)
@@ -117,13 +133,13 @@ class DeviceModel:
             lt["wqkv"] = fill(f"L{l}.wqkv", synth.layer_tid(l, "wqkv"), shape.qkv_rows, d)
             lt["wo"] = fill(f"L{l}.wo", synth.layer_tid(l, "wo"), d, shape.q_dim)
             lt["wr"] = fill(f"L{l}.wr", synth.layer_tid(l, "wr"), E, d)
-            x8 = shape.expert_dtype == "fp8"
-            lt["sh_g"] = fill(f"L{l}.sh_g", synth.layer_tid(l, "sh_g"), shape.d_shared, d, fp8=x8)
-            lt["sh_u"] = fill(f"L{l}.sh_u", synth.layer_tid(l, "sh_u"), shape.d_shared, d, fp8=x8)
-            lt["sh_d"] = fill(f"L{l}.sh_d", synth.layer_tid(l, "sh_d"), d, shape.d_shared, fp8=x8)
-            lt["ex_g"] = fill(f"L{l}.ex_g", synth.layer_tid(l, "ex_g"), shape.d_expert, d, groups=E, fp8=x8)
-            lt["ex_u"] = fill(f"L{l}.ex_u", synth.layer_tid(l, "ex_u"), shape.d_expert, d, groups=E, fp8=x8)
-            lt["ex_d"] = fill(f"L{l}.ex_d", synth.layer_tid(l, "ex_d"), d, shape.d_expert, groups=E, fp8=x8)
+            x8, x4 = shape.expert_dtype == "fp8", shape.expert_dtype == "mxfp4"
+            lt["sh_g"] = fill(f"L{l}.sh_g", synth.layer_tid(l, "sh_g"), shape.d_shared, d, fp8=x8, mx4=x4)
+            lt["sh_u"] = fill(f"L{l}.sh_u", synth.layer_tid(l, "sh_u"), shape.d_shared, d, fp8=x8, mx4=x4)
+            lt["sh_d"] = fill(f"L{l}.sh_d", synth.layer_tid(l, "sh_d"), d, shape.d_shared, fp8=x8, mx4=x4)
+            lt["ex_g"] = fill(f"L{l}.ex_g", synth.layer_tid(l, "ex_g"), shape.d_expert, d, groups=E, fp8=x8, mx4=x4)
+            lt["ex_u"] = fill(f"L{l}.ex_u", synth.layer_tid(l, "ex_u"), shape.d_expert, d, groups=E, fp8=x8, mx4=x4)
+            lt["ex_d"] = fill(f"L{l}.ex_d", synth.layer_tid(l, "ex_d"), d, shape.d_expert, groups=E, fp8=x8, mx4=x4)
             ls = self.layer_structs[l]
             for k, v in lt.items():
                 setattr(ls, k, v.data_ptr())

@@ -50,6 +50,7 @@ extern "C" {
 #define DG_DTYPE_F32 0
 #define DG_DTYPE_BF16 1
 #define DG_DTYPE_FP8_E4M3 2 /* weights only: OCP E4M3 codes with per-output-feature fp32 scales */
+#define DG_DTYPE_MXFP4 3     /* expert weights only: OCP MXFP4 (E2M1 codes, an E8M0 scale per 32 inputs) */
 
 /* canvas.flags bits (device side) */
 #define DG_FLAG_NONFINITE 1u /* some entropy of the step was NaN or infinite */
@@ -66,7 +67,15 @@ extern "C" {
  * is then an OCP E4M3 code whose value, times the fp32 scale of its output
  * feature, is the weight (dequantised exactly to bf16 inside the kernels,
  * bf16 MFMA, the scale applied to the fp32 sum); fp8 experts need
- * d_model % 128 == 0.  Otherwise DG_ERR_UNSUPPORTED. */
+ * d_model % 128 == 0.  expert_dtype may also be DG_DTYPE_MXFP4 in a bf16
+ * model (OCP Microscaling Formats v1.0, MXFP4: along each matrix row, every
+ * block of 32 consecutive inputs shares one E8M0 scale 2^(e - 127) and each
+ * weight is that scale times an FP4 E2M1 element, 0, +-0.5, +-1, +-1.5, +-2,
+ * +-3, +-4, +-6): the kernels convert each element times its block scale to
+ * bf16, which is exact for scale codes 1..254 (code 0 is read as zero, code
+ * 255, NaN, is not a valid input), and feed the bf16 MFMA; MXFP4 experts need
+ * d_model, d_expert and d_shared multiples of 64.  Otherwise
+ * DG_ERR_UNSUPPORTED. */
 typedef struct dg_model_config {
   int32_t n_layers, d_model, n_q_heads, n_kv_heads, d_head;
   int32_t n_experts, top_k, d_expert, d_shared, vocab, d_selfcond;
@@ -88,7 +97,8 @@ typedef struct dg_model_config {
  * fp8 experts: per-output-feature fp32 scales ex_g_scale, ex_u_scale
  * [n_experts][d_expert], ex_d_scale [n_experts][d_model], sh_g_scale,
  * sh_u_scale [d_shared], sh_d_scale [d_model] (16-byte aligned); NULL
- * otherwise. */
+ * otherwise.  MXFP4 experts: every expert matrix in the MXFP4 layout of
+ * dg_pack_weight_mxfp4 (its block scales inside), the *_scale pointers NULL. */
 typedef struct dg_layer_weights {
   const void* wqkv;
   const void* wo;
@@ -211,6 +221,21 @@ int dg_pack_weight_bf16_transposed(void* d_dst, const void* d_src, int64_t rows,
  * (r/16, c/32) at byte ((r/16)*(cols/32) + c/32)*512, code (r, c) inside it
  * at (((c%32)/8)*16 + r%16)*8 + c%8.  rows % 16 == 0, cols % 32 == 0. */
 int dg_pack_weight_fp8(void* d_dst, const void* d_src, int64_t rows, int64_t cols, void* stream);
+
+/* Pack an MXFP4 matrix [rows][cols] into the MXFP4 weight layout.  Inputs
+ * (device): d_codes, one E2M1 element code per byte (low 4 bits; OCP MX v1.0
+ * FP4 encoding S.EE.M), row-major [rows][cols]; d_scales, the E8M0 scale code
+ * of each block of 32 consecutive columns, row-major [rows][cols / 32].
+ * Output: superblocks of 16 rows x 64 columns, 544 B each, superblock
+ * (r/16, c/64) at byte ((r/16)*(cols/64) + c/64)*544.  Inside one: byte
+ * 8l + 4h + q (l = 0..63, h = 0..1, q = 0..3) holds the codes of row r%16 = l%16,
+ * columns c%64 = 32h + 8(l/16) + 2q (low nibble) and + 1 (high nibble), i.e.
+ * lane l's MFMA A-operand elements of the two 32-column halves; byte
+ * 512 + 2(r%16) + h holds the scale code of row r, block (c/32) of half h.
+ * Total size rows*cols*17/32 bytes.  rows % 16 == 0, cols % 64 == 0; the
+ * buffers must not overlap. */
+int dg_pack_weight_mxfp4(void* d_dst, const void* d_codes, const void* d_scales, int64_t rows, int64_t cols,
+                         void* stream);
 
 /* Fill canvas->tokens with uniform noise for `block` (Philox stream 0).
  * (euno.news, "what DiffusionGemma does": a canvas starts as random tokens;

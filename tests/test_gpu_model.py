@@ -11,8 +11,9 @@ from dataclasses import replace
 
 from synth.configs import MINI_BF16, TINY, WORKLOADS
 
-# the small bf16 shape with fp8 expert and LM-head weights
+# the small bf16 shape with fp8 expert and LM-head weights, and with MXFP4 experts
 MINI_FP8 = replace(MINI_BF16, expert_dtype="fp8", lm_dtype="fp8")
+MINI_MX4 = replace(MINI_BF16, expert_dtype="mxfp4")
 
 from .gpu_util import allclose_report, bar_or_twin, bar_then_twin, compare_decisions, compare_step_decisions, say
 
@@ -109,6 +110,13 @@ def mini(env):
 @pytest.fixture(scope="module")
 def mini8(env):
     pb = Problem(env, MINI_FP8, 6.0, 40, 48, B=2, cap_extra=48)
+    pb.encode_prefix()
+    return pb
+
+
+@pytest.fixture(scope="module")
+def mini4(env):
+    pb = Problem(env, MINI_MX4, 6.0, 40, 48, B=2, cap_extra=48)
     pb.encode_prefix()
     return pb
 
@@ -221,14 +229,14 @@ def _forced_ids(trace):
     return np.stack(trace["expert_ids"])  # [layers][T][k]
 
 
-@pytest.mark.parametrize("which", ["tiny", "mini", "mini8"])
+@pytest.mark.parametrize("which", ["tiny", "mini", "mini8", "mini4"])
 def test_encode_cache_matches_oracle(which, request):
     pb = request.getfixturevalue(which)
     pb.compare_cache(pb.prefix)
     pb.check_guards()
 
 
-@pytest.mark.parametrize("which", ["tiny", "mini", "mini8"])
+@pytest.mark.parametrize("which", ["tiny", "mini", "mini8", "mini4"])
 def test_forward_logits_match_oracle(which, request):
     pb = request.getfixturevalue(which)
     torch, dg, rt = pb.env
@@ -280,7 +288,7 @@ def test_forward_logits_match_oracle(which, request):
     pb.check_guards()
 
 
-@pytest.mark.parametrize("which", ["tiny", "mini", "mini8"])
+@pytest.mark.parametrize("which", ["tiny", "mini", "mini8", "mini4"])
 def test_denoise_loop_and_commit_match_oracle(which, request):
     """48 adaptive steps on the GPU.  Every step is checked against the
     sampler's definition (check_sampler_invariants).  The oracle runs the same
@@ -368,7 +376,7 @@ def test_denoise_loop_and_commit_match_oracle(which, request):
     pb.check_guards()
 
 
-@pytest.mark.parametrize("which", ["tiny", "mini", "mini8"])
+@pytest.mark.parametrize("which", ["tiny", "mini", "mini8", "mini4"])
 def test_forced_route_loop_matches_oracle(which, request):
     """Every step of a 12-step schedule compared with the oracle on the
     oracle's routes (dg_test_denoise_step: the product's whole step with
@@ -453,7 +461,7 @@ def _f32_twin_on_inputs(pb, tok, sc, expert_ids):
         om.route = orig
 
 
-@pytest.mark.parametrize("which", ["mini", "mini8"])
+@pytest.mark.parametrize("which", ["mini", "mini8", "mini4"])
 def test_skewed_routing_matches_oracle(which, request):
     """Every token of every layer routed to the same k experts (in one order):
     those experts' segments span several row tiles, the others receive no
@@ -547,7 +555,7 @@ def test_denoise_step_is_deterministic(mini):
 AR_FLIP = {"f32": 1e-5, "bf16": 1e-2}
 
 
-@pytest.mark.parametrize("which", ["tiny", "mini", "mini8", "mini_long"])
+@pytest.mark.parametrize("which", ["tiny", "mini", "mini8", "mini4", "mini_long"])
 def test_ar_decode_matches_oracle(env, which):
     """Greedy single-token decode on the same weights: every step's logits,
     next token and appended K/V rows against the oracle's, teacher-forced with
@@ -561,6 +569,7 @@ def test_ar_decode_matches_oracle(env, which):
         "tiny": (WORKLOADS["tiny"].model, WORKLOADS["tiny"].lm_scale, 24, 1),
         "mini": (MINI_BF16, 6.0, 40, 2),
         "mini8": (MINI_FP8, 6.0, 40, 2),
+        "mini4": (MINI_MX4, 6.0, 40, 2),
         "mini_long": (MINI_BF16, 6.0, 4096, 1),
     }[which]
     n_dec = 8
@@ -773,7 +782,7 @@ def test_many_canvases_match_oracle(env, B):
     pb.check_guards()
 
 
-@pytest.mark.parametrize("which", ["tiny", "mini", "mini8"])
+@pytest.mark.parametrize("which", ["tiny", "mini", "mini8", "mini4"])
 def test_commit_and_step_matches_oracle(env, which):
     """dg_commit_and_step (commit of one block and the next block's first
     step in one pass) against the oracle's commit and step: the appended K/V
@@ -785,6 +794,7 @@ def test_commit_and_step_matches_oracle(env, which):
         "tiny": (WORKLOADS["tiny"].model, WORKLOADS["tiny"].lm_scale, 24, 32, 1),
         "mini": (MINI_BF16, 6.0, 40, 48, 2),
         "mini8": (MINI_FP8, 6.0, 40, 48, 2),
+        "mini4": (MINI_MX4, 6.0, 40, 48, 2),
     }[which]
     pb = Problem(env, shape, lm_scale, prefix, C, B=B, cap_extra=C + (-(prefix + 2 * C)) % 8)
     pb.encode_prefix()
