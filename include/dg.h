@@ -68,7 +68,9 @@ extern "C" {
  * feature, is the weight (dequantised exactly to bf16 inside the kernels,
  * bf16 MFMA, the scale applied to the fp32 sum); fp8 experts need
  * d_model % 128 == 0.  expert_dtype may also be DG_DTYPE_MXFP4 in a bf16
- * model (OCP Microscaling Formats v1.0, MXFP4: along each matrix row, every
+ * model (4-bit expert weights, the counterpart of the NVFP4 kernels of
+ * euno.news, "how it was built"; the format is OCP Microscaling Formats
+ * v1.0, MXFP4: along each matrix row, every
  * block of 32 consecutive inputs shares one E8M0 scale 2^(e - 127) and each
  * weight is that scale times an FP4 E2M1 element, 0, +-0.5, +-1, +-1.5, +-2,
  * +-3, +-4, +-6): the kernels convert each element times its block scale to
