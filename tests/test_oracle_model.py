@@ -266,3 +266,37 @@ def test_synth_c_matches_numpy_definition():
     assert abs(x.std() - 0.02) < 2e-4 and abs(x.mean()) < 1e-4
     d = synth.dirichlet_rows(0, 7, 2, 4096, 0.05)
     assert np.allclose(d.sum(1), 1.0, atol=1e-5) and (d >= 0).all()
+
+
+def test_resume_from_saved_state_is_identical():
+    """Resume invariant of the oracle's step: the state after step t (canvas
+    tokens, the tempered distribution carried as self-conditioning input, the
+    previous argmax, the cache) copied and continued from gives exactly the
+    uninterrupted run's outputs."""
+    import copy
+    from oracle import sampler as smp
+    from oracle import step as ost
+    from synth.configs import TINY
+    shape, C, L, N = TINY, 16, 24, 6
+    W = om.Weights(shape)
+    cache = om.KVCache(shape, 1, L + C)
+    prompt = synth.tokens(0, synth.TID["prompt"], L, shape.vocab)[None]
+    ost.encode_append(shape, W, cache, prompt)
+    tok = smp.initial_canvas(5, 0, C, shape.vocab)[None]
+
+    def run(tok, sc, prev, cache, ts):
+        outs = []
+        for t in ts:
+            _, o = ost.denoise_step(shape, W, cache, tok, sc, t, N, [5], 0, 8.0, prev, True)
+            o = o[0]
+            outs.append(o)
+            tok, sc, prev = o["next_tokens"][None], o["p"][None], o["argmax"][None]
+        return outs, (tok, sc, prev)
+
+    full, _ = run(tok, None, None, cache, range(4))
+    first, state = run(tok, None, None, cache, range(2))
+    saved = copy.deepcopy((state, cache))
+    rest, _ = run(*saved[0], saved[1], range(2, 4))
+    for a, b in zip(full[2:], rest):
+        for key in ("H", "sample", "argmax", "accepted", "next_tokens", "p"):
+            assert np.array_equal(a[key], b[key]), key
