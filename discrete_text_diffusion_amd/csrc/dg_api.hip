@@ -427,6 +427,7 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
                                c.at<int32_t>(c.p.n_tiles), c.at<int32_t>(c.p.rcnt), c.st));
     }
     const int max_tiles = T * s.k / bm + s.E + s.n_sh * ((T + bm - 1) / bm);
+    if (max_tiles >= 65536) return DG_ERR_UNSUPPORTED;  // tile spans hold 16-bit indices
     // experts + shared slices: gate/up with GeGLU
     {
       Phase ph(c, DG_PHASE_MOE_UP);
@@ -449,8 +450,11 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
       a.w_mx4 = s.ex4;
       if (bf) {
         a.n_fb = (s.de + 63) / 64;
-        a.tile_fastest = 1;  // the row tiles of one (expert, feature block) run together (same XCD): a hot
-                             // expert's weight slice comes from HBM once and from L2 for its other tiles
+        // expert by expert, the row tiles of one (expert, feature block)
+        // together (same XCD): a hot expert's weight slice comes from HBM
+        // once and from L2 for its other tiles, and a tile's activation rows
+        // are read again one expert's tile count later, still in L2
+        a.group_major = 1;
         const int kc = bm == 128 ? 64 : s.d % 128 == 0 ? 128 : 64;
         const int64_t rows_moe = (int64_t)T * (s.k + s.n_sh);
         // Fewer (token, slot) pairs than experts (the decode step): a dozen
@@ -497,8 +501,7 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
         // 16-feature tile per wave, twice the workgroups for the few row tiles
         const int nwt = (!s.ex8 && !s.ex4 && (int64_t)T * s.k < s.E) ? 1 : 2;
         a.n_fb = (s.d + 64 * nwt - 1) / (64 * nwt);
-        a.tile_fastest = 1;  // the row tiles of one (expert, feature block) run together (same XCD): a hot
-                             // expert's weight slice comes from HBM once and from L2 for its other tiles
+        a.group_major = 1;  // expert by expert, as the gate/up launch
         DG_TRY(launch_wsgemm(a, bm, nwt, 64, false, c.st));
       } else {
         DG_TRY(launch_gemm_simple(a, c.st));

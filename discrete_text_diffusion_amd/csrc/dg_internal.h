@@ -6,9 +6,11 @@
 
 // One row tile of a (possibly grouped) GEMM: rows [row0, row0 + nrows) of the
 // output, all belonging to weight group `group` (an expert, or one of the
-// shared expert's virtual slices).
+// shared expert's virtual slices).  span: (index of the group's first tile in
+// the list << 16) | the group's tile count (tile lists hold fewer than 65536
+// tiles, a group fewer than 65536).
 struct GemmTile {
-  int32_t group, row0, nrows, pad;
+  int32_t group, row0, nrows, span;
 };
 
 enum GemmEpi : int32_t {
@@ -82,6 +84,7 @@ struct GemmArgs {
   int32_t n_split;   // K splits
   int32_t k_split;   // K per split (multiple of the K chunk)
   int32_t tile_fastest;
+  int32_t group_major;  // grouped GEMMs: blocks ordered (group, feature block, tile of the group)
   int32_t nblocks;   // launched blocks (multiple of 8)
   // epilogue
   int32_t epi;

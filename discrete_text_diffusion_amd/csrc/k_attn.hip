@@ -64,8 +64,10 @@ constexpr int ATT_DMA = (ATT_STAGE / 1024) / ATT_WAVES;  // 1 KiB instructions p
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // K tile: key row r at r * 512 B; 16-byte group c (dims 8c..8c+7) at physical
-// group c ^ fk(r).  fk separates the 8 rows any 8 lanes read together.
-__device__ __forceinline__ int att_fk(int r) { return (r & 3) | (((r >> 3) & 1) << 2); }
+// group c ^ fk(r).  The rows sit 512 B apart, all on the same LDS banks, so
+// fk alone spreads a read: the 16 lanes a 16-byte read serves at a time
+// (gfx950's 64 banks) read 16 rows with 16 distinct fk values.
+__device__ __forceinline__ int att_fk(int r) { return (r & 3) | (((r >> 3) & 3) << 2); }
 // S^T MFMA (step kk, half hf): row i <-> key 32 kk + 8 (i / 4) + 4 hf + i % 4,
 // so lane group g of the output holds keys 32 kk + 8 g + 4 hf + e.
 __device__ __forceinline__ int att_krow(int kk, int hf, int i) { return 32 * kk + 8 * (i >> 2) + 4 * hf + (i & 3); }

@@ -36,33 +36,46 @@ __device__ __forceinline__ int xcd_logical_block(int nblocks) {
   return (hw & 7) * per + (hw >> 3);
 }
 
-__device__ __forceinline__ void decode_block(const GemmArgs& a, int lb, int ntiles, int& tile, int& fb, int& ks) {
-  // order: split outermost, then (tile, fb) with the chosen one fastest
-  const int per_split = ntiles * a.n_fb;
-  ks = lb / per_split;
-  const int r = lb - ks * per_split;
-  // (selects of values: a select between the two references made the
-  // compiler round-trip them through scratch memory)
-  const int fast = a.tile_fastest ? ntiles : a.n_fb;
-  const int lo = r % fast, hi = r / fast;
-  tile = a.tile_fastest ? lo : hi;
-  fb = a.tile_fastest ? hi : lo;
-}
-
-// The workgroup's (tile, feature block, split), or false if it has none.
-// The grid covers max_tiles row tiles; a grouped GEMM's tile list holds only
-// *n_tiles_dev of them, known on the device.  The valid workgroups are dealt
-// to the 8 XCDs in equal contiguous shares (hardware block b runs on XCD
-// b % 8), so every XCD gets the same amount of work and neighbouring
-// logical blocks (data they share) stay on one XCD.
-__device__ __forceinline__ bool block_work(const GemmArgs& a, int& ntiles, int& tile, int& fb, int& ks) {
-  ntiles = a.tiles ? *a.n_tiles_dev : a.max_tiles;
+// The workgroup's (row tile, feature block, split), or false if it has
+// none.  The grid covers max_tiles row tiles; a grouped GEMM's tile list
+// holds only *n_tiles_dev of them, known on the device.  The valid workgroups
+// are dealt to the 8 XCDs in equal contiguous shares (hardware block b runs on
+// XCD b % 8), so every XCD gets the same amount of work and neighbouring
+// logical blocks (data they share) stay on one XCD.  Inside a share the split
+// is outermost, then
+//  * group_major (grouped GEMMs): group by group (a group's tiles are
+//    contiguous in the list), feature block by feature block inside a group,
+//    the group's row tiles fastest.  Group g owns blocks
+//    [n_fb first_g, n_fb (first_g + count_g)), so tile r / n_fb of block r is
+//    one of g's and carries g's span;
+//  * otherwise (tile, feature block) with the one tile_fastest names fastest.
+template <int BM>
+__device__ __forceinline__ bool block_work(const GemmArgs& a, GemmTile& td, int& fb, int& ks) {
+  const int ntiles = a.tiles ? *a.n_tiles_dev : a.max_tiles;
   const int valid = a.n_split * ntiles * a.n_fb;
   const int share = (valid + 7) >> 3;
   const int i = blockIdx.x >> 3;
   const int lb = (blockIdx.x & 7) * share + i;
   if (i >= share || lb >= valid) return false;
-  decode_block(a, lb, ntiles, tile, fb, ks);
+  const int per_split = ntiles * a.n_fb;
+  ks = lb / per_split;
+  const int r = lb - ks * per_split;
+  if (a.group_major) {
+    td = a.tiles[r / a.n_fb];
+    const int first = (int)((uint32_t)td.span >> 16), count = td.span & 0xffff;
+    const int local = r - a.n_fb * first;
+    fb = local / count;
+    if (count > 1) td = a.tiles[first + (local - fb * count)];
+    return true;
+  }
+  // (selects of values: a select between the two references made the
+  // compiler round-trip them through scratch memory)
+  const int fast = a.tile_fastest ? ntiles : a.n_fb;
+  const int lo = r % fast, hi = r / fast;
+  const int tile = a.tile_fastest ? lo : hi;
+  fb = a.tile_fastest ? hi : lo;
+  if (a.tiles) td = a.tiles[tile];
+  else td = GemmTile{0, tile * BM, min(BM, a.M - tile * BM), 0};
   return true;
 }
 
@@ -457,11 +470,9 @@ __global__ __launch_bounds__(kThreads, BM <= 32 ? 4 : 1) void k_wsgemm(GemmArgs 
   constexpr int LD = KC + 8;
   __shared__ __attribute__((aligned(16))) bf16_t xs[2 * BM * LD];
 
-  int ntiles, tile, fb, ks;
-  if (!block_work(a, ntiles, tile, fb, ks)) return;
   GemmTile td;
-  if (a.tiles) td = a.tiles[tile];
-  else td = GemmTile{0, tile * BM, min(BM, a.M - tile * BM), 0};
+  int fb, ks;
+  if (!block_work<BM>(a, td, fb, ks)) return;
   if (td.nrows <= 0) return;
 
   f32x4_t acc[NWT][MW], accu[NWT][MW];

@@ -192,12 +192,13 @@ __global__ __launch_bounds__(1024) void k_route_sort(const int32_t* ids, int T, 
   }
   for (int e = tid; e < E; e += nt) {
     const int base = off[e], n = cnt[e];
-    for (int i = 0, j = toff[e]; i * bm < n; ++i, ++j) tiles[j] = GemmTile{e, base + i * bm, min(bm, n - i * bm), 0};
+    const int span = (toff[e] << 16) | (toff[e + 1] - toff[e]);
+    for (int i = 0, j = toff[e]; i * bm < n; ++i, ++j) tiles[j] = GemmTile{e, base + i * bm, min(bm, n - i * bm), span};
   }
   const int per_sh = (T + bm - 1) / bm;
   for (int i = tid; i < n_sh * per_sh; i += nt) {
     const int c = i / per_sh, q = i - c * per_sh;
-    tiles[toff[E] + i] = GemmTile{E + c, npairs + c * T + q * bm, min(bm, T - q * bm), 0};
+    tiles[toff[E] + i] = GemmTile{E + c, npairs + c * T + q * bm, min(bm, T - q * bm), ((toff[E] + c * per_sh) << 16) | per_sh};
   }
   for (int i = tid; i < n_sh * T; i += nt) row_token[npairs + i] = i % T;
 }
@@ -276,12 +277,13 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* ccnt, int nchunks,
   for (int i = tid; i < nchunks * E; i += nt) ccnt[i] += off[i % E];  // absolute first row of (chunk, expert)
   for (int e = tid; e < E; e += nt) {
     const int base = off[e], n = cnt[e];
-    for (int i = 0, j = toff[e]; i * bm < n; ++i, ++j) tiles[j] = GemmTile{e, base + i * bm, min(bm, n - i * bm), 0};
+    const int span = (toff[e] << 16) | (toff[e + 1] - toff[e]);
+    for (int i = 0, j = toff[e]; i * bm < n; ++i, ++j) tiles[j] = GemmTile{e, base + i * bm, min(bm, n - i * bm), span};
   }
   const int per_sh = (T + bm - 1) / bm;
   for (int i = tid; i < n_sh * per_sh; i += nt) {
     const int c = i / per_sh, q = i - c * per_sh;
-    tiles[toff[E] + i] = GemmTile{E + c, npairs + c * T + q * bm, min(bm, T - q * bm), 0};
+    tiles[toff[E] + i] = GemmTile{E + c, npairs + c * T + q * bm, min(bm, T - q * bm), ((toff[E] + c * per_sh) << 16) | per_sh};
   }
 }
 
