@@ -93,7 +93,7 @@ struct Plan {
   int g_rows;   // rows (x the widest N) of the split-epilogue partial buffer
   int64_t o_rows;  // rows (x d_model) of the O-projection K-split partials
   size_t x, n, q, o, att_o, att_ml, o_part, r_part, ids, wts, row_token, inv, offsets, tiles,
-      n_tiles, h, Y, lm_f, lm_i, logits, e_part, ebar, hsc, g_part, rcnt, total;
+      n_tiles, h, Y, lm_f, lm_i, logits, e_part, ebar, hsc, g_part, rcnt, rope, total;
 };
 
 // step_only: a plan for denoising steps alone (no encode passes), whose
@@ -141,6 +141,7 @@ Plan make_plan(const Shape& s, int batch, int max_canvas, bool step_only = false
   p.g_rows = std::max(kRowPartRows, std::max(p.T, p.Tdn));
   p.g_part = take((size_t)p.g_rows * std::max(s.qkv, s.dsc) * 4);
   p.rcnt = take((size_t)std::max(1, route_chunk_words((int)T)) * 4);     // routing sort, per-chunk counts
+  p.rope = take(T * (s.dh / 2) * sizeof(float2));                         // RoPE (cos, sin) per row and pair
   p.total = off;
   return p;
 }
@@ -346,6 +347,10 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
   const int64_t layer_elems = (int64_t)cache->batch * s.nkv * cache->capacity * s.dh;
   const int64_t c_seq = (int64_t)s.nkv * cache->capacity * s.dh, c_head = (int64_t)cache->capacity * s.dh;
   void* xn = c.at<void>(c.p.n);
+  // RoPE rotations of this call's positions, formed once for every layer
+  for (int seg = 0; seg < n_segs; ++seg)
+    DG_TRY(launch_rope_table(c.at<float2>(c.p.rope) + (size_t)seg * seq_len * (s.dh / 2), seq_len, s.dh,
+                             L + seg * seq_len, s.rope_base, c.st));
   for (int l = 0; l < s.L; ++l) {
     const dg_layer_weights& lw = c.w->layers[l];
     if (c.teacher_x)  // test path: this layer starts from the given residual
@@ -368,6 +373,7 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
       q.k = kc; q.v = vc; q.kv_b_stride = c_seq; q.kv_h_stride = c_head; q.kv_row0 = L + seg * seq_len;
       q.v_pitch = cache->capacity;
       q.seq_len = seq_len; q.pos0 = L + seg * seq_len; q.rope_base = s.rope_base;
+      q.rope = c.at<float2>(c.p.rope) + (size_t)seg * seq_len * (s.dh / 2);
       DG_TRY(dense_gemm(c, a, Tseg, s.qkv, s.d, 1));
     }
     // The causal encode keeps only the K/V rows it appends: past the last

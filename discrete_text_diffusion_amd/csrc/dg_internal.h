@@ -41,6 +41,7 @@ struct QkvEpi {
   int32_t seq_len;      // tokens per sequence in this call
   int32_t pos0;         // absolute position of the first token of each sequence
   float rope_base;
+  const float2* rope;   // [seq_len][d_head / 2] RoPE (cos, sin) of positions pos0 + i (launch_rope_table)
 };
 
 struct GemmArgs {
@@ -112,6 +113,9 @@ struct LmArgs {
 
 // Launchers
 // k_gemm.hip
+// RoPE (cos, sin) of pairs j < d_head / 2 at positions pos0 + i, i < rows:
+// out[i][j], the angle formed in fp64 (every layer's QKV epilogue reads it).
+int launch_rope_table(float2* out, int rows, int d_head, int pos0, float rope_base, hipStream_t s);
 int launch_wsgemm(const GemmArgs& a, int bm, int nwt, int kc, bool geglu, hipStream_t s);
 // Row-resident GEMM (M rows in groups of 256, 256-feature blocks; 128 with
 // scaled activations, whose K and k_split are multiples of 256): fp32

@@ -131,17 +131,12 @@ __device__ __forceinline__ void epi_pair(const GemmArgs& a, int ks, int orow, in
       const int i = orow - seq * q.seq_len;
       float v0 = g0, v1 = g1;
       if (n < q.q_dim + q.kv_dim) {
-        // RoPE on (2j, 2j+1) of the head at absolute position pos0 + i; the
-        // angle is formed in fp64 so long positions keep full accuracy.
-        const int dd = n % q.d_head;
-        const int j = dd >> 1;
-        const double inv_freq = exp2(-(2.0 * j / q.d_head) * log2((double)q.rope_base));
-        const double ang = (double)(q.pos0 + i) * inv_freq;
-        double sd, cd;
-        sincos(ang, &sd, &cd);
-        const float c = (float)cd, s = (float)sd;
-        v0 = g0 * c - g1 * s;
-        v1 = g0 * s + g1 * c;
+        // RoPE on (2j, 2j+1) of the head at absolute position pos0 + i, the
+        // rotation read from the call's table (rope_cs)
+        const int j = (n % q.d_head) >> 1;
+        const float2 cs = q.rope[(int64_t)i * (q.d_head >> 1) + j];
+        v0 = g0 * cs.x - g1 * cs.y;
+        v1 = g0 * cs.y + g1 * cs.x;
       }
       if (n < q.q_dim) {
         store_act2<TA>(q.q, (int64_t)orow * q.q_dim + n, v0, v1);
@@ -163,6 +158,17 @@ __device__ __forceinline__ void epi_pair(const GemmArgs& a, int ks, int orow, in
     default:
       break;
   }
+}
+
+// RoPE rotation of pair j of a d_head-wide head at position pos: angle
+// pos * base^(-2j / d_head), formed in fp64 so long positions keep full
+// accuracy, (cos, sin) rounded to fp32.
+__device__ __forceinline__ float2 rope_cs(int pos, int j, int d_head, float base) {
+  const double inv_freq = exp2(-(2.0 * j / d_head) * log2((double)base));
+  const double ang = (double)pos * inv_freq;
+  double sd, cd;
+  sincos(ang, &sd, &cd);
+  return make_float2((float)cd, (float)sd);
 }
 
 __device__ __forceinline__ uint4 pack8_bf16(const float* f) {
@@ -1156,6 +1162,22 @@ int launch_wsgemm(const GemmArgs& a, int bm, int nwt, int kc, bool geglu, hipStr
   DG_CASE(256, 2, 64, false)
 #undef DG_CASE
   return -2;
+}
+
+__global__ __launch_bounds__(kThreads) void k_rope_table(float2* out, int64_t n, int half, int pos0, int d_head,
+                                                        float base) {
+  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (t >= n) return;
+  const int i = (int)(t / half), j = (int)(t - (int64_t)i * half);
+  out[t] = rope_cs(pos0 + i, j, d_head, base);
+}
+
+int launch_rope_table(float2* out, int rows, int d_head, int pos0, float rope_base, hipStream_t s) {
+  if (rows < 1 || d_head < 2 || d_head % 2) return -1;
+  const int64_t n = (int64_t)rows * (d_head / 2);
+  hipLaunchKernelGGL(k_rope_table, dim3((unsigned)DG_CEIL_DIV(n, kThreads)), dim3(kThreads), 0, s, out, n, d_head / 2,
+                     pos0, d_head, rope_base);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
 int launch_gemm_simple(const GemmArgs& a, hipStream_t s) {
