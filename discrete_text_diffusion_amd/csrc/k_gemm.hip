@@ -1156,10 +1156,8 @@ int launch_wsgemm(const GemmArgs& a, int bm, int nwt, int kc, bool geglu, hipStr
   DG_CASE(32, 1, 64, false)
   DG_CASE(32, 1, 128, false)
   DG_CASE(64, 1, 128, false)
-  DG_CASE(32, 2, 128, false)
   DG_CASE(64, 2, 64, false)
   DG_CASE(128, 2, 64, false)
-  DG_CASE(256, 2, 64, false)
 #undef DG_CASE
   return -2;
 }
