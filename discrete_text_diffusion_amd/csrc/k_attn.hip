@@ -328,27 +328,19 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   // the sums run in split order whatever the pass size
   constexpr int kS = 16;
   const int64_t sstride = T * a.n_q;
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < a.n_split; s0 += kS) {
-    float mx[kS];
-#pragma unroll
-    for (int j = 0; j < kS; ++j) mx[j] = s0 + j < a.n_split ? a.part_ml[(s0 + j) * sstride + row].x : -INFINITY;
-#pragma unroll
-    for (int j = 0; j < kS; ++j) M = fmaxf(M, mx[j]);
-  }
-  const float sh = M == -INFINITY ? 0.f : M;
-  float L = 0.f;
+  float M = -INFINITY, L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < a.n_split; s0 += kS) {
-    float2 ml[kS];
-    float4 v[kS];
+  auto load_pass = [&](int s0, float2 (&ml)[kS], float4 (&v)[kS], bool with_o) {
 #pragma unroll
     for (int j = 0; j < kS; ++j) {
       const int64_t pr = (s0 + j) * sstride + row;
       ml[j] = s0 + j < a.n_split ? a.part_ml[pr] : make_float2(-INFINITY, 0.f);
-      v[j] = s0 + j < a.n_split ? *reinterpret_cast<const float4*>(a.part_o + pr * a.d + 4 * lane)
-                                : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (with_o)
+        v[j] = s0 + j < a.n_split ? *reinterpret_cast<const float4*>(a.part_o + pr * a.d + 4 * lane)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+  };
+  auto add_pass = [&](const float2 (&ml)[kS], const float4 (&v)[kS], float sh) {
     float w[kS];
 #pragma unroll
     for (int j = 0; j < kS; ++j) {
@@ -362,13 +354,39 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
       acc.z += w[j] * v[j].z;
       acc.w += w[j] * v[j].w;
     }
+  };
+  float2 ml[kS];
+  float4 v[kS];
+  if (a.n_split <= kS) {
+    // one pass: the row maxima and the partials are in flight together
+    load_pass(0, ml, v, true);
+#pragma unroll
+    for (int j = 0; j < kS; ++j) M = fmaxf(M, ml[j].x);
+    add_pass(ml, v, M == -INFINITY ? 0.f : M);
+  } else {
+    for (int s0 = 0; s0 < a.n_split; s0 += kS) {
+      load_pass(s0, ml, v, false);
+#pragma unroll
+      for (int j = 0; j < kS; ++j) M = fmaxf(M, ml[j].x);
+    }
+    const float sh = M == -INFINITY ? 0.f : M;
+    for (int s0 = 0; s0 < a.n_split; s0 += kS) {
+      load_pass(s0, ml, v, true);
+      add_pass(ml, v, sh);
+    }
   }
   const float inv_l = L > 0.f ? 1.f / L : 0.f;
   TA* o = reinterpret_cast<TA*>(a.out) + row * a.d + 4 * lane;
-  o[0] = to_act<TA>(acc.x * inv_l);
-  o[1] = to_act<TA>(acc.y * inv_l);
-  o[2] = to_act<TA>(acc.z * inv_l);
-  o[3] = to_act<TA>(acc.w * inv_l);
+  if constexpr (sizeof(TA) == 2) {  // the lane's four bf16 values in one 8-byte store
+    const uint32_t lo = (uint32_t)to_act<TA>(acc.x * inv_l) | ((uint32_t)to_act<TA>(acc.y * inv_l) << 16);
+    const uint32_t hi = (uint32_t)to_act<TA>(acc.z * inv_l) | ((uint32_t)to_act<TA>(acc.w * inv_l) << 16);
+    *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
+  } else {
+    o[0] = to_act<TA>(acc.x * inv_l);
+    o[1] = to_act<TA>(acc.y * inv_l);
+    o[2] = to_act<TA>(acc.z * inv_l);
+    o[3] = to_act<TA>(acc.w * inv_l);
+  }
 }
 
 // Plain path (fp32 models, any d_head <= 256): one wave per (token, head),
