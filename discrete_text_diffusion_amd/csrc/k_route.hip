@@ -11,16 +11,39 @@
 namespace {
 
 // One wave per token.  Router logits arrive as `n_split` fp32 partial sums
-// [split][T][E] added in split order.  Selection by rank: the wave's E logits
-// go to LDS and every lane counts, for each logit it holds, the logits that
-// beat it (larger, or equal with a lower expert id); rank < k is selected at
-// that rank.  The weights are the softmax over the k selected logits, summed
-// in rank order.
+// [split][T][E] added in split order.  Selection in k rounds: each logit
+// becomes a 64-bit key (order-preserving image of the value, then the
+// complement of the expert id, so equal values rank the lower id first; -0
+// is read as +0), and each round takes the wave's largest live key (within
+// 16-lane rows by DPP, then the four row maxima as scalars) and retires it.
+// The weights are the softmax over the k selected logits, summed in rank
+// order.
 // One wave per workgroup (one token): the waves never wait for each other.
 // Every partial load is issued up front and unconditionally (clamped
 // indices; the values past n_split or E are discarded), so all of them are in
 // flight together.
 constexpr int kTopkWaves = 1;
+
+__device__ __forceinline__ uint32_t float_order(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float order_float(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, CTRL, 0xF, 0xF, true);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), CTRL, 0xF, 0xF, true);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
 template <int NQ>  // logits per lane: E <= 64 NQ
 __global__ __launch_bounds__(64 * kTopkWaves) void k_topk(const float* part, int n_split, int64_t split_stride,
                                                           int T, int E, int k, const int32_t* forced, int32_t* ids,
@@ -52,20 +75,13 @@ __global__ __launch_bounds__(64 * kTopkWaves) void k_topk(const float* part, int
     if (live && e < E && r_out) r_out[(int64_t)t * E + e] = v;
     r[q] = v;
   }
-#pragma unroll
-  for (int q = NQ; q < 4; ++q) lg[wave][lane + q * 64] = -INFINITY;  // E <= 256
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) lg[wave][lane + q * 64] = r[q];
-  // defaults keep every id in range should non-finite logits leave a rank empty
-  if (lane < 16) {
-    sv[wave][lane] = -INFINITY;
-    se[wave][lane] = 0;
-  }
-  __syncthreads();
   if (!live) return;
   if (forced) {
     // test path: the caller fixes the k experts (in rank order); weights still
     // come from this token's router logits
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) lg[wave][lane + q * 64] = r[q];
+    __syncthreads();
     if (lane < k) {
       int e = forced[t * k + lane];
       if (e < 0 || e >= E) e = 0;  // keep the grouped GEMMs in bounds on bad test input
@@ -73,33 +89,30 @@ __global__ __launch_bounds__(64 * kTopkWaves) void k_topk(const float* part, int
       se[wave][lane] = e;
     }
   } else {
-    // four logits per LDS read, every held logit compared in the same pass
-    // (lg holds -inf past E, which beats nothing)
-    int rank[NQ];
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) rank[q] = 0;
-    const float4* lg4 = reinterpret_cast<const float4*>(lg[wave]);
-    const int E4 = (E + 3) >> 2;
-#pragma unroll 8
-    for (int o4 = 0; o4 < E4; ++o4) {
-      const float4 u = lg4[o4];
-      const float uu[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) {
-        const int o = 4 * o4 + s2;
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-          const int e = lane + q * 64;
-          rank[q] += (uu[s2] > r[q] || (uu[s2] == r[q] && o < e)) ? 1 : 0;
-        }
-      }
-    }
+    // keys of the live logits; 0 (below every live key) past E and once taken
+    uint64_t key[NQ];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int e = lane + q * 64;
-      if (e < E && rank[q] < k) {
-        sv[wave][rank[q]] = r[q];
-        se[wave][rank[q]] = e;
+      key[q] = e < E ? ((uint64_t)float_order(r[q] + 0.f) << 32) | (uint32_t)~e : 0ull;
+    }
+    for (int j = 0; j < k; ++j) {
+      uint64_t b = key[0];
+#pragma unroll
+      for (int q = 1; q < NQ; ++q) b = max_u64(b, key[q]);
+      b = max_u64(b, dpp_u64<0xB1>(b));   // quad_perm xor 1
+      b = max_u64(b, dpp_u64<0x4E>(b));   // quad_perm xor 2
+      b = max_u64(b, dpp_u64<0x141>(b));  // row half mirror
+      b = max_u64(b, dpp_u64<0x140>(b));  // row mirror: the row's maximum in every lane
+      b = max_u64(max_u64(readlane_u64(b, 0), readlane_u64(b, 16)),
+                  max_u64(readlane_u64(b, 32), readlane_u64(b, 48)));
+      const int e = (int)~(uint32_t)b;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+        if (lane + q * 64 == e) key[q] = 0ull;
+      if (lane == 0) {
+        sv[wave][j] = order_float((uint32_t)(b >> 32));
+        se[wave][j] = e;
       }
     }
   }
