@@ -193,20 +193,46 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void k_attn_mfma(AttnArgs a) {
     }
     // S^T for the four (kk, half) 16-key groups and both query tiles
     f32x4_t st[ATT_QT][4];
+    {
+      // step by step over the 32-dim slices, the four key groups side by
+      // side; the next slice's four K fragments are read before this one's
+      // MFMAs (each st[x] still accumulates s = 0, 1, .. in order)
+      int kr[4];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
+      for (int x = 0; x < 4; ++x) {
+        kr[x] = att_krow(x >> 1, x & 1, c16);
 #pragma unroll
-      for (int qt = 0; qt < ATT_QT; ++qt) st[qt][x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const int r = att_krow(x >> 1, x & 1, c16);
+        for (int qt = 0; qt < ATT_QT; ++qt) st[qt][x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+      bf16x8_t kf[2][4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        kf[0][x] = *reinterpret_cast<const bf16x8_t*>(ks + kr[x] * 512 + ((g ^ att_fk(kr[x])) << 4));
 #pragma unroll
       for (int s = 0; s < ATT_D / 32; ++s) {
-        const bf16x8_t kf =
-            *reinterpret_cast<const bf16x8_t*>(ks + r * 512 + (((s * 4 + g) ^ att_fk(r)) << 4));
+        if (s + 1 < ATT_D / 32) {
 #pragma unroll
-        for (int qt = 0; qt < ATT_QT; ++qt)
-          st[qt][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qt][s], st[qt][x], 0, 0, 0);
+          for (int x = 0; x < 4; ++x)
+            kf[(s + 1) & 1][x] =
+                *reinterpret_cast<const bf16x8_t*>(ks + kr[x] * 512 + ((((s + 1) * 4 + g) ^ att_fk(kr[x])) << 4));
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+          for (int qt = 0; qt < ATT_QT; ++qt)
+            st[qt][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s & 1][x], qf[qt][s], st[qt][x], 0, 0, 0);
       }
     }
+    // schedule (group masks: 0x100 LDS reads, 0x008 MFMAs): the first two
+    // slices' reads, then four MFMAs and the next slice's four reads in turn,
+    // so that each wait for K fragments covers eight reads, not one or two
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int s = 0; s < 6; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     // online softmax per query column; P^T operands: k index 8 g + e' <-> key 32 kk + 8 g + e'
     // A tile whose 64 keys are all visible to all of the wave's queries needs
     // no per-element mask (every tile but a split's last, and in the causal
@@ -271,19 +297,39 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void k_attn_mfma(AttnArgs a) {
       }
     }
     // O^T += V^T P^T: lane reads V^T[dim 16 t + c16][keys 32 kk + 8 g .. +8]
+    {
+      // the next dimension tile's two V^T fragments are read before this
+      // tile's MFMAs
+      bf16x8_t vf[2][2];
 #pragma unroll
-    for (int t = 0; t < ATT_D / 16; ++t) {
-      const int dd = t * 16 + c16;
+      for (int kk = 0; kk < 2; ++kk)
+        vf[0][kk] = *reinterpret_cast<const bf16x8_t*>(vs + c16 * 128 + (((4 * kk + g) ^ (c16 & 7)) << 4));
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(vs + dd * 128 + (((4 * kk + g) ^ (dd & 7)) << 4));
+      for (int t = 0; t < ATT_D / 16; ++t) {
+        if (t + 1 < ATT_D / 16) {
+          const int dn = (t + 1) * 16 + c16;
 #pragma unroll
-        for (int qt = 0; qt < ATT_QT; ++qt) {
-          o[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qt][kk], o[qt][t], 0, 0, 0);
-          o[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[qt][kk], o[qt][t], 0, 0, 0);
+          for (int kk = 0; kk < 2; ++kk)
+            vf[(t + 1) & 1][kk] = *reinterpret_cast<const bf16x8_t*>(vs + dn * 128 + (((4 * kk + g) ^ (dn & 7)) << 4));
         }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int qt = 0; qt < ATT_QT; ++qt) {
+            o[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[t & 1][kk], pf[qt][kk], o[qt][t], 0, 0, 0);
+            o[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[t & 1][kk], pl[qt][kk], o[qt][t], 0, 0, 0);
+          }
       }
     }
+    // schedule: the first three dimension tiles' reads, then the four MFMAs
+    // of a tile and the two reads of a later one in turn
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 1);
+#pragma unroll
+    for (int t = 0; t < 14; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
   }
 #pragma unroll
   for (int qt = 0; qt < ATT_QT; ++qt) {
