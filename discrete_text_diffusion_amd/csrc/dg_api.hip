@@ -357,8 +357,13 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
       DG_TRY(launch_set_norm(bf, c.teacher_x + (int64_t)l * T * s.d, c.at<float>(c.p.x), xn, T, s.d, s.eps, c.st));
     char* kc = reinterpret_cast<char*>(cache->k) + (size_t)l * layer_elems * s.act;
     char* vc = reinterpret_cast<char*>(cache->v) + (size_t)l * layer_elems * s.act;
-    // q, k, v with RoPE
-    for (int seg = 0; seg < n_segs; ++seg) {
+    // q, k, v with RoPE.  With one sequence the two segments are one run of
+    // 2 seq_len tokens at positions L.. (rows, cache rows and rotation table
+    // all contiguous), so one product covers both (one pass over the
+    // weights); with several sequences each segment has its own launch.
+    const int qkv_launches = (n_segs == 1 || n_seq == 1) ? 1 : n_segs;
+    const int qkv_len = seq_len * n_segs / qkv_launches;  // tokens per sequence and launch
+    for (int seg = 0; seg < qkv_launches; ++seg) {
       Phase ph(c, DG_PHASE_QKV);
       GemmArgs a = base_args();
       a.act = c.at<char>(c.p.n) + (size_t)seg * Tseg * s.d * s.act; a.act_ld = s.d;
@@ -372,9 +377,9 @@ int run_layers(const Ctx& c, const dg_kv_cache* cache, int n_seq, int seq_len, i
       // encoder; scratch rows for the denoiser, which leaves the length as is
       q.k = kc; q.v = vc; q.kv_b_stride = c_seq; q.kv_h_stride = c_head; q.kv_row0 = L + seg * seq_len;
       q.v_pitch = cache->capacity;
-      q.seq_len = seq_len; q.pos0 = L + seg * seq_len; q.rope_base = s.rope_base;
+      q.seq_len = qkv_len; q.pos0 = L + seg * seq_len; q.rope_base = s.rope_base;
       q.rope = c.at<float2>(c.p.rope) + (size_t)seg * seq_len * (s.dh / 2);
-      DG_TRY(dense_gemm(c, a, Tseg, s.qkv, s.d, 1));
+      DG_TRY(dense_gemm(c, a, n_seq * qkv_len, s.qkv, s.d, 1));
     }
     // The causal encode keeps only the K/V rows it appends: past the last
     // layer's QKV nothing reads its output (no LM head follows; the next chunk
