@@ -124,7 +124,9 @@ class DeviceModel:
                 synth.dev_normal_f32_transposed(et.data_ptr(), shape.vocab, d, shape.weight_seed,
                                                 synth.TID["embed"], shape.weight_std, st)
             self.tensors["embed_t"] = et
-        fill("lm_head", synth.TID["lm_head"], shape.vocab, d, fp8=shape.lm_dtype == "fp8")
+        # a tied head is drawn from the embedding's stream: the same matrix
+        fill("lm_head", synth.TID["embed" if shape.tied_head else "lm_head"], shape.vocab, d,
+             fp8=shape.lm_dtype == "fp8")
         fill("sc_up", synth.TID["sc_up"], shape.d_selfcond, d)
         fill("sc_down", synth.TID["sc_down"], d, shape.d_selfcond)
         self.layer_structs = (LayerWeights * shape.n_layers)()

@@ -81,6 +81,8 @@ class Weights:
         if self._cache is not None and key in self._cache:
             return self._cache[key]
         tid = synth.TID[name] if layer is None else synth.layer_tid(layer, name)
+        if name == "lm_head" and self.shape.tied_head:
+            tid = synth.TID["embed"]  # input recipe: the head is drawn from the embedding's stream
         dt = self._dtype_of(name)
         shp = self._shape_of(name)
         if dt == "fp8":

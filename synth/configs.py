@@ -30,6 +30,9 @@ class ModelShape:
     norm_eps: float = 1e-6
     weight_std: float = 0.02
     weight_seed: int = 0
+    # LM head tied to the embedding (generated from the embedding's tensor id,
+    # so both are the same matrix); the page workloads keep separate heads
+    tied_head: bool = False
 
     @property
     def qkv_rows(self) -> int:

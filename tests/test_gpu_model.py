@@ -108,6 +108,26 @@ def mini(env):
 
 
 @pytest.fixture(scope="module")
+def tiny_tied(env):
+    # LM head tied to the embedding: the model predicts its own input tokens
+    # with confidence, the canvas reaches a fixed point and the adaptive stop
+    # fires (at the second step)
+    wl = WORKLOADS["tiny"]
+    pb = Problem(env, replace(wl.model, tied_head=True), 20.0, wl.prefix, wl.canvas, cap_extra=wl.canvas)
+    pb.encode_prefix()
+    return pb
+
+
+@pytest.fixture(scope="module")
+def mini_tied(env):
+    # the same for the bf16 mini model: partial acceptance for a dozen steps,
+    # then both canvases stop in the same step (the 13th)
+    pb = Problem(env, replace(MINI_BF16, tied_head=True), 60.0, 40, 48, B=2, cap_extra=48)
+    pb.encode_prefix()
+    return pb
+
+
+@pytest.fixture(scope="module")
 def mini8(env):
     pb = Problem(env, MINI_FP8, 6.0, 40, 48, B=2, cap_extra=48)
     pb.encode_prefix()
@@ -376,9 +396,10 @@ def test_denoise_loop_and_commit_match_oracle(which, request):
     pb.check_guards()
 
 
-@pytest.mark.parametrize("which", ["tiny", "mini", "mini8", "mini4"])
+@pytest.mark.parametrize("which", ["tiny", "mini", "mini8", "mini4", "tiny_tied", "mini_tied"])
 def test_forced_route_loop_matches_oracle(which, request):
-    """Every step of a 12-step schedule compared with the oracle on the
+    """Every step of a 12-step schedule (48 steps with adaptive stopping for
+    the tied-head models, until the oracle stops) compared with the oracle on the
     oracle's routes (dg_test_denoise_step: the product's whole step with
     every layer's experts forced).  The GPU carries its own self-conditioning
     input from step to step (the previous step's tempered distribution,
@@ -391,7 +412,10 @@ def test_forced_route_loop_matches_oracle(which, request):
     pb = request.getfixturevalue(which)
     torch, dg, rt = pb.env
     shape, B, C, V = pb.shape, pb.B, pb.C, pb.shape.vocab
-    N = 12
+    tied = shape.tied_head
+    N = 48 if tied else 12
+    stopped_at = None
+    tsc = None  # the fp32 twin's own self-conditioning input
     say(f"forced-route loop {which}")
     dg.dg_init_canvas(pb.cfg, pb.canvas.struct, 0, pb.st)
     pb.canvas.prev_argmax.fill_(-1)
@@ -421,11 +445,23 @@ def test_forced_route_loop_matches_oracle(which, request):
         nxt = pb.canvas.tokens.cpu().numpy().reshape(B, C)
         stop = pb.canvas.stop.cpu().numpy()
 
+        # The fp32 twin runs a trajectory of its own, like the GPU: the same
+        # canvas and routes, and its own previous step's distribution as the
+        # self-conditioning input, so its error against the oracle carries the
+        # same step-to-step drift as the GPU's (the GPU's input comes from its
+        # own logits, not the oracle's).
         def twin():
             with om.accumulation("f32"):
-                return _f32_twin_on_inputs(pb, otok, osc, tr["expert_ids"])
+                return _f32_twin_on_inputs(pb, otok, tsc, tr["expert_ids"])
 
-        bar_then_twin(f"loop {which} t{t} logits", z, zo, twin, pb.atol, RTOL)
+        zt = twin()
+        calls = [0]
+
+        def twin_fn():
+            calls[0] += 1
+            return zt if calls[0] == 1 else twin()
+
+        bar_then_twin(f"loop {which} t{t} logits", z, zo, twin_fn, pb.atol, RTOL)
         for b, o in enumerate(outs):
             tol = entropy_tolerance(zo[b], o["tau"], pb.atol)
             allclose_report(f"loop {which} t{t} b{b} device entropy", H[b], o["H"], tol, 0.0)
@@ -433,11 +469,19 @@ def test_forced_route_loop_matches_oracle(which, request):
                                            stop[b], dict(o, z=zo[b]))
         worst_dz = max(worst_dz, float(np.abs(z - zo).max()))
         worst_dh = max(worst_dh, float(np.abs(H - np.stack([o["H"] for o in outs])).max()))
+        tsc = np.stack([smp.sample_from_logits(zt[b], t, N, pb.seeds[b], 0, None, True)["p"] for b in range(B)])
         oprev = np.stack([o["argmax"] for o in outs])
         otok = np.stack([o["next_tokens"] for o in outs])
         osc = np.stack([o["p"] for o in outs])
-    say(f"forced-route loop {which}: {N} steps compared; max |dz| {worst_dz:.2e}, max |dH| {worst_dh:.2e}, "
-        f"near-tie decisions {ties}")
+        if all(o["stop"] for o in outs):
+            # the oracle's adaptive stop: every canvas's flag set on the device too
+            assert stop.tolist() == [1] * B, (t, stop)
+            stopped_at = t
+            break
+    say(f"forced-route loop {which}: {t + 1} steps compared; max |dz| {worst_dz:.2e}, max |dH| {worst_dh:.2e}, "
+        f"near-tie decisions {ties}; adaptive stop at step {stopped_at}")
+    if tied:
+        assert stopped_at is not None and stopped_at < N - 1
     pb.check_guards()
 
 

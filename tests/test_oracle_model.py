@@ -300,3 +300,25 @@ def test_resume_from_saved_state_is_identical():
     for a, b in zip(full[2:], rest):
         for key in ("H", "sample", "argmax", "accepted", "next_tokens", "p"):
             assert np.array_equal(a[key], b[key]), key
+
+
+def test_tied_head_reads_the_embedding_and_reaches_the_stop():
+    """A tied head is the embedding matrix itself (same values); the model then
+    scores its own input token highest by far (the self dot product of a row
+    against the cross terms), so with a sharp head every position is accepted,
+    the next step's canvas is the same and the adaptive stop fires at t = 1:
+    argmax unchanged and the canvas-mean entropy below the threshold."""
+    wl = WORKLOADS["tiny"]
+    shape = replace(wl.model, tied_head=True)
+    W = om.Weights(shape)
+    assert np.array_equal(W.get("lm_head"), W.get("embed"))
+    assert not np.array_equal(om.Weights(wl.model).get("lm_head"), W.get("embed"))
+    cache = om.KVCache(shape, 1, wl.prefix + wl.canvas)
+    ost.encode_append(shape, W, cache, np.stack([synth.tokens(0, synth.TID["prompt"], wl.prefix, shape.vocab)]))
+    log = []
+    _, steps = ost.run_canvas(shape, W, cache, 48, [17], 0, 20.0, True, wl.canvas, commit=False, log=log)
+    assert steps == 2
+    o0, o1 = log[0]["outs"][0], log[1]["outs"][0]
+    assert o0["n_accepted"] == wl.canvas and not o0["stop"]  # t = 0 never stops
+    assert np.array_equal(o0["argmax"], log[0]["tokens"][0])   # the input tokens predicted back
+    assert np.array_equal(o1["argmax"], o0["argmax"]) and o1["mean_H"] < 0.005 and o1["stop"]
