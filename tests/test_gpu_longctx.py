@@ -8,7 +8,7 @@ up to 48 adaptive steps, each committed by encode & append (final cache
   computes any row by itself: sampled rows of the 32768-token encode, and of
   canvases appended at positions 32768 and beyond, against the oracle.
 * The denoising step at the last canvas's context (34560 cached keys plus the
-  256 canvas keys) over a seeded N(0,1) cache: logits of sampled positions,
+  256 canvas keys) over a seeded N(0,1) cache: logits of every canvas position,
   their entropies and the router logits against the oracle (routes forced).
 * The 8-canvas generation on the GPU: per-step sampler invariants, the cache
   growing by 256 rows per commit with rows below untouched, and encode &
@@ -29,7 +29,7 @@ from .test_gpu_model import ATOL, RTOL, ROUTE_EPS, _route_margins
 pytestmark = pytest.mark.gpu
 
 SAMPLE_POS = np.array([0, 1, 255, 256, 4095, 16383, 30001, 32766, 32767])
-ROWS = np.arange(0, 256, 17)
+ROWS = np.arange(256)  # every canvas position
 
 
 @pytest.fixture(scope="module")
