@@ -71,9 +71,10 @@ def pmc_copy():
     torch.cuda.synchronize()
 
 
-def pmc_step(workload: str):
+def pmc_step(workload: str, algo_out=None):
     """The bench's prefill and one denoising step (t = 0) of the workload:
     the launches whose counters the traffic summary reads."""
+    import numpy as np
     import torch
     from discrete_text_diffusion_amd import runtime as rt
     import discrete_text_diffusion_amd as dg
@@ -95,6 +96,21 @@ def pmc_step(workload: str):
     dg.dg_encode_append(model.cfg, model.weights, cache.struct, prompt.data_ptr(), wl.batch, wl.prefix, ws.ptr, ws.size,
                         st)
     print("[pmc-step] prefix encoded", file=sys.stderr, flush=True)
+    if algo_out:
+        # the same step once through the test entry point (same launches) for
+        # its routing: the algorithmic bytes of exactly the launches counted
+        shape = wl.model
+        T = wl.batch * wl.canvas
+        rbuf = torch.empty(shape.n_layers * T * shape.n_experts, dtype=torch.float32, device="cuda")
+        dg.dg_init_canvas(model.cfg, cv.struct, 0, st)
+        dg.dg_test_denoise_step(model.cfg, model.weights, cache.struct, cv.struct, rt.step_params(0, 12, 0, False),
+                                None, rbuf.data_ptr(), None, ws.ptr, ws.size, st)
+        ids = rbuf.view(shape.n_layers, T, shape.n_experts).argsort(dim=-1, descending=True, stable=True)[
+            ..., :shape.top_k].cpu().numpy()
+        touched = [int(np.unique(ids[l]).size) for l in range(shape.n_layers)]
+        algo = float(np.mean([moe_up_bytes(shape, T, e) for e in touched]))
+        with open(algo_out, "w") as fh:
+            json.dump({"algorithmic_bytes_per_launch": algo, "experts_touched": touched}, fh)
     dg.dg_init_canvas(model.cfg, cv.struct, 0, st)
     dg.dg_denoise_step(model.cfg, model.weights, cache.struct, cv.struct, rt.step_params(0, 12, 0, False), ws.ptr,
                        ws.size, st)
@@ -241,7 +257,7 @@ def _counter_kib(d, counter, name_has=None, biggest=False, last=None):
     return sum(vals.values()) / len(vals), len(vals), None
 
 
-def pmc_summarize(df, dw, dcf, dcw, out):
+def pmc_summarize(df, dw, dcf, dcw, out, algo_file=None):
     # the denoising step's launches: the last n_layers of the kernel (the
     # prefix encode's come first)
     from synth.configs import WORKLOADS
@@ -257,19 +273,29 @@ def pmc_summarize(df, dw, dcf, dcw, out):
            "copy_kernel": cname, "copy_bytes": COPY_BYTES, "copy_fetch_kib": round(cfetch, 1),
            "copy_write_kib": round(cwrite, 1), "fetch_factor": round(kf, 4), "write_factor": round(kw, 4),
            "traffic_bytes_per_launch": int(traffic), "k_gemm_sha256": _sha256(GEMM_SRC)}
+    algo = json.load(open(algo_file))["algorithmic_bytes_per_launch"] if algo_file else None
+    if algo:
+        rec["algorithmic_bytes_per_launch_same_step"] = int(algo)
+        rec["traffic_over_algorithmic"] = round(traffic / algo, 4)
     with open(out, "w") as fh:
         fh.write("# HBM traffic of the routed + shared expert gate/up GEMM (full30 denoising step)\n\n")
         fh.write("Counters per dispatch (KiB) from four separate rocprofv3 runs, from the repository root:\n\n")
-        for c, m, dd in (("FETCH_SIZE", "--pmc-step", df), ("WRITE_SIZE", "--pmc-step", dw),
+        extra = f" --pmc-algo {algo_file}" if algo_file else ""
+        for c, m, dd in (("FETCH_SIZE", "--pmc-step" + extra, df), ("WRITE_SIZE", "--pmc-step", dw),
                          ("FETCH_SIZE", "--pmc-copy", dcf), ("WRITE_SIZE", "--pmc-copy", dcw)):
             fh.write(f"    rocprofv3 --pmc {c} -d {dd} -o p -- python bench.py {m}\n")
-        fh.write(f"    python bench.py --pmc-summarize {df} {dw} {dcf} {dcw} {out}\n\n")
+        fh.write(f"    python bench.py --pmc-summarize {df} {dw} {dcf} {dcw} {out}{extra}\n\n")
         fh.write(f"* `{MOE_UP_KERNEL}`: FETCH_SIZE {fetch:.0f} KiB, WRITE_SIZE {write:.0f} KiB per launch "
                  f"(mean of the {n_f} and {n_w} launches of one denoising step after the prefix encode).\n")
         fh.write(f"* Copy calibration ({cname}, {COPY_BYTES} B read and written): FETCH_SIZE {cfetch:.0f} KiB, "
                  f"WRITE_SIZE {cwrite:.0f} KiB -> factors {kf:.4f} (fetch) and {kw:.4f} (write).\n")
         fh.write(f"* HBM traffic per launch = fetch / {kf:.4f} + write / {kw:.4f} = {traffic / 1e9:.4f} GB "
-                 f"(algorithmic: the bench's algorithmic_bytes_per_launch).\n\n")
+                 f"(algorithmic: the bench's algorithmic_bytes_per_launch).\n")
+        if algo:
+            fh.write(f"* Algorithmic bytes of the same 30 launches (their own routing, read by a replay of the same "
+                     f"step through the test entry point before the counted one): {algo / 1e9:.4f} GB per launch; "
+                     f"traffic / algorithmic = {traffic / algo:.3f}.\n")
+        fh.write("\n")
         fh.write("```json\n" + json.dumps(rec) + "\n```\n")
     print(json.dumps(rec))
 
@@ -696,6 +722,8 @@ def main():
     ap.add_argument("--pmc-step", action="store_true", help="one denoising step only (counter runs)")
     ap.add_argument("--pmc-copy", action="store_true", help="counter calibration copy only")
     ap.add_argument("--pmc-summarize", nargs=5, metavar=("F", "W", "CF", "CW", "OUT"))
+    ap.add_argument("--pmc-algo", metavar="JSON", help="--pmc-step: write the counted launches' algorithmic bytes "
+                    "here; --pmc-summarize: read them from here")
     ap.add_argument("--profile-summary", nargs=4, metavar=("TRACE_DIR", "BENCH_JSON", "OUT", "COMMAND"),
                     help="kernel-time summary of a profiled bench run (the timed gate/up dispatches selected)")
     ap.add_argument("--ar-profile", type=int, metavar="N", help="N single-token decode steps only (kernel profiles)")
@@ -722,7 +750,7 @@ def main():
         ar_profile(args.workload, args.ar_profile)
         return
     if args.pmc_summarize:
-        pmc_summarize(*args.pmc_summarize)
+        pmc_summarize(*args.pmc_summarize, algo_file=args.pmc_algo)
         return
     if args.profile_summary:
         profile_summary(*args.profile_summary)
@@ -731,7 +759,7 @@ def main():
         pmc_copy()
         return
     if args.pmc_step:
-        pmc_step(args.workload)
+        pmc_step(args.workload, args.pmc_algo)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs the decoding step on one GPU only; "
